@@ -1,0 +1,393 @@
+/*
+ * mips_oracle.c -- CPU oracle for exhaustive inner-product top-K.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the plain, slow, obviously correct
+ * reference that the HIP library is checked against. Only the test suite, the
+ * smoke check and the benchmark's CPU-baseline leg may load it. It shares no code
+ * with the HIP library and includes none of its headers.
+ *
+ * What it computes, and where the pages define it:
+ *
+ *  - l2 normalisation: y = x / sqrt(max(sum x^2, 1e-12)), the form of
+ *    `_l2_normalize_candidates` and of the user-representation normalisation in
+ *    recsys_two_tower_model.py (x-algorithm Phoenix). Done in fp64.
+ *  - packing of the normalised index into a narrow type, as "normalise once at
+ *    index time; store f16/int8" ("Two-tower retrieval", mhtirogla.ai, section
+ *    "Implementation notes") and the bf16 `post_embeddings` index of
+ *    recsys_two_tower_model.py. bf16 and OCP E4M3 codes are produced by
+ *    round-to-nearest-even onto the format's value grid, derived here from the
+ *    format definitions; E4M3 saturates at +-448 and uses one per-row scale,
+ *    the smallest power of two 2^t with max|y| <= 448 * 2^t (a zero row gets 1).
+ *  - scoring: every query against every non-excluded corpus row by dot product
+ *    (`RecsysTwoTowerModel.forward`: matmul of the users against the whole index,
+ *    masked by one shared type mask; Phoenix README, "How Retrieval Works", step 4).
+ *    Operands are decoded exactly to fp64 and summed in dimension order. Each
+ *    product of two stored operands is exact in fp64, so the sums are exact up to
+ *    the final fp64 roundings.
+ *  - selection: a full sort of all eligible (score, id) pairs, by score descending
+ *    and then id ascending (the stable full sort of the toy's `top_k` in
+ *    "Two-tower retrieval", section "Code"), then the first min(k, eligible)
+ *    entries (`local_top_k` takes min(k, N)). Missing entries are padded with
+ *    (-inf, -1). Excluded ids are never returned.
+ *
+ * Non-finite inputs are not supported; the entry points reject them.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_E4M3 = 2 };
+enum { OR_OK = 0, OR_BAD_ARG = 1, OR_NONFINITE = 2, OR_NOMEM = 3 };
+
+/* ------------------------------------------------------------------ formats */
+
+/* bf16 is the upper 16 bits of an IEEE binary32. */
+double oracle_bf16_value(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* OCP 8-bit floating point E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits.
+ * Exponent field 0 is subnormal: m * 2^-9. Exponent 15 with mantissa 7 is NaN.
+ * There are no infinities; the largest finite magnitude is 1.75 * 2^8 = 448. */
+double oracle_e4m3_value(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* Round |a| to the nearest multiple of `q` (a power of two), ties to even.
+ * a / q is exact because q is a power of two; nearbyint uses the default
+ * round-to-nearest-even mode. */
+static double round_to_grid(double a, double q)
+{
+    return nearbyint(a / q) * q;
+}
+
+/* bf16 code of y by round-to-nearest-even. bf16 keeps 8 significant bits, so in
+ * the binade [2^e, 2^(e+1)) the spacing is 2^(e-7); below the smallest normal
+ * 2^-126 the spacing stays 2^-133. The sign is kept, also for zero. */
+uint16_t oracle_bf16_from_f64(double y)
+{
+    uint16_t sign = signbit(y) ? 0x8000u : 0u;
+    double a = fabs(y);
+    if (a == 0.0)
+        return sign;
+    int e2;
+    frexp(a, &e2);
+    int ex = e2 - 1; /* floor(log2 a) */
+    if (ex < -126)
+        ex = -126;
+    double r = round_to_grid(a, ldexp(1.0, ex - 7));
+    float f = (float)r; /* exact: r is a bf16 value */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+/* E4M3 code of v by round-to-nearest-even with saturation at 448. 4 significant
+ * bits: spacing 2^(e-3) in the binade [2^e, 2^(e+1)); below the smallest normal
+ * 2^-6 the spacing stays 2^-9. The code is found by matching the decoded grid. */
+uint8_t oracle_e4m3_from_f64(double v)
+{
+    uint8_t sign = signbit(v) ? 0x80u : 0u;
+    double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    int e2;
+    frexp(a, &e2);
+    int ex = e2 - 1;
+    if (ex < -6)
+        ex = -6;
+    double r = round_to_grid(a, ldexp(1.0, ex - 3));
+    if (r > 448.0)
+        r = 448.0;
+    for (int c = 0; c <= 0x7E; ++c)
+        if (oracle_e4m3_value((uint8_t)c) == r)
+            return (uint8_t)(sign | c);
+    return 0xFF; /* unreachable for finite v */
+}
+
+/* Per-row E4M3 scale: the smallest power of two s = 2^t with amax <= 448 * s.
+ * With amax = f * 2^e, f in [0.5, 1): amax <= 0.875 * 2^(9+t) holds for
+ * t >= e - 9 when f <= 0.875, else for t >= e - 8. A zero row gets s = 1. */
+double oracle_e4m3_row_scale(double amax)
+{
+    if (amax == 0.0)
+        return 1.0;
+    int e;
+    double f = frexp(amax, &e);
+    int t = (f <= 0.875) ? e - 9 : e - 8;
+    return ldexp(1.0, t);
+}
+
+/* ------------------------------------------------------------ normalisation */
+
+/* y[r, :] = x[r, :] / sqrt(max(sum_d x[r, d]^2, 1e-12)), all in fp64. */
+int oracle_l2_normalize(const float *x, int64_t rows, int32_t d, double *y)
+{
+    if (!x || !y || rows < 0 || d <= 0)
+        return OR_BAD_ARG;
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *xr = x + r * (int64_t)d;
+        double ss = 0.0;
+        for (int32_t j = 0; j < d; ++j) {
+            if (!isfinite(xr[j]))
+                return OR_NONFINITE;
+            ss += (double)xr[j] * (double)xr[j];
+        }
+        double nrm = sqrt(fmax(ss, 1e-12));
+        for (int32_t j = 0; j < d; ++j)
+            y[r * (int64_t)d + j] = (double)xr[j] / nrm;
+    }
+    return OR_OK;
+}
+
+/* Normalise `rows` raw rows and pack them row-major into `out`:
+ *   OR_F32:  float  [rows, d]  (y rounded to binary32, nearest-even)
+ *   OR_BF16: uint16 [rows, d]  (bf16 codes)
+ *   OR_E4M3: uint8  [rows, d]  (E4M3 codes of y / scale) and scale[rows] (float)
+ */
+int oracle_prepare(const float *x, int64_t rows, int32_t d, int32_t dtype, void *out,
+                   float *scale)
+{
+    if (!x || !out || rows < 0 || d <= 0 || dtype < OR_F32 || dtype > OR_E4M3)
+        return OR_BAD_ARG;
+    if (dtype == OR_E4M3 && !scale)
+        return OR_BAD_ARG;
+    double *y = (double *)malloc(sizeof(double) * (size_t)d);
+    if (!y)
+        return OR_NOMEM;
+    for (int64_t r = 0; r < rows; ++r) {
+        int rc = oracle_l2_normalize(x + r * (int64_t)d, 1, d, y);
+        if (rc != OR_OK) {
+            free(y);
+            return rc;
+        }
+        int64_t base = r * (int64_t)d;
+        if (dtype == OR_F32) {
+            for (int32_t j = 0; j < d; ++j)
+                ((float *)out)[base + j] = (float)y[j];
+        } else if (dtype == OR_BF16) {
+            for (int32_t j = 0; j < d; ++j)
+                ((uint16_t *)out)[base + j] = oracle_bf16_from_f64(y[j]);
+        } else {
+            double amax = 0.0;
+            for (int32_t j = 0; j < d; ++j)
+                amax = fmax(amax, fabs(y[j]));
+            double s = oracle_e4m3_row_scale(amax);
+            scale[r] = (float)s;
+            for (int32_t j = 0; j < d; ++j)
+                ((uint8_t *)out)[base + j] = oracle_e4m3_from_f64(y[j] / s);
+        }
+    }
+    free(y);
+    return OR_OK;
+}
+
+/* ---------------------------------------------------------------- scoring */
+
+static double stored_value(int32_t dtype, const void *base, int64_t idx)
+{
+    switch (dtype) {
+    case OR_F32:
+        return (double)((const float *)base)[idx];
+    case OR_BF16:
+        return oracle_bf16_value(((const uint16_t *)base)[idx]);
+    default:
+        return oracle_e4m3_value(((const uint8_t *)base)[idx]);
+    }
+}
+
+/* Exact-as-fp64 score of query row `qrow` against corpus row `i`. */
+static double score_one(const double *q, int32_t c_dtype, const void *corpus,
+                        const float *row_scale, int64_t i, int32_t d)
+{
+    double s = 0.0;
+    double rs = (c_dtype == OR_E4M3) ? (double)row_scale[i] : 1.0;
+    for (int32_t j = 0; j < d; ++j)
+        s += q[j] * (stored_value(c_dtype, corpus, i * (int64_t)d + j) * rs);
+    return s;
+}
+
+static int excluded(const uint32_t *bits, int64_t i)
+{
+    return bits && ((bits[i >> 5] >> (i & 31)) & 1u);
+}
+
+typedef struct {
+    double s;
+    int32_t id;
+} pair_t;
+
+/* Score descending, then id ascending. */
+static int cmp_pair(const void *a, const void *b)
+{
+    const pair_t *x = (const pair_t *)a, *y = (const pair_t *)b;
+    if (x->s > y->s)
+        return -1;
+    if (x->s < y->s)
+        return 1;
+    return (x->id > y->id) - (x->id < y->id);
+}
+
+typedef struct {
+    int32_t q_dtype, c_dtype, d, k, b;
+    const void *queries, *corpus;
+    const float *row_scale;
+    const uint32_t *exclude;
+    int64_t n;
+    double *out_s;
+    int32_t *out_id;
+    int next; /* next query to take (guarded by lock) */
+    int status;
+    pthread_mutex_t lock;
+} topk_job_t;
+
+static void *topk_worker(void *arg)
+{
+    topk_job_t *J = (topk_job_t *)arg;
+    pair_t *pairs = (pair_t *)malloc(sizeof(pair_t) * (size_t)(J->n > 0 ? J->n : 1));
+    double *q = (double *)malloc(sizeof(double) * (size_t)J->d);
+    if (!pairs || !q) {
+        pthread_mutex_lock(&J->lock);
+        J->status = OR_NOMEM;
+        pthread_mutex_unlock(&J->lock);
+        free(pairs);
+        free(q);
+        return NULL;
+    }
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        int b = J->next++;
+        pthread_mutex_unlock(&J->lock);
+        if (b >= J->b)
+            break;
+        for (int32_t j = 0; j < J->d; ++j)
+            q[j] = stored_value(J->q_dtype, J->queries, (int64_t)b * J->d + j);
+        int64_t m = 0;
+        for (int64_t i = 0; i < J->n; ++i) {
+            if (excluded(J->exclude, i))
+                continue;
+            pairs[m].s = score_one(q, J->c_dtype, J->corpus, J->row_scale, i, J->d);
+            pairs[m].id = (int32_t)i;
+            ++m;
+        }
+        qsort(pairs, (size_t)m, sizeof(pair_t), cmp_pair);
+        for (int32_t t = 0; t < J->k; ++t) {
+            int64_t o = (int64_t)b * J->k + t;
+            if (t < m) {
+                J->out_s[o] = pairs[t].s;
+                J->out_id[o] = pairs[t].id;
+            } else {
+                J->out_s[o] = -INFINITY;
+                J->out_id[o] = -1;
+            }
+        }
+    }
+    free(pairs);
+    free(q);
+    return NULL;
+}
+
+static int check_finite(int32_t dtype, const void *p, int64_t count)
+{
+    for (int64_t i = 0; i < count; ++i)
+        if (!isfinite(stored_value(dtype, p, i)))
+            return 0;
+    return 1;
+}
+
+/* Top-k of every query against the whole corpus.
+ *   queries:  [b, d] row-major, q_dtype OR_F32 or OR_BF16
+ *   corpus:   [n, d] row-major, c_dtype OR_F32, OR_BF16 or OR_E4M3
+ *   row_scale:[n] for OR_E4M3, else ignored
+ *   exclude:  NULL or uint32[ceil(n/32)], bit (i & 31) of word (i >> 5) excludes id i
+ *   out_s:    [b, k] fp64 scores, out_id: [b, k] int32 ids
+ */
+int oracle_topk(int32_t q_dtype, const void *queries, int32_t b, int32_t c_dtype,
+                const void *corpus, const float *row_scale, int64_t n, int32_t d,
+                const uint32_t *exclude, int32_t k, double *out_s, int32_t *out_id,
+                int32_t threads)
+{
+    if (!queries || !corpus || !out_s || !out_id || b < 0 || n < 0 || d <= 0 || k <= 0)
+        return OR_BAD_ARG;
+    if (q_dtype != OR_F32 && q_dtype != OR_BF16)
+        return OR_BAD_ARG;
+    if (c_dtype < OR_F32 || c_dtype > OR_E4M3 || (c_dtype == OR_E4M3 && !row_scale))
+        return OR_BAD_ARG;
+    if (!check_finite(q_dtype, queries, (int64_t)b * d) ||
+        !check_finite(c_dtype, corpus, n * (int64_t)d))
+        return OR_NONFINITE;
+    if (c_dtype == OR_E4M3)
+        for (int64_t i = 0; i < n; ++i)
+            if (!isfinite(row_scale[i]))
+                return OR_NONFINITE;
+
+    topk_job_t J;
+    memset(&J, 0, sizeof J);
+    J.q_dtype = q_dtype;
+    J.c_dtype = c_dtype;
+    J.d = d;
+    J.k = k;
+    J.b = b;
+    J.queries = queries;
+    J.corpus = corpus;
+    J.row_scale = row_scale;
+    J.exclude = exclude;
+    J.n = n;
+    J.out_s = out_s;
+    J.out_id = out_id;
+    pthread_mutex_init(&J.lock, NULL);
+    if (threads < 1)
+        threads = 1;
+    if (threads > b && b > 0)
+        threads = b;
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)threads);
+    int started = 0;
+    for (int t = 0; t < threads; ++t)
+        if (pthread_create(&tid[t], NULL, topk_worker, &J) == 0)
+            ++started;
+    if (started == 0)
+        topk_worker(&J);
+    for (int t = 0; t < started; ++t)
+        pthread_join(tid[t], NULL);
+    free(tid);
+    pthread_mutex_destroy(&J.lock);
+    return J.status;
+}
+
+/* Exact scores of given (query, id) pairs: out[t] = score(queries[qidx[t]], corpus[ids[t]]). */
+int oracle_scores(int32_t q_dtype, const void *queries, int32_t b, int32_t c_dtype,
+                  const void *corpus, const float *row_scale, int64_t n, int32_t d,
+                  const int32_t *qidx, const int32_t *ids, int64_t count, double *out)
+{
+    if (!queries || !corpus || !qidx || !ids || !out || d <= 0)
+        return OR_BAD_ARG;
+    double *q = (double *)malloc(sizeof(double) * (size_t)d);
+    if (!q)
+        return OR_NOMEM;
+    for (int64_t t = 0; t < count; ++t) {
+        if (qidx[t] < 0 || qidx[t] >= b || ids[t] < 0 || ids[t] >= n) {
+            free(q);
+            return OR_BAD_ARG;
+        }
+        for (int32_t j = 0; j < d; ++j)
+            q[j] = stored_value(q_dtype, queries, (int64_t)qidx[t] * d + j);
+        out[t] = score_one(q, c_dtype, corpus, row_scale, ids[t], d);
+    }
+    free(q);
+    return OR_OK;
+}

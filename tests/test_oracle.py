@@ -1,0 +1,291 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+format definitions and library conversions, closed forms, invariants, and an exact
+rational brute force on tiny inputs. CPU only."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import WORKLOADS, bitmap_from_ids
+
+
+# ------------------------------------------------------------------ formats
+def test_e4m3_decode_closed_forms():
+    # OCP E4M3: bias 7, 3 mantissa bits, subnormal step 2^-9, max 448, 0x7F/0xFF NaN.
+    assert oracle.e4m3_value(0x00) == 0.0
+    assert oracle.e4m3_value(0x01) == 2.0 ** -9
+    assert oracle.e4m3_value(0x07) == 7 * 2.0 ** -9
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6
+    assert oracle.e4m3_value(0x38) == 1.0
+    assert oracle.e4m3_value(0x39) == 1.125
+    assert oracle.e4m3_value(0x7E) == 448.0
+    assert oracle.e4m3_value(0xFE) == -448.0
+    assert np.isnan(oracle.e4m3_value(0x7F)) and np.isnan(oracle.e4m3_value(0xFF))
+    for c in range(0x7F):
+        assert oracle.e4m3_value(c | 0x80) == -oracle.e4m3_value(c)
+
+
+def test_e4m3_decode_matches_torch_float8_e4m3fn():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mine = np.array([oracle.e4m3_value(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(mine))
+    assert np.array_equal(ref[~nan], mine[~nan])
+
+
+def test_e4m3_encode_matches_torch_rne():
+    rng = np.random.default_rng(1)
+    v = np.concatenate([
+        rng.uniform(-448, 448, 4000),
+        rng.standard_normal(4000) * 2.0 ** rng.integers(-12, 6, 4000),
+        # exact midpoints between neighbouring codes (ties go to even)
+        [(oracle.e4m3_value(c) + oracle.e4m3_value(c + 1)) / 2 for c in range(0x7D)],
+    ]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    mine = np.array([oracle.e4m3_from(x) for x in v.astype(np.float64)], np.uint8)
+    assert np.array_equal(ref, mine)
+
+
+def test_e4m3_encode_ties_and_saturation():
+    assert oracle.e4m3_from(1.0 + 2 ** -4) == 0x38        # tie between 1 and 1.125 -> even (1)
+    assert oracle.e4m3_from(1.0 + 3 * 2 ** -4) == 0x3A    # tie between 1.125 and 1.25 -> 1.25
+    assert oracle.e4m3_from(460.0) == 0x7E                # saturates at 448
+    assert oracle.e4m3_from(1e6) == 0x7E
+    assert oracle.e4m3_from(-1e6) == 0xFE
+    assert oracle.e4m3_from(2.0 ** -10) == 0x00           # tie between 0 and 2^-9 -> 0
+    assert oracle.e4m3_from(3 * 2.0 ** -10) == 0x02       # tie between 2^-9 and 2^-8 -> 2^-8
+
+
+def test_bf16_decode_and_encode_match_torch():
+    codes = torch.arange(0, 65536, 7, dtype=torch.int32).to(torch.int16)
+    ref = codes.view(torch.bfloat16).to(torch.float64).numpy()
+    mine = np.array([oracle.bf16_value(int(c) & 0xFFFF) for c in codes.numpy()])
+    fin = np.isfinite(ref)
+    assert np.array_equal(ref[fin], mine[fin])
+    rng = np.random.default_rng(2)
+    v = np.concatenate([rng.standard_normal(5000) * 2.0 ** rng.integers(-130, 40, 5000),
+                        rng.uniform(-1, 1, 5000)]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    mine = np.array([oracle.bf16_from(x) for x in v.astype(np.float64)], np.uint16)
+    assert np.array_equal(ref, mine)
+
+
+def test_bf16_encode_ties():
+    assert oracle.bf16_from(1.0 + 2 ** -8) == 0x3F80        # tie -> even (1.0)
+    assert oracle.bf16_from(1.0 + 3 * 2 ** -8) == 0x3F82    # tie -> even (1 + 2^-6)
+    assert oracle.bf16_from(-0.0) == 0x8000
+
+
+def test_e4m3_row_scale_rule():
+    assert oracle.e4m3_row_scale(448.0) == 1.0
+    assert oracle.e4m3_row_scale(449.0) == 2.0
+    assert oracle.e4m3_row_scale(0.5) == 2.0 ** -9
+    assert oracle.e4m3_row_scale(0.0) == 1.0
+    rng = np.random.default_rng(3)
+    for a in rng.uniform(1e-3, 1.0, 300):
+        s = oracle.e4m3_row_scale(a)
+        assert a <= 448 * s and a > 448 * s / 2
+        assert np.log2(s) == np.round(np.log2(s))
+
+
+# ------------------------------------------------------------- normalisation
+def test_normalize_closed_forms():
+    y = oracle.normalize(np.array([[3, 4], [0, 0], [1e-7, 1e-7]], np.float32))
+    assert np.allclose(y[0], [0.6, 0.8], rtol=0, atol=1e-16)
+    assert np.array_equal(y[1], [0.0, 0.0])
+    # sum of squares 2e-14 < 1e-12: the norm is clamped to sqrt(1e-12) = 1e-6
+    x2 = np.float64(np.float32(1e-7))
+    assert np.allclose(y[2], [x2 / 1e-6, x2 / 1e-6], rtol=1e-15)
+
+
+def test_normalize_matches_numpy_norm():
+    x = np.random.default_rng(4).standard_normal((200, 37)).astype(np.float32)
+    y = oracle.normalize(x)
+    ref = x.astype(np.float64) / np.linalg.norm(x.astype(np.float64), axis=1, keepdims=True)
+    assert np.allclose(y, ref, rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("dtype,tol", [("f32", 1e-6), ("bf16", 2 ** -7), ("fp8", 2 ** -3)])
+def test_prepare_unit_norm_and_elementwise(dtype, tol):
+    x = np.random.default_rng(5).standard_normal((300, 64)).astype(np.float32)
+    codes, scale = oracle.prepare(x, dtype)
+    v = oracle.decode(codes, dtype, scale)
+    y = oracle.normalize(x)
+    # every element within half a step of its exact normalised value
+    if dtype == "f32":
+        assert np.allclose(v, y, rtol=2 ** -24, atol=0)
+    elif dtype == "bf16":
+        assert np.all(np.abs(v - y) <= np.abs(y) * 2 ** -8 + 2.0 ** -134)
+    else:
+        step = np.maximum(np.abs(y / scale[:, None]), 2.0 ** -6)
+        ulp = 2.0 ** (np.floor(np.log2(step)) - 3)
+        assert np.all(np.abs(v / scale[:, None] - y / scale[:, None]) <= ulp / 2 + 1e-18)
+        assert np.all(np.abs(v / scale[:, None]).max(axis=1) <= 448)
+    norms = np.linalg.norm(v, axis=1)
+    assert np.all(np.abs(norms - 1) <= tol)
+
+
+# ------------------------------------------------------------------ top-k
+def _fraction_topk(qv, cv, k, excluded=()):
+    """Exact rational brute force: Fractions, Python's sorted with a (-score, id) key."""
+    qf = [[Fraction(float(a)) for a in row] for row in qv]
+    cf = [[Fraction(float(a)) for a in row] for row in cv]
+    out = []
+    for q in qf:
+        sc = [(sum(a * b for a, b in zip(q, c)), i) for i, c in enumerate(cf) if i not in excluded]
+        sc = sorted(sc, key=lambda t: (-t[0], t[1]))[:k]
+        out.append(sc)
+    return out
+
+
+@pytest.mark.parametrize("c_dtype,q_dtype", [("f32", "f32"), ("bf16", "bf16"), ("fp8", "bf16"),
+                                             ("bf16", "f32")])
+@pytest.mark.parametrize("with_exclusion", [False, True])
+def test_topk_matches_exact_rational_bruteforce(c_dtype, q_dtype, with_exclusion):
+    rng = np.random.default_rng(6)
+    n, d, b, k = 90, 12, 5, 17
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    corpus, scale = oracle.prepare(x, c_dtype)
+    qraw = rng.standard_normal((b, d)).astype(np.float32)
+    queries, _ = oracle.prepare(qraw, q_dtype)
+    excl = set(rng.choice(n, 20, replace=False).tolist()) if with_exclusion else set()
+    bitmap = bitmap_from_ids(np.array(sorted(excl), np.int64), n) if excl else None
+    s, ids = oracle.topk(queries, q_dtype, corpus, c_dtype, k, row_scale=scale, exclude=bitmap,
+                         threads=3)
+    ref = _fraction_topk(oracle.decode(queries, q_dtype), oracle.decode(corpus, c_dtype, scale),
+                         k, excl)
+    for qi in range(b):
+        assert ids[qi].tolist() == [i for _, i in ref[qi]]
+        assert np.allclose(s[qi], [float(v) for v, _ in ref[qi]], rtol=1e-15, atol=1e-17)
+
+
+def test_topk_identity_corpus():
+    d = 16
+    corpus = np.eye(d, dtype=np.float32)
+    for j in range(d):
+        q = np.zeros((1, d), np.float32)
+        q[0, j] = 1.0
+        s, ids = oracle.topk(q, "f32", corpus, "f32", d)
+        assert ids[0, 0] == j and s[0, 0] == 1.0
+        assert ids[0, 1:].tolist() == [i for i in range(d) if i != j]
+        assert np.all(s[0, 1:] == 0.0)
+
+
+def test_topk_all_equal_corpus_tie_rule_and_exclusion():
+    n, d, k = 300, 8, 25
+    corpus = np.full((n, d), 0x3E80, np.uint16)  # every element 0.25
+    q = np.full((2, d), 0x3E80, np.uint16)
+    s, ids = oracle.topk(q, "bf16", corpus, "bf16", k)
+    assert np.all(ids == np.arange(k)) and np.all(s == d * 0.0625)
+    excl = np.array([0, 3, 4, 31, 32, 33, 64], np.int64)
+    s, ids = oracle.topk(q, "bf16", corpus, "bf16", k, exclude=bitmap_from_ids(excl, n))
+    expect = [i for i in range(n) if i not in set(excl.tolist())][:k]
+    assert ids[0].tolist() == expect and ids[1].tolist() == expect
+
+
+def test_exclusion_bit_order():
+    n = 100
+    bm = bitmap_from_ids(np.array([33]), n)
+    assert bm[1] == 2 and bm.sum() == 2
+    corpus = np.zeros((n, 4), np.float32)
+    corpus[33] = 1.0
+    corpus[34] = 0.5
+    s, ids = oracle.topk(np.ones((1, 4), np.float32), "f32", corpus, "f32", 1, exclude=bm)
+    assert ids[0, 0] == 34
+
+
+def _grid_inputs(rng, n, d, b):
+    """bf16-representable values on a coarse grid: every dot product is exact in any order."""
+    cv = rng.integers(-4, 5, (n, d)).astype(np.float32) / 4
+    qv = rng.integers(-4, 5, (b, d)).astype(np.float32) / 4
+    to16 = lambda a: torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return to16(cv), to16(qv), cv.astype(np.float64), qv.astype(np.float64)
+
+
+def test_full_order_matches_numpy_lexsort_and_negation():
+    rng = np.random.default_rng(7)
+    n, d, b = 400, 8, 4
+    c16, q16, cv, qv = _grid_inputs(rng, n, d, b)
+    sc = qv @ cv.T
+    s, ids = oracle.topk(q16, "bf16", c16, "bf16", n)
+    for qi in range(b):
+        order = np.lexsort((np.arange(n), -sc[qi]))
+        assert np.array_equal(ids[qi], order)
+        assert np.array_equal(s[qi], sc[qi][order])
+    # negated query: its full order is the bottom-up order of the original scores
+    neg = (q16 ^ np.uint16(0x8000))
+    s2, ids2 = oracle.topk(neg, "bf16", c16, "bf16", n)
+    for qi in range(b):
+        assert np.array_equal(ids2[qi], np.lexsort((np.arange(n), sc[qi])))
+        assert np.array_equal(s2[qi], -sc[qi][ids2[qi]])
+
+
+def test_k_larger_than_eligible_pads():
+    corpus = np.eye(4, dtype=np.float32)
+    s, ids = oracle.topk(np.ones((1, 4), np.float32), "f32", corpus, "f32", 7,
+                         exclude=bitmap_from_ids(np.array([2]), 4))
+    assert ids[0].tolist() == [0, 1, 3, -1, -1, -1, -1]
+    assert np.all(np.isneginf(s[0, 3:]))
+
+
+def _small_clustered(n=3000, d=32, b=6, clusters=40, seed=11):
+    w = WORKLOADS["bf16_n1m_d128_b16"].replace(n=n, d=d, b=b, clusters=clusters, seed=seed)
+    corpus, _ = oracle.prepare(w.corpus(), "bf16")
+    queries, _ = oracle.prepare(w.queries(), "bf16")
+    return w, corpus, queries
+
+
+def test_k_prefix_and_exclusion_shift():
+    w, corpus, queries = _small_clustered()
+    s1, i1 = oracle.topk(queries, "bf16", corpus, "bf16", 30)
+    s2, i2 = oracle.topk(queries, "bf16", corpus, "bf16", 31)
+    assert np.array_equal(i1, i2[:, :30]) and np.array_equal(s1, s2[:, :30])
+    for qi in range(queries.shape[0]):
+        bm = bitmap_from_ids(np.array([i2[qi, 0]]), w.n)
+        s3, i3 = oracle.topk(queries[qi:qi + 1], "bf16", corpus, "bf16", 30, exclude=bm)
+        assert np.array_equal(i3[0], i2[qi, 1:31]) and np.array_equal(s3[0], s2[qi, 1:31])
+
+
+def test_permutation_invariance():
+    w, corpus, queries = _small_clustered(seed=12)
+    perm = np.random.default_rng(13).permutation(w.n)
+    s1, i1 = oracle.topk(queries, "bf16", corpus, "bf16", 50)
+    s2, i2 = oracle.topk(queries, "bf16", corpus[perm], "bf16", 50)
+    assert np.array_equal(s1, s2)           # score lists bitwise identical
+    for qi in range(queries.shape[0]):
+        untied = np.concatenate([[True], s1[qi, 1:] != s1[qi, :-1]]) & \
+            np.concatenate([s1[qi, :-1] != s1[qi, 1:], [True]])
+        assert np.array_equal(perm[i2[qi]][untied], i1[qi][untied])
+        assert set(perm[i2[qi]].tolist()) == set(i1[qi].tolist()) or s1[qi, -1] == s1[qi, -2]
+
+
+def test_planted_item_and_score_bound():
+    w, _, _ = _small_clustered(seed=14)
+    x = w.corpus()
+    qraw = w.queries()
+    for qi, p in enumerate([5, 777, 2999]):
+        xp = x.copy()
+        xp[p] = qraw[qi]
+        corpus, _ = oracle.prepare(xp, "bf16")
+        q, _ = oracle.prepare(qraw[qi:qi + 1], "bf16")
+        s, ids = oracle.topk(q, "bf16", corpus, "bf16", 5)
+        assert ids[0, 0] == p
+        assert s[0, 0] > s[0, 1] + 0.02
+        qv = oracle.decode(q, "bf16")[0]
+        assert abs(s[0, 0] - float(qv @ qv)) < 1e-12
+        # normalised bf16 rows: every score within (1 + 2^-8)^2 of the unit bound
+        assert np.all(np.abs(s) <= (1 + 2 ** -8) ** 2)
+
+
+def test_tiny_workload_groups():
+    """The toy corpus: each query's best items belong to its own taste group."""
+    w = WORKLOADS["tiny_f32_n400_d16"]
+    corpus, _ = oracle.prepare(w.corpus(), "f32")
+    queries, _ = oracle.prepare(w.queries(), "f32")
+    s, ids = oracle.topk(queries, "f32", corpus, "f32", w.k)
+    g = w.query_clusters()
+    assert np.mean(ids % 8 == g[:, None]) > 0.95
+    assert np.all(s[:, :-1] >= s[:, 1:])
