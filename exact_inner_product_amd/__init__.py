@@ -1,0 +1,199 @@
+"""Python binding of libmips, the gfx950 exhaustive inner-product top-K library.
+
+Argument marshalling only: every step of the path runs in the HIP kernels behind the C ABI
+declared in include/mips.h. PyTorch provides device memory and the current stream.
+Importing works without a GPU; calling needs the built library (``python -m
+exact_inner_product_amd.build``) and raises if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import dataclasses
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmips.so")
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+DTYPE_CODES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+K_MAX = 1024
+
+EXPORTS = (
+    "mips_corpus_bytes", "mips_scale_count", "mips_l2_normalize", "mips_prepare_corpus",
+    "mips_topk_workspace_size", "mips_topk", "mips_set_timing_events", "mips_status_string",
+    "mips_last_hip_error",
+)
+
+
+class MipsError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = lib().mips_status_string(status).decode()
+        if status == 4:
+            msg += f" (hip error {lib().mips_last_hip_error()})"
+        super().__init__(f"{what}: {msg}")
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded libmips.so. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libmips.so is not built ({LIB_PATH}); run "
+                               "`python -m exact_inner_product_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        p, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+        L.mips_corpus_bytes.argtypes = [i64, i32, i32]
+        L.mips_corpus_bytes.restype = i64
+        L.mips_scale_count.argtypes = [i64]
+        L.mips_scale_count.restype = i64
+        L.mips_l2_normalize.argtypes = [p, i64, i32, i32, p, p]
+        L.mips_prepare_corpus.argtypes = [p, i64, i64, i32, i32, p, p, p]
+        L.mips_topk_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32]
+        L.mips_topk_workspace_size.restype = sz
+        L.mips_topk.argtypes = [p, i32, i32, p, p, i32, i64, i32, p, i32, p, p, p, sz, p]
+        L.mips_set_timing_events.argtypes = [p, p]
+        L.mips_status_string.argtypes = [C.c_int]
+        L.mips_status_string.restype = C.c_char_p
+        L.mips_last_hip_error.argtypes = []
+        for f in (L.mips_l2_normalize, L.mips_prepare_corpus, L.mips_topk,
+                  L.mips_set_timing_events, L.mips_last_hip_error):
+            f.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise MipsError(status, what)
+
+
+def _qcode(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported query dtype {t.dtype}")
+
+
+# ---------------------------------------------------------------- normalise
+def l2_normalize(x: torch.Tensor, out_dtype: str = "f32") -> torch.Tensor:
+    """Row-wise x / sqrt(max(sum x^2, 1e-12)) on the GPU; returns float32 or bfloat16."""
+    assert x.is_cuda and x.dtype == torch.float32 and x.dim() == 2
+    x = x.contiguous()
+    out = torch.empty(x.shape, dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16,
+                      device=x.device)
+    _check(lib().mips_l2_normalize(_ptr(x), x.shape[0], x.shape[1], DTYPE_CODES[out_dtype],
+                                   _ptr(out), _stream(x.device)), "mips_l2_normalize")
+    return out
+
+
+# ------------------------------------------------------------------- corpus
+@dataclasses.dataclass
+class Corpus:
+    """A packed, normalised index in the fragment-tiled layout of include/mips.h."""
+    packed: torch.Tensor               # uint8 [mips_corpus_bytes]
+    row_scale: Optional[torch.Tensor]  # float32 [mips_scale_count] (fp8 only)
+    n: int
+    d: int
+    dtype: str
+
+    @property
+    def code(self) -> int:
+        return DTYPE_CODES[self.dtype]
+
+
+def corpus_bytes(n: int, d: int, dtype: str) -> int:
+    return int(lib().mips_corpus_bytes(n, d, DTYPE_CODES[dtype]))
+
+
+def empty_corpus(n: int, d: int, dtype: str, device="cuda") -> Corpus:
+    nbytes = corpus_bytes(n, d, dtype)
+    if nbytes < 0:
+        raise MipsError(2, "mips_corpus_bytes")
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    scale = None
+    if dtype == "fp8":
+        scale = torch.empty(int(lib().mips_scale_count(n)), dtype=torch.float32, device=device)
+    return Corpus(packed, scale, n, d, dtype)
+
+
+def prepare_rows(corpus: Corpus, x: torch.Tensor, row_offset: int) -> None:
+    """Normalise raw rows x (float32 [rows, d], device) and pack them at row_offset."""
+    assert x.is_cuda and x.dtype == torch.float32 and x.dim() == 2 and x.shape[1] == corpus.d
+    x = x.contiguous()
+    _check(lib().mips_prepare_corpus(_ptr(x), x.shape[0], row_offset, corpus.d, corpus.code,
+                                     _ptr(corpus.packed), _ptr(corpus.row_scale),
+                                     _stream(x.device)), "mips_prepare_corpus")
+
+
+def prepare_corpus(x: torch.Tensor, dtype: str) -> Corpus:
+    """Normalise and pack a whole raw corpus (float32 [n, d] on the GPU)."""
+    c = empty_corpus(x.shape[0], x.shape[1], dtype, x.device)
+    prepare_rows(c, x, 0)
+    return c
+
+
+# -------------------------------------------------------------------- top-k
+def workspace_size(b: int, n: int, d: int, k: int, query_dtype: str, corpus_dtype: str) -> int:
+    return int(lib().mips_topk_workspace_size(b, n, d, k, DTYPE_CODES[query_dtype],
+                                              DTYPE_CODES[corpus_dtype]))
+
+
+def empty_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    # torch's caching allocator returns at least 512-byte aligned blocks
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def topk(queries: torch.Tensor, corpus: Corpus, k: int, exclude: Optional[torch.Tensor] = None,
+         workspace: Optional[torch.Tensor] = None,
+         out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None
+         ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Top-k by inner product: (scores float32 [b, k], ids int32 [b, k]).
+
+    queries: float32 or bfloat16 [b, d] on the GPU, L2-normalised.
+    exclude: optional int32/uint32-bit bitmap [ceil(n/32)] on the GPU (bit i of the corpus
+    set => id i is never returned).
+    """
+    assert queries.is_cuda and queries.dim() == 2 and queries.shape[1] == corpus.d
+    queries = queries.contiguous()
+    b = queries.shape[0]
+    qc = _qcode(queries)
+    if workspace is None:
+        nbytes = lib().mips_topk_workspace_size(b, corpus.n, corpus.d, k, qc, corpus.code)
+        if nbytes == 0:
+            raise MipsError(2, "mips_topk_workspace_size")
+        workspace = empty_workspace(nbytes, queries.device)
+    if out is None:
+        scores = torch.empty((b, k), dtype=torch.float32, device=queries.device)
+        ids = torch.empty((b, k), dtype=torch.int32, device=queries.device)
+    else:
+        scores, ids = out
+    if exclude is not None:
+        assert exclude.is_cuda and exclude.dtype in (torch.int32, torch.uint32)
+        assert exclude.numel() >= (corpus.n + 31) // 32
+        exclude = exclude.contiguous()
+    _check(lib().mips_topk(_ptr(queries), qc, b, _ptr(corpus.packed), _ptr(corpus.row_scale),
+                           corpus.code, corpus.n, corpus.d, _ptr(exclude), k, _ptr(scores),
+                           _ptr(ids), _ptr(workspace), workspace.numel(),
+                           _stream(queries.device)), "mips_topk")
+    return scores, ids
+
+
+def set_timing_events(before, after) -> None:
+    """Record hipEvents around the main score kernel of later topk calls (None, None stops)."""
+    lib().mips_set_timing_events(before, after)

@@ -1,0 +1,39 @@
+// host.h -- host-side helpers of the libmips C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mips.h"
+
+namespace mips {
+
+// Records the HIP error of the last failed launch on this thread.
+void set_last_hip_error(hipError_t e);
+
+// Returns MIPS_OK, or records the launch error and returns MIPS_ERR_HIP.
+inline int check_launch() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_last_hip_error(e);
+    return MIPS_ERR_HIP;
+  }
+  return MIPS_OK;
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline bool corpus_d_supported(int dtype, int d) {
+  if (dtype == MIPS_FP8_E4M3) return d == 64 || d == 128 || d == 256;
+  if (dtype == MIPS_F32 || dtype == MIPS_BF16)
+    return d == 16 || d == 32 || d == 64 || d == 128 || d == 256;
+  return false;
+}
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+// Timing hook of mips_set_timing_events.
+void timing_events(hipEvent_t* before, hipEvent_t* after);
+
+}  // namespace mips

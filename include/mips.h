@@ -1,0 +1,172 @@
+/*
+ * mips.h -- C ABI of the MI355X (gfx950) exhaustive inner-product top-K library.
+ *
+ * The operation is the serving step of two-tower retrieval: a batch of L2-normalised
+ * user embeddings queries[B, D] is scored by dot product against a precomputed,
+ * L2-normalised candidate index corpus[N, D], and each user gets its K best candidates
+ * (Phoenix README, "How Retrieval Works", steps 1-4; `RecsysTwoTowerModel.forward` in
+ * recsys_two_tower_model.py, x-algorithm Phoenix, which scores the users against the
+ * whole index, masks it with one shared type mask and takes a sorted top-min(k, N)).
+ * The score matrix is never written to memory.
+ *
+ * Conventions shared by every entry point:
+ *  - All buffers are caller-owned. Pointers marked "device" are HIP device memory;
+ *    the library never allocates, frees or synchronises. Work is enqueued on
+ *    `stream` (a hipStream_t; NULL is the default stream) and the call returns after
+ *    enqueueing. Results are visible once the stream has reached that point.
+ *  - Arguments are validated on the host before anything is enqueued. On any error
+ *    nothing is enqueued and no output is touched. A failed launch returns
+ *    MIPS_ERR_HIP; mips_last_hip_error() then gives the HIP error code (per thread).
+ *    Faults inside kernels surface at the caller's next synchronisation.
+ *  - Inputs must be finite. NaN and infinities are not supported.
+ *  - Element types: MIPS_F32 (IEEE binary32), MIPS_BF16 (the upper 16 bits of a
+ *    binary32), MIPS_FP8_E4M3 (OCP 8-bit float E4M3: bias 7, 3 mantissa bits, no
+ *    infinities, max 448), the last always with one float scale per row.
+ */
+#ifndef MIPS_H
+#define MIPS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Entry points are the only symbols the shared library exports. */
+#define MIPS_API __attribute__((visibility("default")))
+
+#define MIPS_F32 0
+#define MIPS_BF16 1
+#define MIPS_FP8_E4M3 2
+
+#define MIPS_OK 0
+#define MIPS_ERR_INVALID_ARG 1
+#define MIPS_ERR_UNSUPPORTED 2
+#define MIPS_ERR_WORKSPACE 3
+#define MIPS_ERR_HIP 4
+
+/* Largest supported K. */
+#define MIPS_K_MAX 1024
+
+/*
+ * Packed corpus layout ("fragment-tiled"). Rows are grouped in blocks of 32
+ * (N is padded up to a multiple of 32 with zero rows). Block g covers rows
+ * 32g..32g+31 and occupies 32*D*E bytes (E = 4, 2 or 1 bytes per element), split into
+ * 1 KiB chunks of 64 slots x 16 bytes. Slot s of chunk c holds row 32g + (s & 31) and
+ * the following dimensions, with h = s >> 5 and t the element index inside the slot:
+ *   MIPS_F32      (4 per slot):  dim = 8c + 2t + h
+ *   MIPS_BF16     (8 per slot):  dim = 16c + 8h + t
+ *   MIPS_FP8_E4M3 (16 per slot): dim = 64(c >> 1) + 32h + 16(c & 1) + t
+ * Every 16-byte slot is exactly one lane's operand of the gfx950 32x32 MFMA, so the
+ * score kernel streams the corpus from HBM with fully coalesced 1 KiB wave loads and
+ * no LDS transpose. For MIPS_FP8_E4M3 the per-row scale array has one float per padded
+ * row; every scale is a power of two (see mips_prepare_corpus).
+ */
+
+/* Bytes of a packed corpus of n rows (n >= 1) and width d; -1 if unsupported. */
+MIPS_API int64_t mips_corpus_bytes(int64_t n, int32_t d, int32_t dtype);
+
+/* Number of floats in the per-row scale array of an n-row corpus (n rounded up to 32). */
+MIPS_API int64_t mips_scale_count(int64_t n);
+
+/*
+ * mips_l2_normalize -- y = x / sqrt(max(sum_d x^2, 1e-12)) per row, the form of
+ * `_l2_normalize_candidates` and of the user-representation normalisation in
+ * recsys_two_tower_model.py. Computed in fp32; the bf16 output is rounded to nearest
+ * even.
+ *   src   device, float [rows, d] row-major, finite.
+ *   rows  >= 0 (0 enqueues nothing); d in [1, 4096].
+ *   out_dtype  MIPS_F32 or MIPS_BF16.
+ *   dst   device, [rows, d] row-major of out_dtype; may not alias src.
+ * Errors: INVALID_ARG for NULL pointers, rows < 0, d out of range, misaligned pointers
+ * (4 bytes for float, 2 for bf16); UNSUPPORTED for another out_dtype.
+ */
+MIPS_API int mips_l2_normalize(const float *src, int64_t rows, int32_t d, int32_t out_dtype, void *dst,
+                      void *stream);
+
+/*
+ * mips_prepare_corpus -- the offline index build: normalise raw rows as
+ * mips_l2_normalize does and pack them into the fragment-tiled layout ("normalise once
+ * at index time; store f16/int8", "Two-tower retrieval", mhtirogla.ai, section
+ * "Implementation notes"; the bf16 `post_embeddings` index of recsys_two_tower_model.py).
+ *   src         device, float [rows, d] row-major: logical rows
+ *               row_offset .. row_offset+rows-1 of the corpus.
+ *   row_offset  multiple of 32 (lets a large corpus be packed in chunks).
+ *   rows        >= 1. If rows is not a multiple of 32, this must be the last chunk: the
+ *               rest of the last block is written as zero rows (scale 1).
+ *   d           16, 32, 64, 128 or 256 (64, 128, 256 for MIPS_FP8_E4M3).
+ *   dtype       MIPS_F32 (rounded to nearest), MIPS_BF16 (nearest even) or
+ *               MIPS_FP8_E4M3: per row, scale s = the smallest power of two with
+ *               max|y| <= 448 s (1 for a zero row) and codes = E4M3(y / s), nearest even,
+ *               saturating.
+ *   dst         device, packed corpus of at least mips_corpus_bytes(row_offset + rows).
+ *   row_scale   device float [mips_scale_count(row_offset + rows)] for MIPS_FP8_E4M3
+ *               (entries row_offset.. are written), NULL otherwise.
+ * Errors: INVALID_ARG (NULL, rows < 1, row_offset < 0 or not a multiple of 32, dst not
+ * 16-byte aligned, row_scale missing for fp8), UNSUPPORTED (d or dtype).
+ */
+MIPS_API int mips_prepare_corpus(const float *src, int64_t rows, int64_t row_offset, int32_t d,
+                        int32_t dtype, void *dst, float *row_scale, void *stream);
+
+/*
+ * mips_topk_workspace_size -- bytes of device workspace mips_topk needs for these
+ * sizes with its default candidate capacity. A larger workspace raises the per-query
+ * candidate capacity; see mips_topk. Returns 0 for unsupported arguments.
+ */
+MIPS_API size_t mips_topk_workspace_size(int32_t b, int64_t n, int32_t d, int32_t k,
+                                int32_t query_dtype, int32_t corpus_dtype);
+
+/*
+ * mips_topk -- exact top-k by inner product of every query against every corpus row
+ * that the exclusion bitmap does not mask ("already seen"), with ties broken by
+ * score descending, then id ascending.
+ *   queries      device, [b, d] row-major, query_dtype MIPS_F32 or MIPS_BF16, assumed
+ *                L2-normalised (use mips_l2_normalize); 4-byte aligned.
+ *   b            >= 1.
+ *   corpus       device, packed by mips_prepare_corpus (n rows, width d, corpus_dtype);
+ *                16-byte aligned.
+ *   row_scale    device, per-row scales for MIPS_FP8_E4M3 (NULL otherwise).
+ *   corpus_dtype with query_dtype: F32/F32, BF16 with F32 or BF16 queries (queries are
+ *                rounded to bf16), FP8_E4M3 with F32 or BF16 queries (each query row is
+ *                quantised to E4M3 with its own power-of-two scale, the rule of
+ *                mips_prepare_corpus).
+ *   n            1 .. 2^31 - 64.  d: as mips_prepare_corpus.
+ *   exclude      device or NULL: uint32 [ceil(n/32)]; bit (i & 31) of word (i >> 5) set
+ *                means id i is never returned. One bitmap serves the whole batch.
+ *   k            1 .. MIPS_K_MAX.
+ *   out_scores   device float [b, k]; out_ids device int32 [b, k]. Row q holds query q's
+ *                min(k, eligible) best (score, id) pairs, score descending then id
+ *                ascending; remaining slots are (-INFINITY, -1). Scores are fp32
+ *                accumulations of the stored operands (no temperature is applied).
+ *   workspace    device, 256-byte aligned, at least mips_topk_workspace_size(...) bytes;
+ *                its contents are undefined between calls. Calls that share a workspace
+ *                must be ordered on one stream.
+ * Errors: INVALID_ARG (NULL where a buffer is required, b/n/k out of range, fp8 without
+ * row_scale, misalignment), UNSUPPORTED (d, k > MIPS_K_MAX, dtype pair), WORKSPACE
+ * (workspace_bytes too small), HIP (a launch failed).
+ */
+MIPS_API int mips_topk(const void *queries, int32_t query_dtype, int32_t b, const void *corpus,
+              const float *row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
+              const uint32_t *exclude, int32_t k, float *out_scores, int32_t *out_ids,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * mips_set_timing_events -- profiling hook (host, per calling thread). When both are
+ * non-NULL, later mips_topk calls on this thread record `before` (a hipEvent_t)
+ * immediately before and `after` immediately after the launch of the main score
+ * kernel, on the call's stream. Pass NULL, NULL to stop. Returns MIPS_OK.
+ */
+MIPS_API int mips_set_timing_events(void *before, void *after);
+
+/* Human-readable name of a status code (host, static storage). */
+MIPS_API const char *mips_status_string(int status);
+
+/* HIP error code of the last MIPS_ERR_HIP returned on this thread (host). */
+MIPS_API int mips_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIPS_H */

@@ -1,0 +1,130 @@
+"""Test helpers: the top-K acceptance rule, the packed-layout decoder and input builders.
+
+The layout decoder follows the byte-layout formula written in include/mips.h; it is test
+code and does not import anything from the library.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+from typing import Optional
+
+import numpy as np
+
+import oracle
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+# Expected error floors: fp32 accumulation of the same stored operands (f32, bf16) and
+# E4M3 quantisation of the queries (fp8). Far above these means a bug even inside TOL.
+FLOOR = {"f32": 2e-6, "bf16": 5e-4, "fp8": 3e-2}
+
+
+def floor_for(c_dtype: str, q_dtype: str) -> float:
+    """f32 queries against a bf16 corpus are rounded to bf16 on the GPU (the oracle keeps
+    them): each term moves by at most 2^-9 of |q_d c_d|, so the score by at most ~2^-9."""
+    if c_dtype == "bf16" and q_dtype == "f32":
+        return 2.0 ** -9 + FLOOR["bf16"]
+    return FLOOR[c_dtype]
+
+
+def threads() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+# ------------------------------------------------------------------- layout
+def untile(packed: np.ndarray, n: int, d: int, dtype: str) -> np.ndarray:
+    """Logical row-major [n, d] element codes of a fragment-tiled buffer (include/mips.h)."""
+    E = {"f32": 4, "bf16": 2, "fp8": 1}[dtype]
+    per = 16 // E
+    nblk = (n + 31) // 32
+    buf = np.asarray(packed, np.uint8)[: nblk * 32 * d * E]
+    elem = buf.view({"f32": np.uint32, "bf16": np.uint16, "fp8": np.uint8}[dtype])
+    nch = 32 * d * E // 1024
+    elem = elem.reshape(nblk, nch, 64, per)
+    c = np.arange(nch)[:, None, None]
+    s = np.arange(64)[None, :, None]
+    t = np.arange(per)[None, None, :]
+    h = s >> 5
+    if dtype == "f32":
+        dim = 8 * c + 2 * t + h
+    elif dtype == "bf16":
+        dim = 16 * c + 8 * h + t
+    else:
+        dim = 64 * (c >> 1) + 32 * h + 16 * (c & 1) + t
+    row = np.broadcast_to(s & 31, dim.shape)
+    out = np.empty((nblk, 32, d), elem.dtype)
+    out[:, row.ravel(), dim.ravel()] = elem.reshape(nblk, -1)
+    out = out.reshape(nblk * 32, d)[:n]
+    return out.view(np.float32) if dtype == "f32" else out
+
+
+# ---------------------------------------------------------------- acceptance
+def check_topk(g_scores: np.ndarray, g_ids: np.ndarray, o_scores: np.ndarray, o_ids: np.ndarray,
+               q_codes: np.ndarray, q_dtype: str, c_codes: np.ndarray, c_dtype: str,
+               row_scale: Optional[np.ndarray], excluded: Optional[set], n: int, tau: float,
+               floor: Optional[float] = None) -> dict:
+    """Acceptance rule for each query row: well-formed output, score errors and the score
+    profile within tau, id sets equal except swaps within tau of the K-th score.
+
+    o_scores/o_ids: the oracle's exact top-K of the same queries (q_codes). Returns stats.
+    """
+    b, k = g_ids.shape
+    excluded = excluded or set()
+    eligible = n - len(excluded)
+    kk = min(k, eligible)
+    stats = {"max_err": 0.0, "max_profile": 0.0, "swaps": 0}
+    for qi in range(b):
+        gi, gs = g_ids[qi], g_scores[qi]
+        # 1. well-formed
+        assert np.all(gi[kk:] == -1) and np.all(np.isneginf(gs[kk:])), (qi, gi[kk:], gs[kk:])
+        ids = gi[:kk]
+        assert np.all((ids >= 0) & (ids < n)), qi
+        assert len(set(ids.tolist())) == kk, "duplicate ids"
+        assert not (set(ids.tolist()) & excluded), "excluded id returned"
+        sc = gs[:kk]
+        assert np.all(np.isfinite(sc))
+        order_ok = (sc[:-1] > sc[1:]) | ((sc[:-1] == sc[1:]) & (ids[:-1] < ids[1:]))
+        assert np.all(order_ok), "GPU list not sorted by (score desc, id asc)"
+        if kk == 0:
+            continue
+        # 2. score error against the exact score of the returned id
+        e = oracle.scores(q_codes, q_dtype, c_codes, c_dtype, np.full(kk, qi), ids,
+                          row_scale=row_scale)
+        err = np.abs(sc - e).max()
+        stats["max_err"] = max(stats["max_err"], float(err))
+        assert err <= tau, f"query {qi}: score error {err} > {tau}"
+        # 3. profile
+        prof = np.abs(sc - o_scores[qi, :kk]).max()
+        stats["max_profile"] = max(stats["max_profile"], float(prof))
+        assert prof <= tau, f"query {qi}: profile error {prof} > {tau}"
+        # 4. id sets
+        diff = set(ids.tolist()) ^ set(o_ids[qi, :kk].tolist())
+        if diff:
+            dl = np.array(sorted(diff), np.int32)
+            ed = oracle.scores(q_codes, q_dtype, c_codes, c_dtype, np.full(dl.size, qi), dl,
+                               row_scale=row_scale)
+            assert np.all(np.abs(ed - o_scores[qi, kk - 1]) <= tau), \
+                f"query {qi}: id swap beyond tolerance"
+            stats["swaps"] += len(diff) // 2
+    if floor is not None:
+        assert stats["max_err"] <= floor, f"error {stats['max_err']} far above the expected floor {floor}"
+    return stats
+
+
+# ------------------------------------------------------------------- inputs
+def oracle_corpus(w, chunk=1 << 20):
+    """Oracle-side packed corpus (row-major codes) of workload w, prepared in parallel."""
+    E = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[w.corpus_dtype]
+    codes = np.empty((w.n, w.d), E)
+    scale = np.empty(w.n, np.float32) if w.corpus_dtype == "fp8" else None
+
+    def work(item):
+        r0, blk = item
+        c, s = oracle.prepare(blk, w.corpus_dtype)
+        codes[r0:r0 + blk.shape[0]] = c
+        if scale is not None:
+            scale[r0:r0 + blk.shape[0]] = s
+
+    with cf.ThreadPoolExecutor(threads()) as ex:
+        list(ex.map(work, w.corpus_chunks(chunk)))
+    return codes, scale

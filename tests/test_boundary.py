@@ -1,0 +1,134 @@
+"""The C ABI without a GPU: the library loads, exports every entry point include/mips.h
+declares, sizes its buffers as documented, and rejects invalid arguments before any HIP
+call (nothing here launches a kernel)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import exact_inner_product_amd as mips
+from tests.mips_check import untile
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mips.h")
+
+F32, BF16, FP8 = 0, 1, 2
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mips.LIB_PATH):
+        from exact_inner_product_amd import build
+        build.build()
+    return mips.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mips_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_exports(L):
+    names = declared_functions()
+    assert set(names) == set(mips.EXPORTS)
+    for name in names:
+        assert hasattr(L, name), name
+    assert mips.lib().mips_status_string(3).decode() == "workspace too small"
+
+
+def test_corpus_bytes(L):
+    assert L.mips_corpus_bytes(1, 128, BF16) == 32 * 128 * 2
+    assert L.mips_corpus_bytes(33, 128, BF16) == 64 * 128 * 2
+    assert L.mips_corpus_bytes(10_000_000, 128, BF16) == 10_000_000 * 256
+    assert L.mips_corpus_bytes(100, 256, FP8) == 128 * 256
+    assert L.mips_corpus_bytes(100, 16, FP8) == -1      # fp8 needs d in {64, 128, 256}
+    assert L.mips_corpus_bytes(100, 48, BF16) == -1
+    assert L.mips_corpus_bytes(0, 128, BF16) == -1
+    assert L.mips_scale_count(1) == 32 and L.mips_scale_count(64) == 64
+
+
+def test_workspace_size(L):
+    ws = L.mips_topk_workspace_size(256, 10_000_000, 128, 500, BF16, BF16)
+    assert ws > 256 * 32768 * 8
+    assert ws < 1 << 30
+    assert L.mips_topk_workspace_size(0, 100, 128, 10, BF16, BF16) == 0
+    assert L.mips_topk_workspace_size(4, 100, 128, 1025, BF16, BF16) == 0
+    assert L.mips_topk_workspace_size(4, 100, 48, 10, BF16, BF16) == 0
+    assert L.mips_topk_workspace_size(4, 100, 128, 10, BF16, F32) == 0  # bf16 queries need a bf16/fp8 corpus
+
+
+def _topk(L, q=0x1000, qdt=BF16, b=4, corpus=0x2000, scale=None, cdt=BF16, n=1000, d=128,
+          excl=None, k=10, out_s=0x3000, out_i=0x4000, ws=0x10000, wsb=1 << 30):
+    vp = lambda x: None if x is None else C.c_void_p(x)
+    return L.mips_topk(vp(q), qdt, b, vp(corpus), vp(scale), cdt, n, d, vp(excl), k, vp(out_s),
+                       vp(out_i), vp(ws), wsb, None)
+
+
+def test_topk_argument_validation(L):
+    assert _topk(L, q=None) == INVALID
+    assert _topk(L, corpus=None) == INVALID
+    assert _topk(L, out_s=None) == INVALID
+    assert _topk(L, ws=None) == INVALID
+    assert _topk(L, b=0) == INVALID
+    assert _topk(L, n=0) == INVALID
+    assert _topk(L, k=0) == INVALID
+    assert _topk(L, k=1025) == UNSUPPORTED
+    assert _topk(L, d=48) == UNSUPPORTED
+    assert _topk(L, cdt=FP8, d=32, scale=0x5000) == UNSUPPORTED
+    assert _topk(L, cdt=FP8) == INVALID                 # fp8 needs row_scale
+    assert _topk(L, qdt=7) == UNSUPPORTED
+    assert _topk(L, cdt=F32) == UNSUPPORTED             # f32 corpus needs f32 queries
+    assert _topk(L, corpus=0x2008) == INVALID           # corpus must be 16-byte aligned
+    assert _topk(L, ws=0x10010) == INVALID              # workspace must be 256-byte aligned
+    assert _topk(L, q=0x1002) == INVALID
+    assert _topk(L, wsb=1024) == WORKSPACE
+    assert _topk(L, n=(1 << 31)) == INVALID
+
+
+def test_normalize_and_prepare_validation(L):
+    vp = C.c_void_p
+    assert L.mips_l2_normalize(None, 4, 8, F32, vp(0x1000), None) == INVALID
+    assert L.mips_l2_normalize(vp(0x1000), 4, 8, FP8, vp(0x2000), None) == UNSUPPORTED
+    assert L.mips_l2_normalize(vp(0x1000), -1, 8, F32, vp(0x2000), None) == INVALID
+    assert L.mips_l2_normalize(vp(0x1000), 0, 8, F32, vp(0x2000), None) == OK  # nothing to do
+    assert L.mips_prepare_corpus(vp(0x1000), 10, 16, 128, BF16, vp(0x2000), None, None) == INVALID
+    assert L.mips_prepare_corpus(vp(0x1000), 10, 0, 128, FP8, vp(0x2000), None, None) == INVALID
+    assert L.mips_prepare_corpus(vp(0x1000), 10, 0, 100, BF16, vp(0x2000), None, None) == UNSUPPORTED
+    assert L.mips_prepare_corpus(vp(0x1000), 0, 0, 128, BF16, vp(0x2000), None, None) == INVALID
+    assert L.mips_prepare_corpus(vp(0x1000), 10, 0, 128, BF16, vp(0x2008), None, None) == INVALID
+
+
+def test_untile_inverts_the_documented_layout():
+    """The test-side decoder against a hand-placed element, per dtype."""
+    import numpy as np
+    for dtype, E in (("f32", 4), ("bf16", 2), ("fp8", 1)):
+        d, n = 128, 40
+        codes = np.arange(n * d, dtype=np.int64).reshape(n, d)
+        buf = np.zeros(2 * 32 * d * E, np.uint8)
+        view = buf.view({4: np.uint32, 2: np.uint16, 1: np.uint8}[E])
+        # place every element by the header formula, written out per element
+        for row in range(n):
+            for dim in range(d):
+                blk, r = divmod(row, 32)
+                if dtype == "f32":
+                    c, rem = divmod(dim, 8)
+                    t, h = divmod(rem, 2)
+                elif dtype == "bf16":
+                    c, rem = divmod(dim, 16)
+                    h, t = divmod(rem, 8)
+                else:
+                    j, w = divmod(dim, 64)
+                    h, w2 = divmod(w, 32)
+                    hi, t = divmod(w2, 16)
+                    c = 2 * j + hi
+                s = r + 32 * h
+                off = blk * 32 * d * E + c * 1024 + s * 16 + t * E
+                view[off // E] = codes[row, dim] % (1 << (8 * E))
+        got = untile(buf, n, d, dtype)
+        want = codes % (1 << (8 * E))
+        if dtype == "f32":
+            got = got.view(np.uint32)
+        assert np.array_equal(got.astype(np.int64), want)

@@ -1,0 +1,249 @@
+"""GPU parity of the HIP path against the CPU oracle (small and ragged shapes, edge cases,
+invariants). Every call goes through the C ABI of libmips.so."""
+import numpy as np
+import pytest
+import torch
+
+import exact_inner_product_amd as mips
+import oracle
+from tests.mips_check import TOL, check_topk, floor_for, untile
+from workloads import Workload, bitmap_from_ids
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    return torch.device("cuda:0")
+
+
+def _workload(n, d, b, k, cdt, qdt, seed, excl=0.0):
+    return Workload("case", "clustered", n=n, d=d, b=b, k=k, corpus_dtype=cdt, query_dtype=qdt,
+                    clusters=max(2, n // 40), exclude_frac=excl, seed=seed)
+
+
+def _gpu_inputs(w, x, qraw, dev):
+    corpus = mips.prepare_corpus(torch.from_numpy(x).to(dev), w.corpus_dtype)
+    q = mips.l2_normalize(torch.from_numpy(qraw).to(dev), w.query_dtype)
+    return corpus, q
+
+
+def _excl_tensor(bitmap, dev):
+    if bitmap is None:
+        return None
+    return torch.from_numpy(bitmap.view(np.int32)).to(dev)
+
+
+def run_case(n, d, b, k, cdt, qdt, seed, excl=0.0, workspace_bytes=None, x=None):
+    dev = _dev()
+    w = _workload(n, d, b, k, cdt, qdt, seed, excl)
+    x = w.corpus() if x is None else x
+    qraw = w.queries()
+    bitmap = w.exclude_bitmap()
+    corpus, q = _gpu_inputs(w, x, qraw, dev)
+    ws = None if workspace_bytes is None else mips.empty_workspace(workspace_bytes, dev)
+    print(f"case n={n} d={d} b={b} k={k} {cdt}/{qdt} excl={excl} seed={seed}", flush=True)
+    s, i = mips.topk(q, corpus, k, _excl_tensor(bitmap, dev), workspace=ws)
+    torch.cuda.synchronize()
+    s, i = s.cpu().numpy(), i.cpu().numpy()
+    c_or, sc_or = oracle.prepare(x, cdt)
+    q_or, _ = oracle.prepare(qraw, qdt)
+    o_s, o_i = oracle.topk(q_or, qdt, c_or, cdt, k, row_scale=sc_or, exclude=bitmap)
+    excluded = set(w.excluded_ids().tolist()) if bitmap is not None else set()
+    return check_topk(s, i, o_s, o_i, q_or, qdt, c_or, cdt, sc_or, excluded, n, TOL[cdt],
+                      floor=floor_for(cdt, qdt))
+
+
+# --------------------------------------------------------------- prepare parity
+@pytest.mark.parametrize("dtype,d", [("f32", 16), ("f32", 64), ("bf16", 32), ("bf16", 128),
+                                     ("bf16", 256), ("fp8", 64), ("fp8", 256)])
+def test_prepare_matches_oracle_codes(dtype, d):
+    dev = _dev()
+    rng = np.random.default_rng(d)
+    n = 1000 + 17
+    x = (rng.standard_normal((n, d)) * rng.uniform(0.01, 30, (n, 1))).astype(np.float32)
+    x[5] = 0.0                         # zero row stays zero (scale 1 for fp8)
+    corpus = mips.prepare_corpus(torch.from_numpy(x).to(dev), dtype)
+    torch.cuda.synchronize()
+    got = untile(corpus.packed.cpu().numpy(), n, d, dtype)
+    want, scale = oracle.prepare(x, dtype)
+    y = oracle.normalize(x)
+    if dtype == "f32":
+        assert np.allclose(got, want, rtol=3e-7, atol=0)
+        return
+    gs = None
+    if dtype == "fp8":
+        gs = corpus.row_scale.cpu().numpy()[:n]
+        same = gs == scale
+        # a scale may differ only where max|y| sits within fp32 rounding of 448 * 2^t
+        amax = np.abs(y).max(axis=1)
+        edge = np.abs(amax / (448 * np.minimum(gs, scale)) - 1) < 1e-6
+        assert np.all(same | edge)
+        assert gs[5] == 1.0
+        assert np.all(corpus.row_scale.cpu().numpy()[n:] == 1.0)   # padding rows
+    gv = oracle.decode(got, dtype, gs)
+    ov = oracle.decode(want, dtype, scale)
+    exact = np.mean(got == want)
+    assert exact > 0.999, f"only {exact:.5f} of the codes match"
+    # every mismatch is one code step at most: |difference| <= one ulp of the larger value
+    ulp_bits = 7 if dtype == "bf16" else 3
+    diff = np.abs(gv - ov)
+    bound = np.maximum(np.abs(gv), np.abs(ov)) * 2.0 ** -ulp_bits + (2.0 ** -9) * (1 if gs is None else np.maximum(gs, scale)[:, None])
+    assert np.all(diff <= bound)
+    assert np.all(got[5] == 0)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_l2_normalize_matches_oracle(out):
+    dev = _dev()
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((333, 100)) * rng.uniform(1e-3, 1e3, (333, 1))).astype(np.float32)
+    x[0] = 0.0
+    x[1] = 1e-8
+    y = mips.l2_normalize(torch.from_numpy(x).to(dev), out)
+    torch.cuda.synchronize()
+    ref = oracle.normalize(x)
+    if out == "f32":
+        got = y.cpu().numpy().astype(np.float64)
+        assert np.allclose(got, ref, rtol=4e-7, atol=1e-30)
+    else:
+        got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+        want, _ = oracle.prepare(x, "bf16")
+        assert np.mean(got == want) > 0.999
+        gv, ov = oracle.decode(got, "bf16"), oracle.decode(want, "bf16")
+        assert np.all(np.abs(gv - ov) <= np.abs(ov) * 2 ** -7 + 1e-30)
+    assert np.all(y.float().cpu().numpy()[0] == 0)
+
+
+# ----------------------------------------------------------------- top-k parity
+DTYPES = [("f32", "f32", 16), ("f32", "f32", 64), ("bf16", "bf16", 128), ("bf16", "bf16", 64),
+          ("bf16", "f32", 32), ("bf16", "bf16", 256), ("fp8", "bf16", 256), ("fp8", "bf16", 64),
+          ("fp8", "f32", 128)]
+SHAPES = [(1, 1, 1), (63, 5, 10), (64, 33, 64), (65, 3, 100), (1000, 40, 10), (9000, 7, 1024),
+          (40000, 37, 100)]
+
+
+@pytest.mark.parametrize("cdt,qdt,d", DTYPES)
+@pytest.mark.parametrize("n,b,k", SHAPES)
+def test_topk_parity(cdt, qdt, d, n, b, k):
+    run_case(n, d, b, k, cdt, qdt, seed=n * 7 + b + d)
+
+
+@pytest.mark.parametrize("cdt,qdt,d", [("bf16", "bf16", 128), ("fp8", "bf16", 128),
+                                       ("f32", "f32", 32)])
+def test_topk_with_exclusion(cdt, qdt, d):
+    run_case(70001, d, 45, 300, cdt, qdt, seed=5, excl=0.05)
+    run_case(3000, d, 6, 50, cdt, qdt, seed=6, excl=0.5)
+
+
+def test_large_batch_multiple_query_blocks():
+    # 2000 queries do not fit one LDS query block: several blocks share each corpus slice
+    run_case(20000, 256, 2000, 20, "fp8", "bf16", seed=8)
+    run_case(20000, 64, 1100, 30, "bf16", "bf16", seed=9)
+
+
+def test_all_excluded_and_k_above_eligible():
+    dev = _dev()
+    n, d = 500, 64
+    w = _workload(n, d, 3, 50, "bf16", "bf16", 10)
+    corpus, q = _gpu_inputs(w, w.corpus(), w.queries(), dev)
+    allx = torch.full(((n + 31) // 32,), -1, dtype=torch.int32, device=dev)
+    s, i = mips.topk(q, corpus, 50, allx)
+    torch.cuda.synchronize()
+    assert torch.all(i == -1) and torch.all(torch.isneginf(s))
+    keep = np.array([3, 77, 499])
+    bm = np.full((n + 31) // 32, 0xFFFFFFFF, np.uint32)
+    for t in keep:
+        bm[t >> 5] &= ~np.uint32(1 << (t & 31))
+    s, i = mips.topk(q, corpus, 50, torch.from_numpy(bm.view(np.int32)).to(dev))
+    torch.cuda.synchronize()
+    i = i.cpu().numpy()
+    assert np.all(np.sort(i[:, :3], axis=1) == keep) and np.all(i[:, 3:] == -1)
+
+
+@pytest.mark.parametrize("n", [2000, 50000])
+def test_all_equal_corpus_ties(n):
+    """Every score ties: the result is ids 0..k-1 (and, with exclusions, the k smallest
+    eligible ids). At n=50000 every item passes the sampled threshold, the candidate lists
+    overflow and the exact rescan runs."""
+    dev = _dev()
+    d, k, b = 64, 37, 3
+    x = np.ones((n, d), np.float32)
+    corpus = mips.prepare_corpus(torch.from_numpy(x).to(dev), "bf16")
+    q = mips.l2_normalize(torch.ones((b, d), device=dev), "bf16")
+    s, i = mips.topk(q, corpus, k)
+    torch.cuda.synchronize()
+    assert np.all(i.cpu().numpy() == np.arange(k))
+    assert torch.all(s == s[0, 0])
+    excl = np.array([0, 1, 5, 31, 32, 36])
+    bm = bitmap_from_ids(excl, n)
+    s, i = mips.topk(q, corpus, k, torch.from_numpy(bm.view(np.int32)).to(dev))
+    torch.cuda.synchronize()
+    want = [t for t in range(n) if t not in set(excl.tolist())][:k]
+    assert np.all(i.cpu().numpy() == np.array(want))
+
+
+def test_small_workspace_forces_exact_rescan():
+    """A workspace with room for 64 candidates per query: lists overflow, every query is
+    rescanned exactly, and the result still matches the oracle."""
+    n, d, b, k = 30000, 128, 9, 40
+    default_cap = min((n + 31) // 32 * 32, max(16 * k, 32768))
+    fixed = mips.workspace_size(b, n, d, k, "bf16", "bf16") - b * default_cap * 8
+    run_case(n, d, b, k, "bf16", "bf16", seed=12, workspace_bytes=fixed + b * 64 * 8)
+
+
+# -------------------------------------------------------------------- invariants
+def _scores_ids(q, corpus, k, excl=None):
+    s, i = mips.topk(q, corpus, k, excl)
+    torch.cuda.synchronize()
+    return s.cpu().numpy(), i.cpu().numpy()
+
+
+def test_determinism_and_batch_invariance():
+    dev = _dev()
+    w = _workload(60000, 128, 70, 200, "bf16", "bf16", 13, excl=0.05)
+    corpus, q = _gpu_inputs(w, w.corpus(), w.queries(), dev)
+    ex = _excl_tensor(w.exclude_bitmap(), dev)
+    s0, i0 = _scores_ids(q, corpus, w.k, ex)
+    for _ in range(5):
+        s1, i1 = _scores_ids(q, corpus, w.k, ex)
+        assert np.array_equal(s0.view(np.uint32), s1.view(np.uint32)) and np.array_equal(i0, i1)
+    for qi in (0, 31, 32, 69):
+        s1, i1 = _scores_ids(q[qi:qi + 1], corpus, w.k, ex)
+        assert np.array_equal(s0[qi].view(np.uint32), s1[0].view(np.uint32))
+        assert np.array_equal(i0[qi], i1[0])
+
+
+def test_corpus_permutation_invariance():
+    dev = _dev()
+    w = _workload(20000, 64, 12, 100, "bf16", "bf16", 14)
+    x = w.corpus()
+    corpus, q = _gpu_inputs(w, x, w.queries(), dev)
+    perm = np.random.default_rng(15).permutation(w.n)
+    corpus_p = mips.prepare_corpus(torch.from_numpy(x[perm]).to(dev), "bf16")
+    s0, i0 = _scores_ids(q, corpus, w.k)
+    s1, i1 = _scores_ids(q, corpus_p, w.k)
+    # per-item fp32 scores do not depend on the row position: identical score lists
+    assert np.array_equal(s0.view(np.uint32), s1.view(np.uint32))
+    for qi in range(w.b):
+        assert set(perm[i1[qi]].tolist()) == set(i0[qi].tolist()) or s0[qi, -1] == s0[qi, -2]
+
+
+def test_planted_item_exclusion_shift_and_k_prefix():
+    dev = _dev()
+    w = _workload(30000, 128, 8, 50, "bf16", "bf16", 16)
+    x = w.corpus()
+    qraw = w.queries()
+    planted = [11, 4095, 29999, 7, 100, 20000, 3, 15000]
+    for qi, p in enumerate(planted):
+        x[p] = qraw[qi]
+    corpus, q = _gpu_inputs(w, x, qraw, dev)
+    s, i = _scores_ids(q, corpus, 51)
+    assert np.array_equal(i[:, 0], planted)
+    s2, i2 = _scores_ids(q, corpus, 50)
+    assert np.array_equal(i2, i[:, :50]) and np.array_equal(s2, s[:, :50])
+    for qi in range(w.b):
+        bm = bitmap_from_ids(np.array([planted[qi]]), w.n)
+        s3, i3 = _scores_ids(q[qi:qi + 1], corpus, 50, torch.from_numpy(bm.view(np.int32)).to(dev))
+        assert np.array_equal(i3[0], i[qi, 1:51])
