@@ -1,0 +1,207 @@
+"""Benchmark of exhaustive inner-product top-K (mips_topk) on one MI355X.
+
+A step is one mips_topk call over a batch that is already resident in HBM: query prep,
+sampled threshold, the fused MFMA score/filter pass and the final merge. Default workload:
+N=10,000,000 x D=128 bf16 corpus (clustered/Zipf, 16384 clusters), B=256 queries, K=500,
+5% of ids excluded. Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvents through the HIP runtime, for timing on the stream the kernels run on."""
+
+    def __init__(self):
+        self.L = C.CDLL("libamdhip64.so")
+        self.L.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.L.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.L.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.L.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self):
+        ev = C.c_void_p()
+        assert self.L.hipEventCreate(C.byref(ev)) == 0
+        return ev
+
+    def elapsed_ms(self, a, b):
+        assert self.L.hipEventSynchronize(b) == 0
+        ms = C.c_float()
+        assert self.L.hipEventElapsedTime(C.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, ev):
+        self.L.hipEventDestroy(ev)
+
+
+def build_gpu_inputs(w, dev, torch, mips):
+    """Raw corpus chunks -> device -> mips_prepare_corpus; queries -> mips_l2_normalize."""
+    corpus = mips.empty_corpus(w.n, w.d, w.corpus_dtype, dev)
+    t_prep = 0.0
+    nbytes_in = 0
+    for r0, blk in w.corpus_chunks():
+        x = torch.from_numpy(blk).to(dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        mips.prepare_rows(corpus, x, r0)
+        torch.cuda.synchronize()
+        t_prep += time.perf_counter() - t0
+        nbytes_in += blk.nbytes
+        del x
+    q = mips.l2_normalize(torch.from_numpy(w.queries()).to(dev), w.query_dtype)
+    bm = w.exclude_bitmap()
+    excl = None if bm is None else torch.from_numpy(bm.view(np.int32)).to(dev)
+    torch.cuda.synchronize()
+    out_bytes = corpus.packed.numel() + (0 if corpus.row_scale is None else corpus.row_scale.numel() * 4)
+    return corpus, q, excl, (nbytes_in + out_bytes) / t_prep / 1e9
+
+
+def cpu_baseline(w, budget_queries):
+    """The oracle as it stands, on the first `budget_queries` queries of the same workload."""
+    import oracle
+    t0 = time.perf_counter()
+    codes, scale = oracle.prepare_chunks(w.corpus_chunks(), w.n, w.d, w.corpus_dtype)
+    q_or, _ = oracle.prepare(w.queries()[:budget_queries], w.query_dtype)
+    bm = w.exclude_bitmap()
+    log(f"oracle inputs ready in {time.perf_counter() - t0:.1f}s")
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.topk(q_or, w.query_dtype, codes, w.corpus_dtype, w.k, row_scale=scale, exclude=bm,
+                threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": budget_queries * w.n / dt, "unit": "scores/s",
+            "cores": min(threads, budget_queries), "kind": "oracle",
+            "sample": f"first {budget_queries} of {w.b} queries against the full corpus "
+                      f"(n={w.n}, d={w.d}, k={w.k}); exact fp64 dot products and a full sort; "
+                      f"{dt:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-queries", type=int, default=0,
+                    help="queries in the CPU-baseline sample (default: host threads)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import exact_inner_product_amd as mips
+    from workloads import HEADLINE, WORKLOADS
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    dev = torch.device("cuda:0")
+    log(f"workload {w.name}: n={w.n} d={w.d} b={w.b} k={w.k} {w.corpus_dtype}")
+    t0 = time.perf_counter()
+    corpus, q, excl, prep_gbs = build_gpu_inputs(w, dev, torch, mips)
+    log(f"inputs resident in HBM after {time.perf_counter() - t0:.1f}s; prepare {prep_gbs:.0f} GB/s")
+
+    wsb = mips.workspace_size(w.b, w.n, w.d, w.k, w.query_dtype, w.corpus_dtype)
+    ws = mips.empty_workspace(wsb, dev)
+    scores = torch.empty((w.b, w.k), dtype=torch.float32, device=dev)
+    ids = torch.empty((w.b, w.k), dtype=torch.int32, device=dev)
+
+    def step():
+        mips.topk(q, corpus, w.k, excl, workspace=ws, out=(scores, ids))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        mips.set_timing_events(pairs[i][0], pairs[i][1])
+        step()
+    mips.set_timing_events(None, None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    main_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    log(f"timed {args.steps} steps in {wall:.3f}s")
+
+    ms_per_step = wall / args.steps * 1e3
+    scores_per_s = w.b * w.n / (ms_per_step / 1e3)
+    E = {"f32": 4, "bf16": 2, "fp8": 1}[w.corpus_dtype]
+    # Algorithmic bytes of the main score pass: every packed corpus row once (plus its
+    # fp8 scale), the exclusion bitmap and the queries.
+    alg_bytes = w.n * w.d * E + (4 * w.n if w.corpus_dtype == "fp8" else 0)
+    alg_bytes += (w.n / 8 if w.exclude_frac > 0 else 0) + w.b * w.d * E
+    flops = 2.0 * w.b * w.n * w.d
+    main_avg = float(np.mean(main_ms)) / 1e3
+    achieved_gbs = alg_bytes / main_avg / 1e9
+    achieved_tflops = flops / main_avg / 1e12
+    t_hbm = alg_bytes / (PEAK_HBM_GBS * 1e9)
+    t_mfma = flops / (PEAK_TFLOPS[w.corpus_dtype] * 1e12)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved_gbs / PEAK_HBM_GBS}
+    else:
+        roof = {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_TFLOPS[w.corpus_dtype],
+                "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_TFLOPS[w.corpus_dtype]}
+    roof["traffic"] = None
+    roof["kernel"] = "score_kernel (main pass)"
+    roof["kernel_avg_us"] = main_avg * 1e6
+    roof["algorithmic_bytes"] = alg_bytes
+    roof["mfma_frac"] = achieved_tflops / PEAK_TFLOPS[w.corpus_dtype]
+
+    result = {
+        "metric": "query-item scores/s (exhaustive inner-product top-K)",
+        "value": scores_per_s,
+        "unit": "scores/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.corpus_dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "n": w.n, "d": w.d, "b": w.b, "k": w.k,
+                   "corpus_dtype": w.corpus_dtype, "query_dtype": w.query_dtype,
+                   "exclude_frac": w.exclude_frac, "clusters": w.clusters},
+        "queries_per_s": w.b / (ms_per_step / 1e3),
+        "prepare_gbs": prep_gbs,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        nq = args.cpu_queries or min(w.b, max(1, min(16, len(os.sched_getaffinity(0)))))
+        log(f"cpu baseline: oracle on {nq} queries")
+        result["cpu_baseline"] = cpu_baseline(w, nq)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -25,6 +25,9 @@ FLAGS = [
     # no packed-fp32 VALU instructions in any generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fvisibility=hidden",
+    # MFMA accumulators in VGPRs, where the top-K epilogue reads them; operands that only
+    # the matrix pipe reads may then live in AGPRs.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -136,7 +136,7 @@ static int dispatch_prepare_d(const float* src, int64_t rows, int64_t row_offset
     case 32: if constexpr (DT != MIPS_FP8_E4M3) return launch_prepare<DT, 32>(src, rows, row_offset, dst, row_scale, s); break;
     case 64: return launch_prepare<DT, 64>(src, rows, row_offset, dst, row_scale, s);
     case 128: return launch_prepare<DT, 128>(src, rows, row_offset, dst, row_scale, s);
-    case 256: return launch_prepare<DT, 256>(src, rows, row_offset, dst, row_scale, s);
+    case 256: if constexpr (DT != MIPS_F32) return launch_prepare<DT, 256>(src, rows, row_offset, dst, row_scale, s); break;
   }
   return MIPS_ERR_UNSUPPORTED;
 }

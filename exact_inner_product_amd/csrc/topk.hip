@@ -30,20 +30,16 @@
 
 namespace mips {
 
-constexpr int kLevels = 8;          // threshold levels per query
-constexpr int kScoreThreads = 512;  // 8 waves
+constexpr int kLevels = 12;         // threshold levels per query
+constexpr int kScoreThreads = 256;  // 4 waves: one per SIMD, up to 512 registers each
 constexpr int kScoreWaves = kScoreThreads / kWave;
 constexpr int kSampleGroups = 8192; // delegates per query (prefix sample of 8192 blocks)
 constexpr int kSelThreads = 256;
-constexpr int kFallbackBuf = 4096;  // fallback candidate buffer (entries)
-constexpr int kLdsScoreBudget = 150 * 1024;  // query block + scales + per-wave thresholds
-
-// Fragments (32-row blocks) per wave tile: keeps the corpus operand at <= 128 VGPRs
-// (a fragment's operand is d * elem_bytes / 8 VGPRs per lane).
-__host__ __device__ constexpr int tile_frags(int ct, int d) {
-  const int r = 1024 / (d * elem_bytes(ct));
-  return r < 1 ? 1 : (r > 8 ? 8 : r);
-}
+constexpr int kLdsScoreBudget = 150 * 1024;  // query block + scales + thresholds + staging
+constexpr int kStageCap = 384;               // staged survivors per wave
+constexpr int kStageBurst = 256;             // room kept free before each group
+constexpr int kMaxQueryBlock = 512;          // queries staged in LDS per workgroup
+constexpr int kRefreshRegs = kMaxQueryBlock / kScoreThreads;  // threshold loads per lane
 
 enum { MODE_SAMPLE = 0, MODE_MAIN = 1 };
 
@@ -68,6 +64,7 @@ struct ScoreArgs {
   const uint32_t* lvl;
   uint32_t* lcnt;
   uint32_t* cnt;
+  uint32_t* ovf;
   uint64_t* cand;
   uint32_t* delegates;
   int G;
@@ -94,29 +91,77 @@ __device__ __forceinline__ void mfma_step(f32x16_t& acc, const u32x4_t* a, const
   }
 }
 
-// Appends one survivor of query q and counts it against the query's levels.
-__device__ __forceinline__ void append_candidate(const ScoreArgs& A, int q, float v, uint32_t id) {
-  const uint32_t key = score_key(v);
+// Appends one survivor (composite key) of query q and counts it against the query's
+// levels L (ascending where set): once K survivors at or above level j exist, level j
+// is a valid threshold and is published with atomicMax.
+__device__ __forceinline__ void append_candidate(const ScoreArgs& A, int q, uint64_t ckey,
+                                                 const uint32_t* L) {
+  const uint32_t key = (uint32_t)(ckey >> 32);
   const uint32_t pos = atomicAdd(&A.cnt[q], 1u);
-  if ((int64_t)pos < A.cap) A.cand[(int64_t)q * A.cap + pos] = composite(key, id);
-  const uint32_t* L = A.lvl + (int64_t)q * kLevels;
+  if ((int64_t)pos < A.cap) A.cand[(int64_t)q * A.cap + pos] = ckey;
   uint32_t* C = A.lcnt + (int64_t)q * kLevels;
+  uint32_t res[kLevels];
 #pragma unroll
-  for (int j = 0; j < kLevels; ++j) {
-    const uint32_t lj = L[j];
-    if (key >= lj && lj != 0xFFFFFFFFu) {
-      const uint32_t c = atomicAdd(&C[j], 1u);
-      if (c + 1u == (uint32_t)A.k) atomicMax(&A.thr[q], lj);
+  for (int j = 0; j < kLevels; ++j)
+    if (key >= L[j] && L[j] != 0xFFFFFFFFu) res[j] = atomicAdd(&C[j], 1u);
+#pragma unroll
+  for (int j = 0; j < kLevels; ++j)
+    if (key >= L[j] && L[j] != 0xFFFFFFFFu && res[j] + 1u == (uint32_t)A.k)
+      atomicMax(&A.thr[q], L[j]);
+}
+
+__device__ __forceinline__ bool is_excluded(const uint32_t* bits, int64_t id) {
+  return bits && ((bits[id >> 5] >> (id & 31)) & 1u);
+}
+
+// Appends a wave's staged survivors (one entry per lane per round).
+__device__ __forceinline__ void flush_staged(const uint64_t* st_key, const uint16_t* st_q, int nst,
+                                          int q0, const uint32_t* lvl_lds, int64_t n,
+                                          const uint32_t* exclude, uint32_t* cnt, uint64_t* cand,
+                                          int64_t cap, uint32_t* lcnt, uint32_t* thr, int k) {
+  const int lane = threadIdx.x & 63;
+  for (int e = lane; e < nst; e += kWave) {
+    const uint64_t ck = st_key[e];
+    const int64_t id = composite_id(ck);
+    const int ql = st_q[e];
+    if (id >= n || is_excluded(exclude, id)) continue;
+    const int q = q0 + ql;
+    const uint32_t* L = lvl_lds + ql * kLevels;
+    const uint32_t key = (uint32_t)(ck >> 32);
+    const uint32_t pos = atomicAdd(&cnt[q], 1u);
+    if ((int64_t)pos < cap) cand[(int64_t)q * cap + pos] = ck;
+    uint32_t* C = lcnt + (int64_t)q * kLevels;
+    for (int j = 0; j < kLevels; ++j) {
+      const uint32_t lj = L[j];
+      if (lj == 0xFFFFFFFFu || key < lj) continue;
+      if (atomicAdd(&C[j], 1u) + 1u == (uint32_t)k) atomicMax(&thr[q], lj);
     }
   }
+}
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Corpus fragments per pipeline stage: at most 2 (16 KiB of corpus per wave and stage for
+// 256-byte rows), so that two stages of corpus operand, two query operands and two sets of
+// accumulators fit one wave's 512 registers.
+__host__ __device__ constexpr int stage_frags(int ct, int d) {
+  const int r = 512 / (d * elem_bytes(ct));
+  return r < 1 ? 1 : (r > 2 ? 2 : r);
 }
 
 template <int CT, int D, int MODE>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs A) {
   constexpr int E = elem_bytes(CT);
   constexpr int NCH = chunks_per_block(CT, D);
-  constexpr int RM = tile_frags(CT, D);
-  constexpr int RG = RM >= 2 ? 2 : 1;  // fragments whose accumulators are live together
+  constexpr int RM = stage_frags(CT, D);
   constexpr int KSTEPS = (CT == MIPS_F32) ? D / 2 : (CT == MIPS_BF16 ? D / 16 : D / 64);
   constexpr int64_t BLK = block_bytes(CT, D);
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -142,7 +187,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs A) {
   const int nq = min(A.qb, A.b32 - q0);
   const int nqf = nq >> 5;
 
-  // Stage the query block (already in operand layout) into LDS.
+  // LDS: query block operand | fp8 query exponents | thresholds (shared by the waves) |
+  // levels | per-wave survivor staging (composite keys, query index).
   {
     const u32x4_t* src = (const u32x4_t*)(A.qtile + (int64_t)q0 * D * E);
     u32x4_t* dst = (u32x4_t*)lds;
@@ -150,107 +196,249 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs A) {
     for (int i = threadIdx.x; i < n16; i += kScoreThreads) dst[i] = src[i];
   }
   int* qexp_lds = (int*)(lds + (size_t)A.qb * D * E);
-  float* thr_lds = (float*)(qexp_lds + A.qb) + wave * A.qb;
+  float* thr_lds = (float*)(qexp_lds + A.qb);
+  uint32_t* lvl_lds = (uint32_t*)(thr_lds + A.qb);
+  uint64_t* st_key = (uint64_t*)(lvl_lds + (size_t)A.qb * kLevels) + wave * kStageCap;
+  uint16_t* st_q = (uint16_t*)((uint64_t*)(lvl_lds + (size_t)A.qb * kLevels) +
+                               kScoreWaves * kStageCap) + wave * kStageCap;
   if (CT == MIPS_FP8_E4M3)
     for (int i = threadIdx.x; i < nq; i += kScoreThreads) qexp_lds[i] = A.qexp[q0 + i];
+  if (MODE == MODE_MAIN) {
+    for (int i = threadIdx.x; i < nq; i += kScoreThreads) {
+      const int q = q0 + i;
+      thr_lds[i] = q < A.b ? key_threshold(A.thr[q]) : INFINITY;
+    }
+    for (int i = threadIdx.x; i < nq * kLevels; i += kScoreThreads) {
+      const int q = q0 + i / kLevels;
+      lvl_lds[i] = q < A.b ? A.lvl[(int64_t)q * kLevels + (i % kLevels)] : 0xFFFFFFFFu;
+    }
+  }
   __syncthreads();
+
+  int st_n = 0;  // staged survivors of this wave (wave-uniform; may exceed the capacity)
+  auto flush = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    flush_staged(st_key, st_q, min(st_n, kStageCap), q0, lvl_lds, A.n, A.exclude, A.cnt, A.cand,
+                 A.cap, A.lcnt, A.thr, A.k);
+    __builtin_amdgcn_wave_barrier();
+    st_n = 0;
+  };
+
+  // Threshold refresh: each wave refreshes its slice of the shared LDS copy. Any published
+  // threshold is valid, so the other waves may read a copy that is one refresh old.
+  uint32_t rv[kRefreshRegs];
+  auto refresh_issue = [&]() {
+#pragma unroll
+    for (int r = 0; r < kRefreshRegs; ++r) {
+      const int i = min(threadIdx.x + r * kScoreThreads, nq - 1);
+      rv[r] = __hip_atomic_load(&A.thr[min(q0 + i, A.b - 1)], __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  auto refresh_commit = [&]() {
+#pragma unroll
+    for (int r = 0; r < kRefreshRegs; ++r) {
+      const int i = threadIdx.x + r * kScoreThreads;
+      if (i < nq && q0 + i < A.b) thr_lds[i] = key_threshold(rv[r]);
+    }
+  };
+
+  // A stage's loads are unconditional: fragments past the end read the last block again
+  // (their ids are >= n and never survive), so the compiler's wait counts stay exact.
+  auto load_stage = [&](u32x4_t (&a)[RM][NCH], int (&sa)[RM], uint32_t (&wd)[RM], int64_t f0) {
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      const int64_t fr = min<int64_t>(f0 + r, A.n32 - 1);
+      const u32x4_t* p = (const u32x4_t*)(A.corpus + fr * BLK) + lane;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) a[r][c] = p[c * (kChunkBytes / 16)];
+      sa[r] = 127;
+      if (CT == MIPS_FP8_E4M3)
+        sa[r] = (int)((__float_as_uint(A.row_scale[fr * kFrag + (lane & 31)]) >> 23) & 0xFFu);
+      wd[r] = 0u;
+      if (MODE == MODE_SAMPLE && A.exclude) wd[r] = A.exclude[fr];
+    }
+  };
+
+  // A query fragment's B operand and this lane's threshold, read from LDS one fragment
+  // ahead of their use.
+  auto load_b = [&](u32x4_t (&bq)[NCH], float& T, int qf) {
+    const u32x4_t* bsrc = (const u32x4_t*)(lds + (size_t)qf * BLK) + lane;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) bq[c] = bsrc[c * (kChunkBytes / 16)];
+    T = (MODE == MODE_MAIN) ? thr_lds[qf * 32 + (lane & 31)] : 0.0f;
+  };
+  auto mfmas = [&](f32x16_t (&acc)[RM], const u32x4_t (&a)[RM][NCH], const int (&sa)[RM],
+                   const u32x4_t (&bq)[NCH], int qf) {
+    const int sb = (CT == MIPS_FP8_E4M3) ? qexp_lds[qf * 32 + (lane & 31)] : 127;
+#pragma unroll
+    for (int g = 0; g < RM; ++g) acc[g] = f32x16_t{};
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int g = 0; g < RM; ++g) mfma_step<CT>(acc[g], a[g], bq, sa[g], sb, s);
+  };
+
+  // Epilogue of one query fragment against the stage's RM corpus fragments.
+  // Sample mode: per-(query, block) maxima. Main mode, fast part: one max per fragment
+  // (16 scores per lane) and a ballot of `max >= threshold`, branch-free so it can be
+  // interleaved with the next fragment's MFMAs.
+  auto epi_sample = [&](const f32x16_t (&acc)[RM], const uint32_t (&wd)[RM], int64_t f0, int qf) {
+    const int q = q0 + qf * 32 + (lane & 31);
+#pragma unroll
+    for (int g = 0; g < RM; ++g) {
+      const int64_t frag = f0 + g;
+      const uint32_t word = wd[g];
+      float m = neg_inf();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = acc_row(i, lane);
+        const bool ok = (frag * kFrag + row < A.n) && !((word >> row) & 1u);
+        m = ok ? fmaxf(m, acc[g][i]) : m;
+      }
+      m = fmaxf(m, __shfl_xor(m, 32, kWave));
+      if (lane < 32 && frag < A.G && q < A.b)
+        A.delegates[(int64_t)q * A.G + frag] = (m == neg_inf()) ? 0u : score_key(m);
+    }
+  };
+  auto epi_fast = [&](const f32x16_t (&acc)[RM], const float T, uint64_t (&hit)[RM]) {
+#pragma unroll
+    for (int g = 0; g < RM; ++g) {
+      float m = acc[g][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) m = fmaxf(m, acc[g][i]);
+      hit[g] = __ballot(m >= T);
+    }
+  };
+  // Rare part: a fragment that cleared the threshold is resolved by 4-row blocks, then
+  // value by value with ballot + mbcnt compaction into the wave's staging buffer. The
+  // block and value loops index the accumulators with a wave-uniform runtime index and
+  // stay rolled, so the rare path adds little code to the MFMA loop.
+  auto epi_slow = [&](const f32x16_t (&acc)[RM], const uint64_t (&hit)[RM], int64_t f0, int qf,
+                      const float T) {
+    const int ql = qf * 32 + (lane & 31);  // query within the block
+    const int q = q0 + ql;
+#pragma unroll
+    for (int g = 0; g < RM; ++g) {
+      if (!hit[g]) continue;
+      const int64_t frag = f0 + g;
+#pragma unroll 1
+      for (int bb = 0; bb < 4; ++bb) {
+        const float pm = fmaxf(fmaxf(acc[g][4 * bb], acc[g][4 * bb + 1]),
+                               fmaxf(acc[g][4 * bb + 2], acc[g][4 * bb + 3]));
+        if (!__ballot(pm >= T)) continue;
+#pragma unroll 1
+        for (int i = 4 * bb; i < 4 * bb + 4; ++i) {
+          const float v = acc[g][i];
+          const bool pass = v >= T && q < A.b;
+          const uint64_t bm = __ballot(pass);
+          if (!bm) continue;
+          const int pos = st_n + (int)__builtin_amdgcn_mbcnt_hi(
+                                     (uint32_t)(bm >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+          if (pass) {
+            const int64_t id = frag * kFrag + acc_row(i, lane);
+            if (pos < kStageCap) {
+              st_key[pos] = composite(score_key(v), (uint32_t)id);
+              st_q[pos] = (uint16_t)ql;
+            } else {
+              atomicOr(&A.ovf[q], 1u);  // no room: the query is rescanned exactly
+            }
+          }
+          st_n += __popcll(bm);
+        }
+      }
+    }
+  };
+
+  // One stage against every query fragment, software-pipelined over the fragments: the
+  // MFMAs of fragment qf+1 and the LDS reads of fragment qf+2's operand are issued before
+  // the epilogue of fragment qf, so the epilogue (and its rare path) runs while the matrix
+  // pipe works on the next fragment.
+  auto compute_stage = [&](const u32x4_t (&a)[RM][NCH], const int (&sa)[RM],
+                           const uint32_t (&wd)[RM], int64_t f0) {
+    u32x4_t b0[NCH], b1[NCH];
+    f32x16_t c0[RM], c1[RM];
+    uint64_t hit[RM];
+    float t0, t1, tc0, tc1;  // thresholds: loaded (t*) and in use (tc*)
+    load_b(b0, t0, 0);
+    load_b(b1, t1, min(1, nqf - 1));
+    mfmas(c0, a, sa, b0, 0);
+    tc0 = t0;
+    int qf = 0;
+    for (;;) {
+      // c0 holds fragment qf; b1 holds fragment qf+1's operand.
+      if (MODE == MODE_MAIN && st_n > kStageCap - kStageBurst) flush();
+      const bool more0 = qf + 1 < nqf;
+      if (more0) {
+        mfmas(c1, a, sa, b1, qf + 1);
+        tc1 = t1;
+        load_b(b0, t0, min(qf + 2, nqf - 1));
+      }
+      if (MODE == MODE_SAMPLE) {
+        epi_sample(c0, wd, f0, qf);
+      } else {
+        epi_fast(c0, tc0, hit);
+        epi_slow(c0, hit, f0, qf, tc0);
+      }
+      if (!more0) break;
+      ++qf;
+      // c1 holds fragment qf; b0 holds fragment qf+1's operand.
+      if (MODE == MODE_MAIN && st_n > kStageCap - kStageBurst) flush();
+      const bool more1 = qf + 1 < nqf;
+      if (more1) {
+        mfmas(c0, a, sa, b0, qf + 1);
+        tc0 = t0;
+        load_b(b1, t1, min(qf + 2, nqf - 1));
+      }
+      if (MODE == MODE_SAMPLE) {
+        epi_sample(c1, wd, f0, qf);
+      } else {
+        epi_fast(c1, tc1, hit);
+        epi_slow(c1, hit, f0, qf, tc1);
+      }
+      if (!more1) break;
+      ++qf;
+    }
+  };
 
   const int64_t t_begin = (int64_t)slice * A.ntiles / A.nslices;
   const int64_t t_end = (int64_t)(slice + 1) * A.ntiles / A.nslices;
 
-  for (int64_t t = t_begin + wave; t < t_end; t += kScoreWaves) {
-    const int64_t f0 = t * RM;
-    u32x4_t a[RM][NCH];
-    int sa[RM];
-#pragma unroll
-    for (int r = 0; r < RM; ++r) {
-      const bool live = f0 + r < A.nfrag;
-      const u32x4_t* p = (const u32x4_t*)(A.corpus + (f0 + r) * BLK) + lane;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) a[r][c] = live ? p[c * (kChunkBytes / 16)] : u32x4_t{0u, 0u, 0u, 0u};
-      sa[r] = 127;
-      if (CT == MIPS_FP8_E4M3 && live)
-        sa[r] = (int)((__float_as_uint(A.row_scale[(f0 + r) * kFrag + (lane & 31)]) >> 23) & 0xFFu);
-    }
-    if (MODE == MODE_MAIN) {
-      for (int i = lane; i < nq; i += kWave) {
-        const int q = q0 + i;
-        thr_lds[i] = q < A.b ? key_threshold(__hip_atomic_load(&A.thr[q], __ATOMIC_RELAXED,
-                                                               __HIP_MEMORY_SCOPE_AGENT))
-                             : INFINITY;
+  // Two-stage software pipeline: the next stage's corpus fragments are in flight while
+  // the current stage is multiplied against every query fragment.
+  u32x4_t a0[RM][NCH], a1[RM][NCH];
+  int s0[RM], s1[RM];
+  uint32_t w0[RM], w1[RM];
+  int64_t t = t_begin + wave;
+  if (t < t_end) {
+    // Threshold refreshes are committed one stage after they are issued: they were issued
+    // before that stage's corpus loads, so waiting for them then is free.
+    if (MODE == MODE_MAIN) refresh_issue();
+    load_stage(a0, s0, w0, t * RM);
+    for (;;) {
+      const int64_t t1 = t + kScoreWaves;
+      if (MODE == MODE_MAIN) {
+        refresh_commit();
+        refresh_issue();
       }
-    }
-
-    for (int qf = 0; qf < nqf; ++qf) {
-      // The query fragment's whole B operand, loaded once from LDS.
-      u32x4_t bq[NCH];
-      const u32x4_t* bsrc = (const u32x4_t*)(lds + (size_t)qf * BLK) + lane;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) bq[c] = bsrc[c * (kChunkBytes / 16)];
-      const int sb = (CT == MIPS_FP8_E4M3) ? qexp_lds[qf * 32 + (lane & 31)] : 127;
-      const int ql = qf * 32 + (lane & 31);  // query within the block
-      const int q = q0 + ql;
-      const float T = (MODE == MODE_MAIN) ? thr_lds[ql] : 0.0f;
-
-#pragma unroll
-      for (int r0 = 0; r0 < RM; r0 += RG) {
-        f32x16_t acc[RG];
-#pragma unroll
-        for (int g = 0; g < RG; ++g) acc[g] = f32x16_t{};
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-#pragma unroll
-          for (int g = 0; g < RG; ++g) mfma_step<CT>(acc[g], a[r0 + g], bq, sa[r0 + g], sb, s);
-
-        if (MODE == MODE_SAMPLE) {
-#pragma unroll
-          for (int g = 0; g < RG; ++g) {
-            const int64_t frag = f0 + r0 + g;
-            const uint32_t word = (A.exclude && frag < A.nfrag) ? A.exclude[frag] : 0u;
-            float m = neg_inf();
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int row = acc_row(i, lane);
-              const bool ok = (frag * kFrag + row < A.n) && !((word >> row) & 1u);
-              m = ok ? fmaxf(m, acc[g][i]) : m;
-            }
-            m = fmaxf(m, __shfl_xor(m, 32, kWave));
-            if (lane < 32 && frag < A.G && q < A.b)
-              A.delegates[(int64_t)q * A.G + frag] = (m == neg_inf()) ? 0u : score_key(m);
-          }
-        } else {
-          float m = acc[0][0];
-#pragma unroll
-          for (int g = 0; g < RG; ++g)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) m = fmaxf(m, acc[g][i]);
-          if (__ballot(m >= T)) {
-            // Rare path: park this group's scores in a private array and a pass mask,
-            // then append the set bits in one loop (keeps the unrolled code small so the
-            // corpus operand stays in registers).
-            float tv[RG * 16];
-            uint32_t mask = 0u;
-#pragma unroll
-            for (int g = 0; g < RG; ++g)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                tv[g * 16 + i] = acc[g][i];
-                mask |= (acc[g][i] >= T ? 1u : 0u) << (g * 16 + i);
-              }
-            if (q >= A.b) mask = 0u;
-            while (mask) {
-              const int bit = __builtin_ctz(mask);
-              mask &= mask - 1u;
-              const int64_t id = (f0 + r0 + (bit >> 4)) * kFrag + acc_row(bit & 15, lane);
-              bool ok = id < A.n;
-              if (ok && A.exclude) ok = !((A.exclude[id >> 5] >> (id & 31)) & 1u);
-              if (ok) append_candidate(A, q, tv[bit], (uint32_t)id);
-            }
-          }
-        }
+      load_stage(a1, s1, w1, t1 * RM);
+      compute_stage(a0, s0, w0, t * RM);
+      if (t1 >= t_end) break;
+      const int64_t t2 = t1 + kScoreWaves;
+      if (MODE == MODE_MAIN) {
+        refresh_commit();
+        refresh_issue();
       }
+      load_stage(a0, s0, w0, t2 * RM);
+      compute_stage(a1, s1, w1, t1 * RM);
+      if (t2 >= t_end) break;
+      t = t2;
     }
   }
+  if (MODE == MODE_MAIN && st_n > 0) flush();
 }
 
 // ------------------------------------------------------------------ query prep
@@ -260,6 +448,7 @@ __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict
                                                           int* __restrict__ qexp,
                                                           uint32_t* __restrict__ thr,
                                                           uint32_t* __restrict__ cnt,
+                                                          uint32_t* __restrict__ ovf,
                                                           uint32_t* __restrict__ lvl,
                                                           uint32_t* __restrict__ lcnt) {
   constexpr int NCH = chunks_per_block(CT, D);
@@ -298,6 +487,7 @@ __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict
   if (lane < 32 && live) {
     thr[q] = 0u;
     cnt[q] = 0u;
+    ovf[q] = 0u;
     for (int j = 0; j < kLevels; ++j) {
       lvl[(int64_t)q * kLevels + j] = 0xFFFFFFFFu;
       lcnt[(int64_t)q * kLevels + j] = 0u;
@@ -306,45 +496,117 @@ __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict
 }
 
 // --------------------------------------------------------------- radix select
-// r-th largest (r >= 1) of n 32-bit keys in LDS, by four 8-bit digit passes.
-__device__ uint32_t select_rth_u32(const uint32_t* keys, int n, int r, uint32_t* hist,
-                                   uint32_t* shared2) {
-  uint32_t prefix = 0u, mask = 0u;
-  int rem = r;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0u;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      const uint32_t key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t acc = 0u, dsel = 0u;
-      for (int dg = 255; dg >= 0; --dg) {
-        if (acc + hist[dg] >= (uint32_t)rem) {
-          dsel = (uint32_t)dg;
-          break;
-        }
-        acc += hist[dg];
-      }
-      shared2[0] = dsel;
-      shared2[1] = (uint32_t)rem - acc;
-    }
-    __syncthreads();
-    prefix |= shared2[0] << shift;
-    mask |= 255u << shift;
-    rem = (int)shared2[1];
-    __syncthreads();
+// Block-wide helpers; every caller runs with kSelThreads (= 256) threads.
+
+struct DigitPick {
+  uint32_t digit, rem, bin;
+};
+
+// hist[0..255]: keys per digit value (under the current prefix). Finds the digit d with
+// fewer than `rem` keys above it and at least `rem` at or above it, by a prefix sum over
+// the bins taken from the top. Returns d, the rank left inside bin d and the bin's size.
+__device__ DigitPick pick_digit(const uint32_t* hist, uint32_t rem, uint32_t* wsum,
+                                DigitPick* out) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const uint32_t h = hist[255 - t];
+  uint32_t c = h;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t u = __shfl_up(c, o, kWave);
+    if (lane >= o) c += u;
   }
-  return prefix;
+  if (lane == kWave - 1) wsum[w] = c;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) c += wsum[i];
+  const uint32_t prev = c - h;
+  if (prev < rem && c >= rem) *out = DigitPick{(uint32_t)(255 - t), rem - prev, h};
+  __syncthreads();
+  const DigitPick r = *out;
+  __syncthreads();
+  return r;
 }
 
-// Descending bitonic sort of p (power of two) 64-bit keys in LDS.
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
+  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Selection state: the keys with (key & mask) >= prefix are the r largest.
+struct Sel64 {
+  uint64_t prefix, mask;
+};
+
+struct SelScratch {
+  uint32_t hist[256];
+  uint32_t wsum[4];
+  DigitPick pick;
+  uint64_t red[8];
+};
+
+// The r largest of n keys (1 <= r <= n), MSD radix select with 8-bit digits starting at
+// the highest bit where the keys differ; stops as soon as the boundary bin holds exactly
+// the remaining rank. With distinct keys exactly r keys satisfy the returned test; with
+// ties, prefix is still a lower bound of the r-th largest key.
+template <typename Get>
+__device__ Sel64 select_top(Get get, int64_t n, int r, SelScratch& S) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  uint64_t lo = ~0ull, hi = 0ull;
+  for (int64_t i = t; i < n; i += kSelThreads) {
+    const uint64_t k = get(i);
+    lo = k < lo ? k : lo;
+    hi = k > hi ? k : hi;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t l2 = shfl_xor_u64(lo, o), h2 = shfl_xor_u64(hi, o);
+    lo = l2 < lo ? l2 : lo;
+    hi = h2 > hi ? h2 : hi;
+  }
+  if (lane == 0) {
+    S.red[w] = lo;
+    S.red[4 + w] = hi;
+  }
+  __syncthreads();
+  lo = S.red[0];
+  hi = S.red[4];
+  for (int i = 1; i < 4; ++i) {
+    lo = S.red[i] < lo ? S.red[i] : lo;
+    hi = S.red[4 + i] > hi ? S.red[4 + i] : hi;
+  }
+  __syncthreads();
+  const uint64_t diff = lo ^ hi;
+  if (diff == 0ull) return Sel64{lo, ~0ull};  // all keys equal
+  int hb = 63 - __builtin_clzll(diff);        // highest bit not yet fixed
+  uint64_t mask = hb == 63 ? 0ull : ~((2ull << hb) - 1ull);
+  uint64_t prefix = lo & mask;
+  uint32_t rem = (uint32_t)r;
+  for (;;) {
+    const int lb = hb >= 7 ? hb - 7 : 0;
+    const int width = hb - lb + 1;
+    const uint64_t dmask = (1ull << width) - 1ull;
+    S.hist[t] = 0u;
+    __syncthreads();
+    for (int64_t i = t; i < n; i += kSelThreads) {
+      const uint64_t k = get(i);
+      if ((k & mask) == prefix) atomicAdd(&S.hist[(k >> lb) & dmask], 1u);
+    }
+    __syncthreads();
+    const DigitPick pk = pick_digit(S.hist, rem, S.wsum, &S.pick);
+    prefix |= (uint64_t)pk.digit << lb;
+    mask |= dmask << lb;
+    rem = pk.rem;
+    if (pk.bin == pk.rem || lb == 0) break;
+    hb = lb - 1;
+  }
+  return Sel64{prefix, mask};
+}
+
+// Descending bitonic sort of p (a power of two) 64-bit keys in LDS.
 __device__ void bitonic_desc(uint64_t* s, int p) {
   for (int size = 2; size <= p; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < (p >> 1); i += blockDim.x) {
+      for (int i = threadIdx.x; i < (p >> 1); i += kSelThreads) {
         const int lo = 2 * stride * (i / stride) + (i % stride);
         const int hi = lo + stride;
         const bool desc = (lo & size) == 0;
@@ -359,26 +621,35 @@ __device__ void bitonic_desc(uint64_t* s, int p) {
   }
 }
 
-// Per query: the K-th largest delegate becomes the starting threshold; the delegates
-// of rank K/2, K/4, ... become the levels.
+__device__ __forceinline__ int pow2_at_least(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// Per query: the K-th largest delegate is the starting threshold (K distinct blocks hold an
+// item at least that good). The delegates of geometrically spaced ranks below K become the
+// levels: once K survivors reach a level, the level is a valid threshold too.
 __global__ __launch_bounds__(kSelThreads) void sample_threshold_kernel(const uint32_t* __restrict__ del,
                                                                        int G, int b, int k,
+                                                                       float rank_ratio,
                                                                        uint32_t* __restrict__ thr,
                                                                        uint32_t* __restrict__ lvl) {
   __shared__ uint32_t keys[kSampleGroups];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh[2];
   __shared__ uint64_t top[2048];
+  __shared__ SelScratch S;
   __shared__ uint32_t ntop;
   const int q = blockIdx.x;
   if (q >= b) return;
-  for (int i = threadIdx.x; i < G; i += blockDim.x) keys[i] = del[(int64_t)q * G + i];
+  for (int i = threadIdx.x; i < G; i += kSelThreads) keys[i] = del[(int64_t)q * G + i];
   if (threadIdx.x == 0) ntop = 0u;
   __syncthreads();
   uint32_t kth = 0u;
-  if (G >= k) kth = select_rth_u32(keys, G, k, hist, sh);
-  // Gather the delegates >= kth (ties may give more than k; keep at most 2048).
-  for (int i = threadIdx.x; i < G; i += blockDim.x) {
+  if (G >= k) {
+    const Sel64 sel = select_top([&](int64_t i) { return (uint64_t)keys[i]; }, G, k, S);
+    kth = (uint32_t)sel.prefix;
+  }
+  for (int i = threadIdx.x; i < G; i += kSelThreads) {
     if (keys[i] >= kth && keys[i] != 0u) {
       const uint32_t slot = atomicAdd(&ntop, 1u);
       if (slot < 2048u) top[slot] = keys[i];
@@ -386,19 +657,23 @@ __global__ __launch_bounds__(kSelThreads) void sample_threshold_kernel(const uin
   }
   __syncthreads();
   const int m = (int)min(ntop, 2048u);
-  for (int i = m + threadIdx.x; i < 2048; i += blockDim.x) top[i] = 0u;
+  const int p = pow2_at_least(m < 2 ? 2 : m);
+  for (int i = m + threadIdx.x; i < p; i += kSelThreads) top[i] = 0u;
   __syncthreads();
-  bitonic_desc(top, 2048);
-  if (threadIdx.x == 0) {
-    thr[q] = kth;
-    for (int j = 0; j < kLevels; ++j) {
-      const int rank = k >> (j + 1);
-      uint32_t v = 0xFFFFFFFFu;
-      if (rank >= 1 && rank <= m) v = (uint32_t)top[rank - 1];
-      if (v == 0u) v = 0xFFFFFFFFu;
-      lvl[(int64_t)q * kLevels + j] = v;
-    }
+  bitonic_desc(top, p);
+  if (threadIdx.x < kLevels) {
+    // Level j sits at sample rank k * rho^(j+1), rho chosen so the last level lands near
+    // the sample rank the final K-th best is expected at (k / rank_ratio).
+    const int j = threadIdx.x;
+    const float rmin = fmaxf(1.0f, 0.5f * (float)k / rank_ratio);
+    const float rho = powf(rmin / (float)k, 1.0f / (float)kLevels);
+    const int rank = (int)ceilf((float)k * powf(rho, (float)(j + 1)));
+    uint32_t v = 0xFFFFFFFFu;
+    if (rank >= 1 && rank < k && rank <= m) v = (uint32_t)top[rank - 1];
+    if (v == 0u) v = 0xFFFFFFFFu;
+    lvl[(int64_t)q * kLevels + j] = v;
   }
+  if (threadIdx.x == 0) thr[q] = kth;
 }
 
 // ---------------------------------------------------------------- final select
@@ -413,58 +688,17 @@ struct SelectArgs {
   int k;
   int64_t cap;
   const uint32_t* cnt;
+  const uint32_t* ovf;
   const uint64_t* cand;
   float* out_scores;
   int32_t* out_ids;
 };
 
-// Selection state of select_top: keys with (key & mask) >= prefix are the r best.
-struct Sel64 {
-  uint64_t prefix, mask;
-};
+constexpr int kSelCache = 6144;  // candidates cached in LDS by the final select
 
-// The r best of n unique 64-bit keys (1 <= r <= n), MSD radix with 8-bit digits; stops
-// as soon as the boundary digit's bin holds exactly the remaining count.
-template <typename Get>
-__device__ Sel64 select_top(Get get, int64_t n, int r, uint32_t* hist, uint64_t* sh) {
-  uint64_t prefix = 0u, mask = 0u;
-  int64_t rem = r;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0u;
-    __syncthreads();
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
-      const uint64_t key = get(i);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int64_t acc = 0;
-      int dsel = 0;
-      for (int dg = 255; dg >= 0; --dg) {
-        if (acc + (int64_t)hist[dg] >= rem) {
-          dsel = dg;
-          break;
-        }
-        acc += hist[dg];
-      }
-      sh[0] = (uint64_t)dsel;
-      sh[1] = (uint64_t)(rem - acc);
-      sh[2] = hist[dsel];
-    }
-    __syncthreads();
-    prefix |= sh[0] << shift;
-    mask |= 255ull << shift;
-    rem = (int64_t)sh[1];
-    const bool done = sh[2] == sh[1];
-    __syncthreads();
-    if (done) break;
-  }
-  return Sel64{prefix, mask};
-}
-
-// Writes the (already gathered, sorted descending) keys of query q, padding the rest.
+// Writes query q's sorted keys (descending) and pads the rest with (-inf, -1).
 __device__ void write_out(const SelectArgs& A, int q, const uint64_t* s, int cnt) {
-  for (int t = threadIdx.x; t < A.k; t += blockDim.x) {
+  for (int t = threadIdx.x; t < A.k; t += kSelThreads) {
     float sc = -INFINITY;
     int32_t id = -1;
     if (t < cnt) {
@@ -476,23 +710,33 @@ __device__ void write_out(const SelectArgs& A, int q, const uint64_t* s, int cnt
   }
 }
 
-__device__ __forceinline__ int pow2_at_least(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
+// Gathers the r selected keys of `get` into out[0..r), sorts them descending.
+template <typename Get>
+__device__ void gather_sort(Get get, int64_t n, int r, Sel64 sel, uint64_t* out, uint32_t* cnt) {
+  if (threadIdx.x == 0) *cnt = 0u;
+  __syncthreads();
+  for (int64_t i = threadIdx.x; i < n; i += kSelThreads) {
+    const uint64_t key = get(i);
+    if ((key & sel.mask) >= sel.prefix) {
+      const uint32_t slot = atomicAdd(cnt, 1u);
+      if (slot < (uint32_t)r) out[slot] = key;
+    }
+  }
+  __syncthreads();
+  const int p = pow2_at_least(r < 2 ? 2 : r);
+  for (int i = r + threadIdx.x; i < p; i += kSelThreads) out[i] = 0u;
+  __syncthreads();
+  bitonic_desc(out, p);
 }
 
-// Exact rescan of query q when its candidate list overflowed: VALU dot products in
-// dimension order, a candidate buffer in LDS pruned by a composite threshold.
+// Exact rescan of query q: VALU dot products in dimension order, candidates buffered in
+// LDS behind a composite-key threshold that rises whenever the buffer is compacted to
+// its k best.
 template <int CT, int D>
-__device__ void fallback_scan(const SelectArgs& A, int q, uint64_t start_thr, uint64_t* buf,
-                              uint32_t* hist, uint64_t* sh, float* qv) {
-  __shared__ uint32_t nbuf;
-  const int lane_t = threadIdx.x;
-  // Query values in fp32 (fp8: code * 2^t, exact).
-  for (int j = lane_t; j < D; j += blockDim.x) {
-    const int64_t off = (int64_t)(q >> 5) * block_bytes(CT, D) +
-                        (packed_offset(CT, D, q & 31, j));
+__device__ void fallback_scan(const SelectArgs& A, int q, uint64_t thr, uint64_t* buf,
+                              uint64_t* sel_buf, SelScratch& S, float* qv, uint32_t* nbuf_p) {
+  for (int j = threadIdx.x; j < D; j += kSelThreads) {
+    const int64_t off = (int64_t)(q >> 5) * block_bytes(CT, D) + packed_offset(CT, D, q & 31, j);
     float v;
     if (CT == MIPS_F32)
       v = *(const float*)(A.qtile + off);
@@ -502,41 +746,25 @@ __device__ void fallback_scan(const SelectArgs& A, int q, uint64_t start_thr, ui
       v = e4m3_to_f32(A.qtile[off]) * exp2_int(A.qexp[q] - 127);
     qv[j] = v;
   }
-  if (threadIdx.x == 0) nbuf = 0u;
+  if (threadIdx.x == 0) *nbuf_p = 0u;
   __syncthreads();
-  uint64_t thr = start_thr;
-  const int round = blockDim.x * 4;
-  for (int64_t base = 0; base < A.n; base += round) {
-    if (nbuf + (uint32_t)round > (uint32_t)kFallbackBuf) {
-      const int m = (int)nbuf;
+  constexpr int kRound = kSelThreads * 4;
+  for (int64_t base = 0; base < A.n; base += kRound) {
+    if (*nbuf_p + (uint32_t)kRound > (uint32_t)kSelCache) {
+      // Compact to the k best and raise the threshold to their lower bound.
+      const int m = (int)*nbuf_p;
       const int r = min(A.k, m);
-      const Sel64 sel = select_top([&](int64_t i) { return buf[i]; }, m, r, hist, sh);
-      __syncthreads();
-      if (threadIdx.x == 0) nbuf = 0u;
-      __syncthreads();
-      // Compact in place through a second pass: keep the r selected keys.
-      uint64_t mine[kFallbackBuf / kSelThreads];
-      int nm = 0;
-      for (int i = threadIdx.x; i < m; i += blockDim.x) mine[nm++] = buf[i];
-      __syncthreads();
-      for (int t = 0; t < nm; ++t)
-        if ((mine[t] & sel.mask) >= sel.prefix) buf[atomicAdd(&nbuf, 1u)] = mine[t];
-      __syncthreads();
-      // New threshold: the smallest kept key once k are held.
-      if ((int)nbuf >= A.k) {
-        uint64_t lo = ~0ull;
-        for (int i = 0; i < (int)nbuf; ++i) lo = buf[i] < lo ? buf[i] : lo;
-        thr = lo > thr ? lo : thr;
-      }
+      const Sel64 sel = select_top([&](int64_t i) { return buf[i]; }, m, r, S);
+      gather_sort([&](int64_t i) { return buf[i]; }, m, r, sel, sel_buf, &S.hist[0]);
+      for (int i = threadIdx.x; i < r; i += kSelThreads) buf[i] = sel_buf[i];
+      if (threadIdx.x == 0) *nbuf_p = (uint32_t)r;
+      if (r == A.k) thr = sel_buf[r - 1] > thr ? sel_buf[r - 1] : thr;
       __syncthreads();
     }
     for (int u = 0; u < 4; ++u) {
-      const int64_t i = base + (int64_t)u * blockDim.x + threadIdx.x;
-      if (i >= A.n) continue;
-      if (A.exclude && ((A.exclude[i >> 5] >> (i & 31)) & 1u)) continue;
+      const int64_t i = base + (int64_t)u * kSelThreads + threadIdx.x;
+      if (i >= A.n || is_excluded(A.exclude, i)) continue;
       float s = 0.0f;
-      float rs = 1.0f;
-      if (CT == MIPS_FP8_E4M3) rs = A.row_scale[i];
       for (int j = 0; j < D; ++j) {
         const int64_t off = packed_offset(CT, D, i, j);
         float c;
@@ -548,76 +776,59 @@ __device__ void fallback_scan(const SelectArgs& A, int q, uint64_t start_thr, ui
           c = e4m3_to_f32(A.corpus[off]);
         s = fmaf(qv[j], c, s);
       }
-      if (CT == MIPS_FP8_E4M3) s *= rs;
+      if (CT == MIPS_FP8_E4M3) s *= A.row_scale[i];
       const uint64_t key = composite(score_key(s), (uint32_t)i);
-      if (key >= thr) buf[atomicAdd(&nbuf, 1u)] = key;
+      if (key >= thr) buf[atomicAdd(nbuf_p, 1u)] = key;
     }
     __syncthreads();
   }
-  const int m = (int)nbuf;
+  const int m = (int)*nbuf_p;
   const int r = min(A.k, m);
-  __shared__ uint32_t nsel;
-  if (threadIdx.x == 0) nsel = 0u;
-  __syncthreads();
   if (r > 0) {
-    const Sel64 sel = select_top([&](int64_t i) { return buf[i]; }, m, r, hist, sh);
-    uint64_t mine[kFallbackBuf / kSelThreads];
-    int nm = 0;
-    for (int i = threadIdx.x; i < m; i += blockDim.x) mine[nm++] = buf[i];
-    __syncthreads();
-    for (int t = 0; t < nm; ++t)
-      if ((mine[t] & sel.mask) >= sel.prefix) buf[atomicAdd(&nsel, 1u)] = mine[t];
-    __syncthreads();
+    Sel64 sel{0ull, 0ull};
+    if (m > r) sel = select_top([&](int64_t i) { return buf[i]; }, m, r, S);
+    gather_sort([&](int64_t i) { return buf[i]; }, m, r, sel, sel_buf, &S.hist[0]);
   }
-  const int p = pow2_at_least(r < 2 ? 2 : r);
-  for (int i = r + threadIdx.x; i < p; i += blockDim.x) buf[i] = 0u;
-  __syncthreads();
-  bitonic_desc(buf, p);
-  write_out(A, q, buf, r);
+  write_out(A, q, sel_buf, r);
 }
 
 template <int CT, int D>
 __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint64_t sh[4];
-  __shared__ uint64_t buf[kFallbackBuf];
+  __shared__ uint64_t cache[kSelCache];
+  __shared__ uint64_t sel_buf[MIPS_K_MAX];
+  __shared__ SelScratch S;
   __shared__ float qv[D];
-  __shared__ uint32_t ngot;
+  __shared__ uint32_t nbuf;
   const int q = blockIdx.x;
   if (q >= A.b) return;
   const int64_t c = A.cnt[q];
   const uint64_t* list = A.cand + (int64_t)q * A.cap;
-  if (c > A.cap) {
-    // Overflow: the stored entries are still valid candidates, so their k-th best is
-    // a lower bound for the exact rescan.
-    uint64_t start = 0u;
-    if (A.cap >= A.k) {
-      const Sel64 sel = select_top([&](int64_t i) { return list[i]; }, A.cap, A.k, hist, sh);
-      // The k-th best stored key is the smallest key with (key & mask) >= prefix;
-      // prefix itself is a lower bound of it.
-      start = sel.prefix;
-    }
+  if (c > A.cap || A.ovf[q] != 0u) {
+    // The list is incomplete. Its stored entries are still real candidates, so their
+    // k-th best bounds the exact rescan from below.
+    uint64_t start = 0ull;
+    const int64_t stored = min<int64_t>(c, A.cap);
+    if (stored >= A.k) start = select_top([&](int64_t i) { return list[i]; }, stored, A.k, S).prefix;
     __syncthreads();
-    fallback_scan<CT, D>(A, q, start, buf, hist, sh, qv);
+    fallback_scan<CT, D>(A, q, start, cache, sel_buf, S, qv, &nbuf);
     return;
   }
   const int r = (int)min<int64_t>(c, A.k);
-  if (threadIdx.x == 0) ngot = 0u;
-  __syncthreads();
   if (r > 0) {
-    Sel64 sel{0u, 0u};
-    if (c > r) sel = select_top([&](int64_t i) { return list[i]; }, c, r, hist, sh);
-    for (int64_t i = threadIdx.x; i < c; i += blockDim.x) {
-      const uint64_t key = list[i];
-      if ((key & sel.mask) >= sel.prefix) buf[atomicAdd(&ngot, 1u)] = key;
+    if (c <= kSelCache) {
+      for (int64_t i = threadIdx.x; i < c; i += kSelThreads) cache[i] = list[i];
+      __syncthreads();
+      auto get = [&](int64_t i) { return cache[i]; };
+      Sel64 sel{0ull, 0ull};
+      if (c > r) sel = select_top(get, c, r, S);
+      gather_sort(get, c, r, sel, sel_buf, &S.hist[0]);
+    } else {
+      auto get = [&](int64_t i) { return list[i]; };
+      const Sel64 sel = select_top(get, c, r, S);
+      gather_sort(get, c, r, sel, sel_buf, &S.hist[0]);
     }
-    __syncthreads();
   }
-  const int p = pow2_at_least(r < 2 ? 2 : r);
-  for (int i = r + threadIdx.x; i < p; i += blockDim.x) buf[i] = 0u;
-  __syncthreads();
-  bitonic_desc(buf, p);
-  write_out(A, q, buf, r);
+  write_out(A, q, sel_buf, r);
 }
 
 // ------------------------------------------------------------------- planning
@@ -626,7 +837,7 @@ struct Plan {
   int64_t n, n32;
   int rm, qb, nqblk, G;
   int64_t ntiles, cap;
-  size_t off_qtile, off_qexp, off_thr, off_cnt, off_lvl, off_lcnt, off_del, off_cand, fixed;
+  size_t off_qtile, off_qexp, off_thr, off_cnt, off_ovf, off_lvl, off_lcnt, off_del, off_cand, fixed;
   size_t lds_score;
 };
 
@@ -646,17 +857,20 @@ static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt)
   p.cdt = cdt;
   p.n = n;
   p.n32 = (n + 31) / 32;
-  p.rm = tile_frags(cdt, d);
+  p.rm = stage_frags(cdt, d);
   p.ntiles = (p.n32 + p.rm - 1) / p.rm;
   const int E = elem_bytes(cdt);
-  // LDS per query: its operand row, its fp8 exponent and one threshold per wave.
-  int qb = kLdsScoreBudget / (d * E + 4 + 4 * kScoreWaves);
+  // LDS per query: its operand row, its fp8 exponent, its threshold and its levels; plus
+  // each wave's survivor staging buffer.
+  const int stage_bytes = kScoreWaves * kStageCap * 10;
+  const int per_query = d * E + 4 + 4 + 4 * kLevels;
+  int qb = (kLdsScoreBudget - stage_bytes) / per_query;
   qb = qb / 32 * 32;
-  if (qb > 2048) qb = 2048;
+  if (qb > kMaxQueryBlock) qb = kMaxQueryBlock;
   if (qb > p.b32) qb = p.b32;
   p.nqblk = (p.b32 + qb - 1) / qb;
   p.qb = ((p.b32 + p.nqblk - 1) / p.nqblk + 31) / 32 * 32;
-  p.lds_score = (size_t)p.qb * d * E + (size_t)p.qb * 4 + (size_t)kScoreWaves * p.qb * 4;
+  p.lds_score = (size_t)p.qb * per_query + (size_t)stage_bytes;
   size_t o = 0;
   p.off_qtile = o;
   o = align256(o + (size_t)p.b32 * d * E);
@@ -665,6 +879,8 @@ static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt)
   p.off_thr = o;
   o = align256(o + (size_t)b * 4);
   p.off_cnt = o;
+  o = align256(o + (size_t)b * 4);
+  p.off_ovf = o;
   o = align256(o + (size_t)b * 4);
   p.off_lvl = o;
   o = align256(o + (size_t)b * kLevels * 4);
@@ -685,6 +901,7 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   int* qexp = (int*)(ws + p.off_qexp);
   uint32_t* thr = (uint32_t*)(ws + p.off_thr);
   uint32_t* cnt = (uint32_t*)(ws + p.off_cnt);
+  uint32_t* ovf = (uint32_t*)(ws + p.off_ovf);
   uint32_t* lvl = (uint32_t*)(ws + p.off_lvl);
   uint32_t* lcnt = (uint32_t*)(ws + p.off_lcnt);
   uint32_t* del = (uint32_t*)(ws + p.off_del);
@@ -692,10 +909,10 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
 
   if (p.qdt == MIPS_F32)
     hipLaunchKernelGGL((prep_queries_kernel<CT, MIPS_F32, D>), dim3(p.b32 / 32), dim3(64), 0, s,
-                       queries, p.b, qtile, qexp, thr, cnt, lvl, lcnt);
+                       queries, p.b, qtile, qexp, thr, cnt, ovf, lvl, lcnt);
   else
     hipLaunchKernelGGL((prep_queries_kernel<CT, MIPS_BF16, D>), dim3(p.b32 / 32), dim3(64), 0, s,
-                       queries, p.b, qtile, qexp, thr, cnt, lvl, lcnt);
+                       queries, p.b, qtile, qexp, thr, cnt, ovf, lvl, lcnt);
   int rc = check_launch();
   if (rc) return rc;
 
@@ -727,6 +944,7 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   A.lvl = lvl;
   A.lcnt = lcnt;
   A.cnt = cnt;
+  A.ovf = ovf;
   A.cand = cand;
   A.delegates = del;
   A.G = p.G;
@@ -749,7 +967,7 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
                        dim3(kScoreThreads), p.lds_score, s, A);
     if ((rc = check_launch())) return rc;
     hipLaunchKernelGGL(sample_threshold_kernel, dim3(p.b), dim3(kSelThreads), 0, s, del, p.G, p.b,
-                       p.k, thr, lvl);
+                       p.k, (float)((double)p.n32 / (double)p.G), thr, lvl);
     if ((rc = check_launch())) return rc;
   }
 
@@ -775,6 +993,7 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   S.k = p.k;
   S.cap = p.cap;
   S.cnt = cnt;
+  S.ovf = ovf;
   S.cand = cand;
   S.out_scores = out_scores;
   S.out_ids = out_ids;
@@ -792,7 +1011,7 @@ static int dispatch_d(const Plan& p, const void* queries, const void* corpus,
     case 32: if constexpr (CT != MIPS_FP8_E4M3) { MIPS_RUN(32); } break;
     case 64: MIPS_RUN(64);
     case 128: MIPS_RUN(128);
-    case 256: MIPS_RUN(256);
+    case 256: if constexpr (CT != MIPS_F32) { MIPS_RUN(256); } break;
   }
 #undef MIPS_RUN
   return MIPS_ERR_UNSUPPORTED;

@@ -95,7 +95,8 @@ MIPS_API int mips_l2_normalize(const float *src, int64_t rows, int32_t d, int32_
  *   row_offset  multiple of 32 (lets a large corpus be packed in chunks).
  *   rows        >= 1. If rows is not a multiple of 32, this must be the last chunk: the
  *               rest of the last block is written as zero rows (scale 1).
- *   d           16, 32, 64, 128 or 256 (64, 128, 256 for MIPS_FP8_E4M3).
+ *   d           16, 32, 64, 128 or 256 (MIPS_F32: up to 128; MIPS_FP8_E4M3: 64, 128,
+ *               256).
  *   dtype       MIPS_F32 (rounded to nearest), MIPS_BF16 (nearest even) or
  *               MIPS_FP8_E4M3: per row, scale s = the smallest power of two with
  *               max|y| <= 448 s (1 for a zero row) and codes = E4M3(y / s), nearest even,

@@ -18,6 +18,7 @@ Functions take and return numpy arrays:
 """
 from __future__ import annotations
 
+import concurrent.futures as _cf
 import ctypes as C
 import os
 import subprocess
@@ -139,6 +140,31 @@ def prepare(x: np.ndarray, dtype: str) -> Tuple[np.ndarray, Optional[np.ndarray]
     _check(lib().oracle_prepare(_ptr(x), rows, d, DTYPES[dtype], _ptr(out), _ptr(scale)),
            "prepare")
     return out, scale
+
+
+def prepare_chunks(chunks, n: int, d: int, dtype: str, threads: Optional[int] = None
+                   ) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """prepare() of a corpus given as (row0, raw rows) chunks, in parallel threads."""
+    codes = np.empty((n, d), {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dtype])
+    scale = np.empty(n, np.float32) if dtype == "fp8" else None
+
+    def work(item):
+        r0, blk = item
+        c, s = prepare(blk, dtype)
+        codes[r0:r0 + blk.shape[0]] = c
+        if scale is not None:
+            scale[r0:r0 + blk.shape[0]] = s
+
+    nt = threads or min(16, default_threads())
+    with _cf.ThreadPoolExecutor(nt) as ex:
+        pending = []
+        for it in chunks:
+            pending.append(ex.submit(work, it))
+            if len(pending) >= nt:          # bound the raw chunks held in memory
+                pending.pop(0).result()
+        for f in pending:
+            f.result()
+    return codes, scale
 
 
 def topk(queries: np.ndarray, q_dtype: str, corpus: np.ndarray, c_dtype: str, k: int,

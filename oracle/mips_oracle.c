@@ -97,9 +97,18 @@ uint16_t oracle_bf16_from_f64(double y)
     return (uint16_t)(sign | (u >> 16));
 }
 
+/* Decoded values of all 256 E4M3 codes, filled once from oracle_e4m3_value. */
+static double g_e4m3[256];
+__attribute__((constructor)) static void fill_e4m3_table(void)
+{
+    for (int c = 0; c < 256; ++c)
+        g_e4m3[c] = oracle_e4m3_value((uint8_t)c);
+}
+
 /* E4M3 code of v by round-to-nearest-even with saturation at 448. 4 significant
  * bits: spacing 2^(e-3) in the binade [2^e, 2^(e+1)); below the smallest normal
- * 2^-6 the spacing stays 2^-9. The code is found by matching the decoded grid. */
+ * 2^-6 the spacing stays 2^-9. The code is found by matching the decoded grid: the
+ * positive codes 0x00..0x7E decode in increasing order, so a binary search finds it. */
 uint8_t oracle_e4m3_from_f64(double v)
 {
     uint8_t sign = signbit(v) ? 0x80u : 0u;
@@ -114,9 +123,16 @@ uint8_t oracle_e4m3_from_f64(double v)
     double r = round_to_grid(a, ldexp(1.0, ex - 3));
     if (r > 448.0)
         r = 448.0;
-    for (int c = 0; c <= 0x7E; ++c)
-        if (oracle_e4m3_value((uint8_t)c) == r)
-            return (uint8_t)(sign | c);
+    int lo = 0, hi = 0x7E;
+    while (lo < hi) {
+        int mid = (lo + hi) / 2;
+        if (g_e4m3[mid] < r)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    if (g_e4m3[lo] == r)
+        return (uint8_t)(sign | lo);
     return 0xFF; /* unreachable for finite v */
 }
 
@@ -207,7 +223,7 @@ static double stored_value(int32_t dtype, const void *base, int64_t idx)
     case OR_BF16:
         return oracle_bf16_value(((const uint16_t *)base)[idx]);
     default:
-        return oracle_e4m3_value(((const uint8_t *)base)[idx]);
+        return g_e4m3[((const uint8_t *)base)[idx]];
     }
 }
 

@@ -5,7 +5,6 @@ code and does not import anything from the library.
 """
 from __future__ import annotations
 
-import concurrent.futures as cf
 import os
 from typing import Optional
 
@@ -114,17 +113,4 @@ def check_topk(g_scores: np.ndarray, g_ids: np.ndarray, o_scores: np.ndarray, o_
 # ------------------------------------------------------------------- inputs
 def oracle_corpus(w, chunk=1 << 20):
     """Oracle-side packed corpus (row-major codes) of workload w, prepared in parallel."""
-    E = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[w.corpus_dtype]
-    codes = np.empty((w.n, w.d), E)
-    scale = np.empty(w.n, np.float32) if w.corpus_dtype == "fp8" else None
-
-    def work(item):
-        r0, blk = item
-        c, s = oracle.prepare(blk, w.corpus_dtype)
-        codes[r0:r0 + blk.shape[0]] = c
-        if scale is not None:
-            scale[r0:r0 + blk.shape[0]] = s
-
-    with cf.ThreadPoolExecutor(threads()) as ex:
-        list(ex.map(work, w.corpus_chunks(chunk)))
-    return codes, scale
+    return oracle.prepare_chunks(w.corpus_chunks(chunk), w.n, w.d, w.corpus_dtype, threads())

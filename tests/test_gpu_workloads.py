@@ -1,0 +1,101 @@
+"""Parity at the five measured workload sizes, in the launch configuration the benchmark
+times (full batch, default workspace). Large workloads are checked on sampled queries that
+the oracle computes one by one; every query is checked for properties that hold at any
+size (well-formed, sorted, no excluded id, scores within the unit bound)."""
+import concurrent.futures as cf
+
+import numpy as np
+import pytest
+import torch
+
+import exact_inner_product_amd as mips
+import oracle
+from tests.mips_check import TOL, check_topk, floor_for, threads
+from workloads import WORKLOADS
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def build_both(w, dev):
+    """One pass over the raw chunks feeds both sides: GPU prepare and oracle prepare."""
+    corpus = mips.empty_corpus(w.n, w.d, w.corpus_dtype, dev)
+    codes = np.empty((w.n, w.d), {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[w.corpus_dtype])
+    scale = np.empty(w.n, np.float32) if w.corpus_dtype == "fp8" else None
+
+    def cpu(r0, blk):
+        c, s = oracle.prepare(blk, w.corpus_dtype)
+        codes[r0:r0 + blk.shape[0]] = c
+        if scale is not None:
+            scale[r0:r0 + blk.shape[0]] = s
+
+    with cf.ThreadPoolExecutor(threads()) as ex:
+        pending = []
+        for r0, blk in w.corpus_chunks():
+            mips.prepare_rows(corpus, torch.from_numpy(blk).to(dev), r0)
+            pending.append(ex.submit(cpu, r0, blk))
+            if len(pending) >= threads():
+                pending.pop(0).result()
+        for f in pending:
+            f.result()
+    qraw = w.queries()
+    q = mips.l2_normalize(torch.from_numpy(qraw).to(dev), w.query_dtype)
+    q_or, _ = oracle.prepare(qraw, w.query_dtype)
+    bm = w.exclude_bitmap()
+    torch.cuda.synchronize()
+    return corpus, q, bm, codes, scale, q_or
+
+
+def run_workload(name, sample):
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[name]
+    print(f"workload {name}: building inputs", flush=True)
+    corpus, q, bm, codes, scale, q_or = build_both(w, dev)
+    excl = None if bm is None else torch.from_numpy(bm.view(np.int32)).to(dev)
+    print(f"workload {name}: mips_topk b={w.b}", flush=True)
+    s, i = mips.topk(q, corpus, w.k, excl)
+    torch.cuda.synchronize()
+    s, i = s.cpu().numpy(), i.cpu().numpy()
+    excluded = set(w.excluded_ids().tolist()) if bm is not None else set()
+    # every query: well-formed and within the unit bound
+    delta = {"f32": 2 ** -23, "bf16": 2 ** -8, "fp8": 2 ** -4}[w.corpus_dtype]
+    kk = min(w.k, w.n - len(excluded))
+    assert np.all(i[:, :kk] >= 0) and np.all(i[:, :kk] < w.n)
+    assert np.all(s[:, :-1] >= s[:, 1:])
+    assert np.all(np.abs(s[:, :kk]) <= (1 + delta) ** 2 + 1e-3)
+    if excluded:
+        ex = np.array(sorted(excluded))
+        assert not np.isin(i, ex).any()
+    # sampled queries against the oracle
+    sel = np.array(sorted(set(sample)), np.int64)
+    print(f"workload {name}: oracle on queries {sel.tolist()}", flush=True)
+    o_s, o_i = oracle.topk(q_or[sel], w.query_dtype, codes, w.corpus_dtype, w.k, row_scale=scale,
+                           exclude=bm, threads=threads())
+    stats = check_topk(s[sel], i[sel], o_s, o_i, q_or[sel], w.query_dtype, codes, w.corpus_dtype,
+                       scale, excluded, w.n, TOL[w.corpus_dtype],
+                       floor=floor_for(w.corpus_dtype, w.query_dtype))
+    print(f"workload {name}: {stats}", flush=True)
+
+
+def test_tiny_f32():
+    run_workload("tiny_f32_n400_d16", range(128))
+
+
+def test_bf16_n1m():
+    run_workload("bf16_n1m_d128_b16", range(16))
+
+
+@pytest.mark.timeout(900)
+def test_bf16_n10m_headline():
+    run_workload("bf16_n10m_d128_b256_excl5", [0, 1, 31, 32, 100, 128, 200, 255])
+
+
+@pytest.mark.timeout(900)
+def test_fp8_n10m():
+    run_workload("fp8_n10m_d256_b4096", [0, 1, 511, 512, 2047, 3000, 4094, 4095])
+
+
+@pytest.mark.timeout(1200)
+def test_bf16_n100m():
+    run_workload("bf16_n100m_d64_b1024", [0, 1023])
