@@ -25,7 +25,7 @@ import numpy as np  # noqa: E402
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_inner_product_amd", "csrc", f)
-                  for f in ("topk.hip", "common.h")]
+                  for f in ("score.h", "score_api.h", "score_inst.hip", "common.h")]
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}
 
 

@@ -1,0 +1,66 @@
+// score_api.h -- the fused score pass of mips_topk: shared constants, its argument block
+// and the launcher that each per-(dtype, width) translation unit instantiates.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace mips {
+
+constexpr int kScoreThreads = 256;  // 4 waves: one per SIMD, up to 512 registers each
+constexpr int kScoreWaves = kScoreThreads / kWave;
+constexpr int kStageCap = 512;      // staged survivors per wave
+constexpr int kStageBurst = 256;    // room kept free before each stage
+constexpr int kStageLds = kScoreWaves * kStageCap * (8 + 2);
+constexpr int kLdsLimit = 160 * 1024;
+constexpr int kMaxSample = 8192;    // sampled 32-row blocks
+constexpr int kSelCache = 6144;     // candidates the final select caches in LDS
+
+enum { MODE_MAIN = 0, MODE_AUX = 1 };
+
+// Corpus blocks per pipeline stage: 16 KiB of corpus per wave and stage (at most 4 blocks).
+__host__ __device__ constexpr int stage_frags(int ct, int d) {
+  const int r = 16384 / (kFrag * d * elem_bytes(ct));
+  return r < 1 ? 1 : (r > 4 ? 4 : r);
+}
+// LDS of a score workgroup holding 32 * nqf queries.
+__host__ __device__ constexpr int score_lds_bytes(int ct, int d, int nqf) {
+  return kFrag * nqf * (d * elem_bytes(ct) + 4) + kStageLds;
+}
+__host__ __device__ constexpr bool nqf_fits(int ct, int d, int nqf) {
+  return score_lds_bytes(ct, d, nqf) <= kLdsLimit;
+}
+
+struct ScoreArgs {
+  const uint8_t* corpus;
+  const float* row_scale;
+  const uint32_t* exclude;
+  const uint8_t* qtile;
+  const int* qexp;
+  int64_t n;
+  int64_t n32;      // 32-row blocks in the corpus
+  int64_t nfrag;    // blocks this pass covers: n32, or G sampled blocks
+  int64_t ntiles;   // stage tiles of the pass
+  int b;
+  int b32;
+  int nqblk;        // query blocks in the grid
+  int nslices;      // corpus slices in the grid
+  int dense;        // AUX pass: write every score (1) or the sample delegates (0)
+  const uint32_t* thr;    // per-query threshold keys (0: query not scored here)
+  uint32_t* cnt;
+  uint32_t* ovf;
+  uint64_t* cand;
+  int64_t cap;
+  const uint32_t* qlist;  // rescue pass: queued query ids ...
+  const uint32_t* nlist;  // ... and their number (device); NULL for the full batch
+  uint32_t* del;          // sample delegates [G][b32]
+};
+
+// Launches score_kernel<CT, D, nqf, MODE> (nqf in {1, 2, 4, 8, 16}); defined in
+// score_inst.hip, built once per corpus dtype and width.
+template <int CT, int D, int MODE>
+int launch_score_nqf(int nqf, const ScoreArgs& A, int grid, hipStream_t s);
+
+}  // namespace mips
