@@ -23,8 +23,8 @@ K_MAX = 1024
 
 EXPORTS = (
     "mips_corpus_bytes", "mips_scale_count", "mips_l2_normalize", "mips_prepare_corpus",
-    "mips_topk_workspace_size", "mips_topk", "mips_set_timing_events", "mips_status_string",
-    "mips_last_hip_error",
+    "mips_topk_workspace_size", "mips_topk_workspace_size_for", "mips_topk",
+    "mips_set_timing_events", "mips_status_string", "mips_last_hip_error",
 )
 
 
@@ -57,6 +57,8 @@ def lib() -> C.CDLL:
         L.mips_prepare_corpus.argtypes = [p, i64, i64, i32, i32, p, p, p]
         L.mips_topk_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32]
         L.mips_topk_workspace_size.restype = sz
+        L.mips_topk_workspace_size_for.argtypes = [i32, i64, i32, i32, i32, i32, i64]
+        L.mips_topk_workspace_size_for.restype = sz
         L.mips_topk.argtypes = [p, i32, i32, p, p, i32, i64, i32, p, i32, p, p, p, sz, p]
         L.mips_set_timing_events.argtypes = [p, p]
         L.mips_status_string.argtypes = [C.c_int]
@@ -149,9 +151,14 @@ def prepare_corpus(x: torch.Tensor, dtype: str) -> Corpus:
 
 
 # -------------------------------------------------------------------- top-k
-def workspace_size(b: int, n: int, d: int, k: int, query_dtype: str, corpus_dtype: str) -> int:
-    return int(lib().mips_topk_workspace_size(b, n, d, k, DTYPE_CODES[query_dtype],
-                                              DTYPE_CODES[corpus_dtype]))
+def workspace_size(b: int, n: int, d: int, k: int, query_dtype: str, corpus_dtype: str,
+                   candidates_per_query: Optional[int] = None) -> int:
+    """Workspace bytes of mips_topk: the default candidate capacity, or at least
+    `candidates_per_query` candidates per query."""
+    qc, cc = DTYPE_CODES[query_dtype], DTYPE_CODES[corpus_dtype]
+    if candidates_per_query is None:
+        return int(lib().mips_topk_workspace_size(b, n, d, k, qc, cc))
+    return int(lib().mips_topk_workspace_size_for(b, n, d, k, qc, cc, candidates_per_query))
 
 
 def empty_workspace(nbytes: int, device="cuda") -> torch.Tensor:

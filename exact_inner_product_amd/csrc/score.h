@@ -2,6 +2,8 @@
 // epilogues); included only by score_inst.hip.
 #pragma once
 
+#include <utility>
+
 #include "host.h"
 #include "score_api.h"
 
@@ -29,8 +31,21 @@ __device__ __forceinline__ void mfma_step(f32x16_t& acc, const u32x4_t* a, const
   }
 }
 
-__device__ __forceinline__ uint32_t lane_rank(uint64_t bm) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time (the
+// register arrays it indexes must never be indexed at run time).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Buffer descriptor of `bytes` bytes at p (gfx9 raw buffer: stride 0, offsets in bytes;
+// loads past the range return zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
 }
 
 // One workgroup = 4 waves (one per SIMD) = one corpus slice x one block of 32 * NQF
@@ -40,7 +55,7 @@ __device__ __forceinline__ uint32_t lane_rank(uint64_t bm) {
 // fragment qf+1 and the LDS reads of fragment qf+2's operand are issued before the
 // epilogue of fragment qf.
 template <int CT, int D, int NQF, int MODE>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs A) {
+__global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void score_kernel(ScoreArgs A) {
   constexpr int E = elem_bytes(CT);
   constexpr int NCH = chunks_per_block(CT, D);
   constexpr int RM = stage_frags(CT, D);
@@ -71,8 +86,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs A) {
   // LDS: query operand tile | global query id per column | per-wave survivor staging
   // (composite keys, query column).
   int* qid_lds = (int*)(lds + (size_t)QB * D * E);
-  uint64_t* st_key = (uint64_t*)(qid_lds + QB) + wave * kStageCap;
-  uint16_t* st_q = (uint16_t*)((uint64_t*)(qid_lds + QB) + kScoreWaves * kStageCap) + wave * kStageCap;
+  uint32_t* seg_lds = (uint32_t*)(qid_lds + QB);  // survivors per query column (this segment)
+  uint64_t* st_key = (uint64_t*)(seg_lds + QB) + wave * kStageCap;
+  uint16_t* st_q = (uint16_t*)((uint64_t*)(seg_lds + QB) + kScoreWaves * kStageCap) + wave * kStageCap;
 
   const int64_t t_begin = (int64_t)slice * A.ntiles / A.nslices;
   const int64_t t_end = (int64_t)(slice + 1) * A.ntiles / A.nslices;
@@ -89,10 +105,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs A) {
       const int n16 = rows * D * E / 16;
       for (int i = threadIdx.x; i < QB * D * E / 16; i += kScoreThreads)
         dst[i] = i < n16 ? src[i] : u32x4_t{0u, 0u, 0u, 0u};
-      for (int i = threadIdx.x; i < QB; i += kScoreThreads) qid_lds[i] = qbase + i < A.b ? qbase + i : -1;
+      for (int i = threadIdx.x; i < QB; i += kScoreThreads) {
+        qid_lds[i] = qbase + i < A.b ? qbase + i : -1;
+        seg_lds[i] = 0u;
+      }
     } else {
-      for (int i = threadIdx.x; i < QB; i += kScoreThreads)
+      for (int i = threadIdx.x; i < QB; i += kScoreThreads) {
         qid_lds[i] = qbase + i < nq_total ? (int)A.qlist[qbase + i] : -1;
+        seg_lds[i] = 0u;
+      }
       __syncthreads();
       // gather the queued queries' operand rows: 16-byte slot s of chunk c of column
       // fragment qf comes from slot (q & 31) + 32 (s >> 5) of the same chunk of q's block
@@ -127,32 +148,27 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs A) {
 
     int st_n = 0;  // staged survivors of this wave (wave-uniform; may exceed the capacity)
 
-    // Appends the staged survivors to their queries' lists: all returning atomics are
-    // issued before the first store waits for one.
-    auto flush = [&]() {
+    // Appends the staged survivors to their queries' lists. Every workgroup owns one
+    // segment of each query's list (segment = its corpus slice); positions come from LDS
+    // counters, so no global atomic is needed. The counters also count what does not fit
+    // the segment, which the final select sees as an overflow.
+    auto flush = [&]() __attribute__((always_inline)) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const int nst = min(st_n, kStageCap);
       constexpr int R = kStageCap / kWave;
-      uint64_t ck[R];
-      uint32_t pos[R];
-      int qg[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int e = r * kWave + lane;
-        ck[r] = 0ull;
-        qg[r] = 0;
-        pos[r] = 0xFFFFFFFFu;
         if (e < nst) {
-          ck[r] = st_key[e];
-          qg[r] = qid_lds[st_q[e]];
-          pos[r] = atomicAdd(&A.cnt[qg[r]], 1u);
+          const uint64_t ck = st_key[e];
+          const int qc = st_q[e];
+          const uint32_t pos = atomicAdd(&seg_lds[qc], 1u);
+          if ((int64_t)pos < A.capw)
+            A.cand[((int64_t)qid_lds[qc] * A.nseg + slice) * A.capw + pos] = ck;
         }
       }
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-        if ((int64_t)pos[r] < A.cap) A.cand[(int64_t)qg[r] * A.cap + pos[r]] = ck[r];
       __builtin_amdgcn_wave_barrier();
       st_n = 0;
     };
@@ -160,14 +176,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs A) {
     // A stage's loads are unconditional: blocks past the end of the pass read the last
     // block again and are masked out, so the compiler's wait counts stay exact. Lane r < RM
     // also loads the exclusion word of block r, with the rows past n set.
-    auto load_stage = [&](u32x4_t (&a)[RM][NCH], int (&sa)[RM], uint32_t& xwv, int64_t j0) {
+    auto load_stage = [&](u32x4_t (&a)[RM][NCH], int (&sa)[RM], uint32_t& xwv, int64_t j0) __attribute__((always_inline)) {
 #pragma unroll
       for (int r = 0; r < RM; ++r) {
         const int64_t j = min<int64_t>(j0 + r, A.nfrag - 1);
-        const int64_t fr = (MODE == MODE_AUX && !A.dense) ? j * A.n32 / A.nfrag : j;
-        const u32x4_t* p = (const u32x4_t*)(A.corpus + fr * BLK) + lane;
+        const int64_t fr = (MODE == MODE_AUX && !A.dense) ? (int64_t)(((uint64_t)j * A.sample_step) >> 32) : j;
+        // one buffer descriptor per block (scalar base, range = the block's bytes) and a
+        // 32-bit lane offset: no per-lane 64-bit addresses to keep live
+        const __amdgpu_buffer_rsrc_t rs = block_rsrc(A.corpus + fr * BLK, (int)BLK);
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) a[r][c] = p[c * (kChunkBytes / 16)];
+        for (int c = 0; c < NCH; ++c)
+          a[r][c] = __builtin_bit_cast(
+              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, c * kChunkBytes, 0));
         sa[r] = 127;
         if (CT == MIPS_FP8_E4M3)
           sa[r] = (int)((__float_as_uint(A.row_scale[fr * kFrag + (lane & 31)]) >> 23) & 0xFFu);
@@ -175,34 +195,60 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs A) {
       const int r = lane < RM ? lane : RM - 1;
       const bool live = j0 + r < A.nfrag;
       const int64_t j = live ? j0 + r : A.nfrag - 1;
-      const int64_t fr = (MODE == MODE_AUX && !A.dense) ? j * A.n32 / A.nfrag : j;
-      uint32_t w = A.exclude ? A.exclude[fr] : 0u;
+      const int64_t fr = (MODE == MODE_AUX && !A.dense) ? (int64_t)(((uint64_t)j * A.sample_step) >> 32) : j;
+      // branch-free: without a bitmap, any readable word masked to zero (a conditional
+      // load would make the compiler's wait counts conservative at the join)
+      const uint32_t* wp = A.exclude ? A.exclude + fr : (const uint32_t*)A.corpus;
+      uint32_t w = *wp & (A.exclude ? ~0u : 0u);
       const int64_t rows = A.n - fr * kFrag;
       if (rows < kFrag) w |= ~0u << rows;
       xwv = live ? w : ~0u;
     };
 
-    auto load_b = [&](u32x4_t (&bq)[NCH], int qf) {
+    auto load_b = [&](u32x4_t (&bq)[NCH], int qf) __attribute__((always_inline)) {
       const u32x4_t* bsrc = (const u32x4_t*)(lds + (size_t)qf * BLK) + lane;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) bq[c] = bsrc[c * (kChunkBytes / 16)];
     };
+    // MFMAs of one query fragment against the stage's RM blocks. With `next` >= 0 the
+    // operand chunks are refilled from fragment `next` in LDS as soon as their last MFMA
+    // has been issued, so the next fragment's operand streams in behind this one's.
     auto mfmas = [&](f32x16_t (&acc)[RM], const u32x4_t (&a)[RM][NCH], const int (&sa)[RM],
-                     const u32x4_t (&bq)[NCH], int sb) {
+                     u32x4_t (&bq)[NCH], int sb, int next) __attribute__((always_inline)) {
+      const u32x4_t* bsrc = (const u32x4_t*)(lds + (size_t)(next < 0 ? 0 : next) * BLK) + lane;
 #pragma unroll
       for (int g = 0; g < RM; ++g) acc[g] = f32x16_t{};
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
+      for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
         for (int g = 0; g < RM; ++g) mfma_step<CT>(acc[g], a[g], bq, sa[g], sb, s);
+        if (next >= 0) {
+          // chunks whose last use was step s: bf16 chunk s; fp8 chunks 2s, 2s+1; f32 chunk
+          // s/4 after its fourth step
+          if constexpr (CT == MIPS_BF16) {
+            bq[s] = bsrc[s * (kChunkBytes / 16)];
+          } else if constexpr (CT == MIPS_FP8_E4M3) {
+            bq[2 * s] = bsrc[2 * s * (kChunkBytes / 16)];
+            bq[2 * s + 1] = bsrc[(2 * s + 1) * (kChunkBytes / 16)];
+          } else {
+            if ((s & 3) == 3) bq[s >> 2] = bsrc[(s >> 2) * (kChunkBytes / 16)];
+          }
+        }
+      }
     };
+    // Query operand held in registers for the whole q-block when it fits (up to 256
+    // registers: 256 queries at 256 bytes per row); otherwise streamed from LDS.
+    constexpr bool BREG = false;
+    u32x4_t breg[BREG ? NQF : 1][NCH];
+    if constexpr (BREG) {
+#pragma unroll
+      for (int qf = 0; qf < NQF; ++qf) load_b(breg[qf], qf);
+    }
 
     // Main epilogue of one query fragment: one max per block (16 scores per lane) and one
     // ballot, branch-free so it interleaves with the next fragment's MFMAs. A block that
-    // clears the threshold is resolved by 4-row groups, then value by value with ballot +
-    // mbcnt compaction into the wave's staging buffer; those loops index the accumulators
-    // with a wave-uniform runtime index and stay rolled.
-    auto epi_main = [&](const f32x16_t (&acc)[RM], uint32_t xwv, int64_t j0, int qf) {
+    // clears the threshold is resolved on the scalar unit (below).
+    auto epi_main = [&](const f32x16_t (&acc)[RM], uint32_t xwv, int64_t j0, int qf) __attribute__((always_inline)) {
       const float T = Tq[qf];
       float m[RM];
       bool any = false;
@@ -215,34 +261,38 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs A) {
         any = any || (x >= T);
       }
       if (__builtin_expect(__ballot(any) != 0ull, 0)) {
-        const int ql = qf * kFrag + (lane & 31);
 #pragma unroll
         for (int g = 0; g < RM; ++g) {
           if (__ballot(m[g] >= T) == 0ull) continue;
           const uint32_t w = __builtin_amdgcn_readlane(xwv, g);
           const uint32_t idb = (uint32_t)((j0 + g) * kFrag);
+          // value i of every lane: one ballot of `v >= T`; the rows it covers are rlo (lanes
+          // 0-31) and rlo + 4 (lanes 32-63), so the exclusion bits turn into a lane mask
+          // on the scalar unit; each survivor is read out with readlane and appended by
+          // lane 0 (survivors are rare: usually one per hit block). The loop stays rolled
+          // (a wave-uniform index into the accumulators) to keep this cold code small.
 #pragma unroll 1
-          for (int bb = 0; bb < 4; ++bb) {
-            const float pm = fmaxf(fmaxf(acc[g][4 * bb], acc[g][4 * bb + 1]),
-                                   fmaxf(acc[g][4 * bb + 2], acc[g][4 * bb + 3]));
-            if (__ballot(pm >= T) == 0ull) continue;
-#pragma unroll 1
-            for (int i = 4 * bb; i < 4 * bb + 4; ++i) {
-              const float v = acc[g][i];
-              const int row = acc_row(i, lane);
-              const bool pass = v >= T && !((w >> row) & 1u);
-              const uint64_t bm = __ballot(pass);
-              if (bm == 0ull) continue;
-              const int pos = st_n + (int)lane_rank(bm);
-              if (pass) {
-                if (pos < kStageCap) {
-                  st_key[pos] = composite(score_key(v), idb + (uint32_t)row);
-                  st_q[pos] = (uint16_t)ql;
-                } else {
-                  atomicOr(&A.ovf[qid_lds[ql]], 1u);  // no room: the query is rescued
+          for (int i = 0; i < 16; ++i) {
+            uint64_t P = __ballot(acc[g][i] >= T);
+            if (P == 0ull) continue;
+            constexpr uint64_t kLo = 0x00000000FFFFFFFFull, kHi = 0xFFFFFFFF00000000ull;
+            const int rlo = 8 * (i >> 2) + (i & 3);
+            P &= ~((((w >> rlo) & 1u) ? kLo : 0ull) | (((w >> (rlo + 4)) & 1u) ? kHi : 0ull));
+            while (P != 0ull) {
+              const int L = __builtin_ctzll(P);
+              P &= P - 1ull;
+              const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[g][i]), L));
+              const uint32_t id = idb + (uint32_t)(rlo + 4 * (L >> 5));
+              const int qcol = qf * kFrag + (L & 31);
+              if (st_n < kStageCap) {
+                if (lane == 0) {
+                  st_key[st_n] = composite(score_key(v), id);
+                  st_q[st_n] = (uint16_t)qcol;
                 }
+              } else if (lane == 0) {
+                atomicOr(&A.ovf[qid_lds[qcol]], 1u);  // no room: the query is rescued
               }
-              st_n += __popcll(bm);
+              ++st_n;
             }
           }
         }
@@ -250,17 +300,21 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs A) {
     };
 
     // Auxiliary epilogue. Dense pass: every score of the block goes to the query's list at
-    // its id (0 for excluded and padding rows). Sample pass: the best eligible score of the
-    // block is the (block, query) delegate (key 0 if the block has no eligible row).
-    auto epi_aux = [&](const f32x16_t (&acc)[RM], uint32_t xwv, int64_t j0, int qf) {
+    // its id (0 for excluded and padding rows). Sample pass: each half of the wave holds 16
+    // of a block's 32 rows, and its best eligible score is the delegate of that half-block
+    // (key 0 if none is eligible); the stage's 2 RM delegates of a query form one slot,
+    // written by the two lanes of the query's column (no cross-lane reduction). Slots are
+    // laid out del[tile / 16][query][tile % 16][2 RM], so that each query's delegates lie in
+    // runs of 16 slots.
+    auto epi_aux = [&](const f32x16_t (&acc)[RM], uint32_t xwv, int64_t j0, int qf) __attribute__((always_inline)) {
       const int qg = qgq[qf];
+      if (A.dense) {
 #pragma unroll
-      for (int g = 0; g < RM; ++g) {
-        const int64_t j = j0 + g;
-        const uint32_t w = __builtin_amdgcn_readlane(xwv, g);
-        if (A.dense) {
+        for (int g = 0; g < RM; ++g) {
+          const int64_t j = j0 + g;
+          const uint32_t w = __builtin_amdgcn_readlane(xwv, g);
           if (j < A.nfrag && qg >= 0) {
-            uint64_t* dst = A.cand + (int64_t)qg * A.cap + j * kFrag;
+            uint64_t* dst = A.cand + (int64_t)qg * A.nseg * A.capw + j * kFrag;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int row = acc_row(i, lane);
@@ -268,65 +322,98 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs A) {
                                            : composite(score_key(acc[g][i]), (uint32_t)(j * kFrag + row));
             }
           }
-        } else {
+        }
+      } else {
+        uint32_t d[RM];
+#pragma unroll
+        for (int g = 0; g < RM; ++g) {
+          const uint32_t w = __builtin_amdgcn_readlane(xwv, g);
           float mx = -INFINITY;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int row = acc_row(i, lane);
             mx = ((w >> row) & 1u) ? mx : fmaxf(mx, acc[g][i]);
           }
-          mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-          const int qc = qbase + qf * kFrag + lane;
-          if (lane < kFrag && j < A.nfrag && qc < A.b32)
-            A.del[j * A.b32 + qc] = (mx == -INFINITY) ? 0u : score_key(mx);
+          d[g] = (mx == -INFINITY) ? 0u : score_key(mx);
+        }
+        const int qc = qbase + qf * kFrag + (lane & 31);
+        if (qc < A.b32) {
+          const int64_t tt = j0 / RM;  // sample tile
+          uint32_t* dst = A.del + (((tt >> 4) * A.b32 + qc) * 16 + (tt & 15)) * (2 * RM) + (lane >> 5) * RM;
+#pragma unroll
+          for (int g = 0; g < RM; ++g) dst[g] = d[g];
         }
       }
     };
 
+    // One stage against every query fragment, software-pipelined: the MFMAs of fragment
+    // qf+1 are issued before the epilogue of fragment qf, so the epilogue (and its rare
+    // path) runs while the matrix pipe works on the next fragment.
     auto compute_stage = [&](const u32x4_t (&a)[RM][NCH], const int (&sa)[RM], uint32_t xwv,
-                             int64_t j0) {
-      u32x4_t bq[2][NCH];
+                             int64_t j0) __attribute__((always_inline)) {
       f32x16_t acc[2][RM];
-      load_b(bq[0], 0);
-      if (NQF > 1) load_b(bq[1], 1);
-      mfmas(acc[0], a, sa, bq[0], sbq[0]);
-#pragma unroll
-      for (int qf = 0; qf < NQF; ++qf) {
-        const int cur = qf & 1;
-        if (qf + 1 < NQF) {
-          mfmas(acc[cur ^ 1], a, sa, bq[cur ^ 1], sbq[qf + 1 < NQF ? qf + 1 : 0]);
-          if (qf + 2 < NQF) load_b(bq[cur], qf + 2 < NQF ? qf + 2 : 0);
+      u32x4_t bq[BREG ? 1 : NCH];
+      if constexpr (BREG) {
+        mfmas(acc[0], a, sa, breg[0], sbq[0], -1);
+      } else {
+        load_b(bq, 0);
+        mfmas(acc[0], a, sa, bq, sbq[0], NQF > 1 ? 1 : -1);
+      }
+      static_for<NQF>([&](auto qfc) __attribute__((always_inline)) {
+        constexpr int qf = decltype(qfc)::value;
+        constexpr int cur = qf & 1;
+        if constexpr (qf + 1 < NQF) {
+          if constexpr (BREG)
+            mfmas(acc[cur ^ 1], a, sa, breg[qf + 1], sbq[qf + 1], -1);
+          else
+            mfmas(acc[cur ^ 1], a, sa, bq, sbq[qf + 1], qf + 2 < NQF ? qf + 2 : -1);
         }
-        if (MODE == MODE_MAIN)
+        if constexpr (MODE == MODE_MAIN)
           epi_main(acc[cur], xwv, j0, qf);
         else
           epi_aux(acc[cur], xwv, j0, qf);
-      }
+      });
     };
 
-    // Two-stage software pipeline over this wave's stage tiles: the next stage's corpus
-    // blocks are in flight while the current one is multiplied against every query.
-    u32x4_t a0[RM][NCH], a1[RM][NCH];
-    int s0[RM], s1[RM];
-    uint32_t x0, x1;
+    // NS-stage software pipeline over this wave's stage tiles (a stage every kScoreWaves
+    // tiles): while stage i is multiplied against every query, stages i+1 .. i+NS-1 are in
+    // flight. With one wave per SIMD, the bytes in flight per wave set the HBM bandwidth
+    // (Little's law at several microseconds of loaded latency), hence NS - 1 = 2 stages.
+    constexpr int NS = kPipeStages;
+    u32x4_t a[NS][RM][NCH];
+    int sa[NS][RM];
+    uint32_t xw[NS];
     int64_t t = t_begin + wave;
+    auto tile = [&](int64_t tt) __attribute__((always_inline)) { return tt < t_end ? tt * RM : A.nfrag; };
     if (t < t_end) {
-      load_stage(a0, s0, x0, t * RM);
-      for (;;) {
-        const int64_t t1 = t + kScoreWaves;
-        load_stage(a1, s1, x1, t1 < t_end ? t1 * RM : A.nfrag);
+      static_for<NS - 1>([&](auto uc) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;
+        load_stage(a[u], sa[u], xw[u], tile(t + u * kScoreWaves));
+      });
+      // one pipeline step; returns true after the wave's last stage. The steps are chained
+      // with || so that the exits are plain branches and every wait count stays exact.
+      auto step = [&](auto uc) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;
+        constexpr int ld = (u + NS - 1) % NS;
+        load_stage(a[ld], sa[ld], xw[ld], tile(t + (u + NS - 1) * kScoreWaves));
         if (MODE == MODE_MAIN && st_n > kStageCap - kStageBurst) flush();
-        compute_stage(a0, s0, x0, t * RM);
-        if (t1 >= t_end) break;
-        const int64_t t2 = t1 + kScoreWaves;
-        load_stage(a0, s0, x0, t2 < t_end ? t2 * RM : A.nfrag);
-        if (MODE == MODE_MAIN && st_n > kStageCap - kStageBurst) flush();
-        compute_stage(a1, s1, x1, t1 * RM);
-        if (t2 >= t_end) break;
-        t = t2;
+        compute_stage(a[u], sa[u], xw[u], (t + u * kScoreWaves) * RM);
+        return t + (u + 1) * kScoreWaves >= t_end;
+      };
+      static_assert(NS == 3, "the step chain below is written for three stages");
+      while (!(step(std::integral_constant<int, 0>{}) || step(std::integral_constant<int, 1>{}) ||
+               step(std::integral_constant<int, 2>{})))
+        t += NS * kScoreWaves;
+    }
+    if (MODE == MODE_MAIN) {
+      if (st_n > 0) flush();
+      // this workgroup's segment counts of the block's queries
+      __syncthreads();
+      for (int i = threadIdx.x; i < QB; i += kScoreThreads) {
+        const int q = qid_lds[i];
+        if (q >= 0) A.segcnt[(int64_t)q * A.nseg + slice] = seg_lds[i];
       }
     }
-    if (MODE == MODE_MAIN && st_n > 0) flush();
   }
 }
 

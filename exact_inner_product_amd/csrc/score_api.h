@@ -16,6 +16,8 @@ constexpr int kStageBurst = 256;    // room kept free before each stage
 constexpr int kStageLds = kScoreWaves * kStageCap * (8 + 2);
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int kMaxSample = 8192;    // sampled 32-row blocks
+constexpr int kPipeStages = 3;      // corpus stages held in registers per wave
+constexpr int kMaxSegments = 256;   // list segments per query (corpus slices of a pass)
 constexpr int kSelCache = 6144;     // candidates the final select caches in LDS
 
 enum { MODE_MAIN = 0, MODE_AUX = 1 };
@@ -27,7 +29,7 @@ __host__ __device__ constexpr int stage_frags(int ct, int d) {
 }
 // LDS of a score workgroup holding 32 * nqf queries.
 __host__ __device__ constexpr int score_lds_bytes(int ct, int d, int nqf) {
-  return kFrag * nqf * (d * elem_bytes(ct) + 4) + kStageLds;
+  return kFrag * nqf * (d * elem_bytes(ct) + 8) + kStageLds;
 }
 __host__ __device__ constexpr bool nqf_fits(int ct, int d, int nqf) {
   return score_lds_bytes(ct, d, nqf) <= kLdsLimit;
@@ -41,7 +43,7 @@ struct ScoreArgs {
   const int* qexp;
   int64_t n;
   int64_t n32;      // 32-row blocks in the corpus
-  int64_t nfrag;    // blocks this pass covers: n32, or G sampled blocks
+  int64_t nfrag;    // blocks this pass covers: n32, or G sampled blocks (strided)
   int64_t ntiles;   // stage tiles of the pass
   int b;
   int b32;
@@ -49,13 +51,15 @@ struct ScoreArgs {
   int nslices;      // corpus slices in the grid
   int dense;        // AUX pass: write every score (1) or the sample delegates (0)
   const uint32_t* thr;    // per-query threshold keys (0: query not scored here)
-  uint32_t* cnt;
+  uint32_t* segcnt;       // [b][nseg] survivors found per (query, segment)
   uint32_t* ovf;
-  uint64_t* cand;
-  int64_t cap;
+  uint64_t* cand;         // [b][nseg][capw] candidate keys; dense pass: [b][nseg * capw]
+  int64_t capw;           // entries per segment
+  int nseg;               // segments per query (one per corpus slice)
   const uint32_t* qlist;  // rescue pass: queued query ids ...
   const uint32_t* nlist;  // ... and their number (device); NULL for the full batch
-  uint32_t* del;          // sample delegates [G][b32]
+  uint32_t* del;          // sample delegates [tile/16][b32][16][2 RM]: one per half-block and query
+  uint64_t sample_step;   // sampled block j is block (j * sample_step) >> 32
 };
 
 // Launches score_kernel<CT, D, nqf, MODE> (nqf in {1, 2, 4, 8, 16}); defined in

@@ -6,7 +6,7 @@
 // Retrieval Works", step 4). The score matrix is never written out. One call runs:
 //
 //   prep_queries     queries -> MFMA operand layout (E4M3 + power-of-two scale for an
-//                    fp8 corpus); clears the per-query counters.
+//                    fp8 corpus); clears the per-query flags.
 //   score<AUX>       sample pass: scores a strided sample of G 32-row blocks and writes,
 //                    per (block, query), the best eligible score of the block ("delegate").
 //   sample_threshold per query: the K-th largest delegate is a proven lower bound of the
@@ -45,7 +45,6 @@ template <int CT, int QT, int D>
 __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict__ queries, int b,
                                                           uint8_t* __restrict__ qtile,
                                                           int* __restrict__ qexp,
-                                                          uint32_t* __restrict__ cnt,
                                                           uint32_t* __restrict__ ovf,
                                                           uint32_t* __restrict__ nfail) {
   constexpr int NCH = chunks_per_block(CT, D);
@@ -81,43 +80,97 @@ __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict
     }
     *(u32x4_t*)(out + (int64_t)c * kChunkBytes + lane * 16) = v;
   }
-  if (lane < 32 && live) {
-    cnt[q] = 0u;
-    ovf[q] = 0u;
-  }
+  if (lane < 32 && live) ovf[q] = 0u;
   if (blockIdx.x == 0 && lane == 0) *nfail = 0u;
 }
 
 // ------------------------------------------------------------ sampled threshold
-// Per query, from the G delegates (best eligible score per sampled block): tb = the K-th
-// largest, a proven lower bound of the K-th best score, and te = the r-th largest
-// (r <= K), the estimate that the main pass filters with. Key 0 means "no bound".
+// Per query, from the G delegates (best eligible score per sampled half-block of 16 rows):
+// tb, a proven lower bound of the K-th best score (at least K delegates, i.e. K distinct
+// half-blocks, reach it), and te >= tb at delegate rank r (r <= K), the estimate the main pass filters with.
+// Both come from one histogram of the delegate scores over kThrBins equal bins of
+// [-kThrRange, kThrRange] (scores outside fall into the end bins) and a suffix scan: the
+// threshold of rank r is the lower edge of the bin holding the r-th largest delegate, less
+// a margin that absorbs the rounding of the bin computation, so at least r delegates
+// reach it. Key 0 means "no bound" (fewer than K, resp. r, eligible sampled blocks).
+constexpr int kThrBins = 4096;
+constexpr float kThrRange = 1.25f;  // > (1 + 2^-4)^2, the largest fp8 score of unit vectors
+
+__device__ __forceinline__ int thr_bin(float s) {
+  const float x = (s + kThrRange) * ((float)kThrBins / (2.0f * kThrRange));
+  const int b = (int)floorf(x);
+  return b < 0 ? 0 : (b >= kThrBins ? kThrBins - 1 : b);
+}
+__device__ __forceinline__ uint32_t thr_bin_key(int b) {
+  if (b <= 0) return 0u;  // the lowest bin is open below: no bound
+  const float e = -kThrRange + (float)b * (2.0f * kThrRange / (float)kThrBins);
+  return score_key(e - 1e-5f);
+}
+
 __global__ __launch_bounds__(kSelThreads) void sample_threshold_kernel(const uint32_t* __restrict__ del,
-                                                                       int G, int b32, int b, int k,
-                                                                       int r, uint32_t* __restrict__ thr,
+                                                                       int ntiles, int slot, int b32, int b,
+                                                                       int k, int r, uint32_t* __restrict__ thr,
                                                                        uint32_t* __restrict__ thrb) {
-  __shared__ uint32_t keys[kMaxSample];
-  __shared__ SelScratch S;
-  __shared__ uint32_t nz;
+  constexpr int PER = kThrBins / kSelThreads;  // bins per thread
+  __shared__ uint32_t hist[kThrBins];
+  __shared__ uint32_t wsum[kSelThreads / kWave];
+  __shared__ int found[2];
   const int q = blockIdx.x;
   if (q >= b) return;
-  if (threadIdx.x == 0) nz = 0u;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  for (int i = t; i < kThrBins; i += kSelThreads) hist[i] = 0u;
+  if (t < 2) found[t] = 0;
   __syncthreads();
-  uint32_t mine = 0u;
-  for (int i = threadIdx.x; i < G; i += kSelThreads) {
-    const uint32_t v = del[(int64_t)i * b32 + q];
-    keys[i] = v;
-    mine += v != 0u;
+  // the query's delegates: runs of 16 slots of `slot` delegates each (one slot per sample
+  // tile); each thread reads whole runs, contiguous bytes
+  const int ngroups = (ntiles + 15) / 16;
+  for (int gi = t; gi < ngroups; gi += kSelThreads) {
+    const u32x4_t* src = (const u32x4_t*)(del + ((int64_t)gi * b32 + q) * 16 * slot);
+    const int nvec = 16 * slot / 4;  // slot is 2, 4 or 8
+    for (int v0 = 0; v0 < nvec; v0 += 8) {
+      u32x4_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = v0 + u < nvec ? src[v0 + u] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // slots of tiles past the end of the pass are never written
+          const int tile = gi * 16 + ((v0 + u) * 4 + e) / slot;
+          if (tile < ntiles && v[u][e] != 0u) atomicAdd(&hist[thr_bin(key_score(v[u][e]))], 1u);
+        }
+    }
   }
-  atomicAdd(&nz, mine);
   __syncthreads();
-  const int m = (int)nz;
-  auto get = [&](int64_t i) { return (uint64_t)keys[i]; };
-  uint32_t tb = 0u, te = 0u;
-  if (m >= k) tb = (uint32_t)select_top(get, G, k, S).prefix;
+  // thread t owns bins [t*PER, (t+1)*PER); the suffix sum over threads above t gives the
+  // count of delegates in higher bins
+  uint32_t own = 0u;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) own += hist[t * PER + i];
+  // inclusive suffix scan over the wave (lanes above), then over waves
+  uint32_t c = own;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t u = __shfl_down(c, o, kWave);
+    if (lane + o < kWave) c += u;
+  }
+  if (lane == 0) wsum[w] = c;
   __syncthreads();
-  if (m >= r) te = (uint32_t)select_top(get, G, r, S).prefix;
-  if (threadIdx.x == 0) {
+  for (int i = w + 1; i < kSelThreads / kWave; ++i) c += wsum[i];
+  uint32_t above = c - own;  // delegates in bins above this thread's range
+  // walk this thread's bins from the top; record the bins where ranks r and k are reached
+  // (found[] holds bin + 1; exactly one thread reaches each rank)
+#pragma unroll
+  for (int i = PER - 1; i >= 0; --i) {
+    const uint32_t h = hist[t * PER + i];
+    if (above < (uint32_t)r && above + h >= (uint32_t)r) found[0] = t * PER + i + 1;
+    if (above < (uint32_t)k && above + h >= (uint32_t)k) found[1] = t * PER + i + 1;
+    above += h;
+  }
+  __syncthreads();
+  if (t == 0) {
+    const uint32_t tb = found[1] > 0 ? thr_bin_key(found[1] - 1) : 0u;
+    const uint32_t te = found[0] > 0 ? thr_bin_key(found[0] - 1) : 0u;
     thr[q] = te > tb ? te : tb;
     thrb[q] = tb;
   }
@@ -133,11 +186,13 @@ struct SelectArgs {
   int64_t n;
   int b;
   int k;
-  int64_t cap;
+  int64_t capw;         // entries per list segment
+  int nseg;             // segments per query list
+  int nseg_used;        // segments written by the pass being selected from
   int64_t dense_count;  // > 0: lists hold one slot per row (0 = empty), this many
   uint32_t* thr;
   const uint32_t* thrb;
-  uint32_t* cnt;
+  const uint32_t* segcnt;
   uint32_t* ovf;
   const uint64_t* cand;
   uint32_t* nfail;
@@ -223,7 +278,29 @@ __device__ void fallback_scan(const SelectArgs& A, int q, uint64_t thr, uint64_t
   write_out(A, q, sel_buf, r);
 }
 
+// Exclusive prefix sum over the workgroup's threads; returns (exclusive, total).
+__device__ inline uint2 block_exclusive_sum(uint32_t v, uint32_t* wsum) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  uint32_t c = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t u = __shfl_up(c, o, kWave);
+    if (lane >= o) c += u;
+  }
+  if (lane == kWave - 1) wsum[w] = c;
+  __syncthreads();
+  uint32_t before = 0u, total = 0u;
+  for (int i = 0; i < kSelThreads / kWave; ++i) {
+    if (i < w) before += wsum[i];
+    total += wsum[i];
+  }
+  __syncthreads();
+  return make_uint2(before + c - v, total);
+}
+
 // One workgroup per query. Round 0 covers the batch; round 1 the queries queued by round 0.
+// A query's candidates lie in segments (one per workgroup of the pass that found them);
+// thread s handles segment s.
 template <int CT, int D>
 __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A, int round) {
   __shared__ uint64_t cache[kSelCache];
@@ -231,83 +308,114 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
   __shared__ SelScratch S;
   __shared__ float qv[D];
   __shared__ uint32_t nbuf;
+  __shared__ uint32_t segoff[kSelThreads + 1];
+  __shared__ uint32_t wsum[kSelThreads / kWave];
   int q = blockIdx.x;
   if (round > 0) {
     if ((uint32_t)q >= *A.nfail) return;
     q = (int)A.flist[q];
   }
   if (q >= A.b) return;
-  const uint64_t* list = A.cand + (int64_t)q * A.cap;
+  const int t = threadIdx.x;
+  const uint64_t* qlist = A.cand + (int64_t)q * A.nseg * A.capw;
   int64_t c;
+  bool cached;
   if (A.dense_count > 0) {
+    // dense list: one slot per row; empty slots (key 0) are not candidates, so select
+    // among the others only and no tie at the boundary involves an empty slot
     c = A.dense_count;
-  } else {
-    const uint32_t tu = A.thr[q], tb = A.thrb[q];
-    if (tu == 0u) {
-      // no sampled bound for this query (fewer than K eligible sampled blocks)
-      fallback_scan<CT, D>(A, q, 0ull, cache, sel_buf, S, qv, &nbuf);
-      return;
-    }
-    c = A.cnt[q];
-    const bool over = c > A.cap || A.ovf[q] != 0u;
-    const bool shortfall = !over && c < A.k && tu > tb;
-    if (over || shortfall) {
-      if (round > 0) {
-        fallback_scan<CT, D>(A, q, 0ull, cache, sel_buf, S, qv, &nbuf);
-        return;
-      }
-      // Rescue threshold: the proven bound after a shortfall; after an overflow, the k-th
-      // best stored candidate (k real items reach it).
-      uint32_t nt = tb;
-      if (over) {
-        nt = tu;
-        const int64_t stored = min<int64_t>(c, A.cap);
-        if (stored >= A.k) {
-          const uint32_t kth = (uint32_t)(select_top([&](int64_t i) { return list[i]; }, stored, A.k, S).prefix >> 32);
-          nt = kth > nt ? kth : nt;
-        }
-      }
-      if (threadIdx.x == 0) {
-        const uint32_t slot = atomicAdd(A.nfail, 1u);
-        A.flist[slot] = (uint32_t)q;
-        A.thr[q] = nt;
-        A.cnt[q] = 0u;
-        A.ovf[q] = 0u;
-      }
-      return;
-    }
-  }
-  const bool cached = c <= kSelCache;
-  int64_t live = c;
-  if (A.dense_count > 0) {
-    // a dense list's empty slots (key 0) are not candidates: select among the others only,
-    // so that no tie at the boundary involves an empty slot
-    if (threadIdx.x == 0) nbuf = 0u;
+    cached = c <= kSelCache;
+    if (t == 0) nbuf = 0u;
     __syncthreads();
     uint32_t mine = 0u;
-    for (int64_t i = threadIdx.x; i < c; i += kSelThreads) {
-      const uint64_t key = list[i];
+    for (int64_t i = t; i < c; i += kSelThreads) {
+      const uint64_t key = qlist[i];
       if (cached) cache[i] = key;
       mine += key != 0ull;
     }
     atomicAdd(&nbuf, mine);
     __syncthreads();
-    live = nbuf;
-  } else if (cached) {
-    for (int64_t i = threadIdx.x; i < c; i += kSelThreads) cache[i] = list[i];
+    const int r = (int)min<int64_t>((int64_t)nbuf, A.k);
+    if (r > 0) {
+      Sel64 sel{0ull, 0ull};
+      if (cached) {
+        auto get = [&](int64_t i) { return cache[i]; };
+        if (c > r) sel = select_top(get, c, r, S);
+        gather_sort(get, c, r, sel, sel_buf, &S.hist[0]);
+      } else {
+        auto get = [&](int64_t i) { return qlist[i]; };
+        if (c > r) sel = select_top(get, c, r, S);
+        gather_sort(get, c, r, sel, sel_buf, &S.hist[0]);
+      }
+    }
+    write_out(A, q, sel_buf, r);
+    return;
   }
-  const int r = (int)min<int64_t>(live, A.k);
+  const uint32_t tu = A.thr[q], tb = A.thrb[q];
+  if (tu == 0u) {
+    // no sampled bound for this query (fewer than K eligible sampled half-blocks)
+    fallback_scan<CT, D>(A, q, 0ull, cache, sel_buf, S, qv, &nbuf);
+    return;
+  }
+  // segment s: found (counted by the pass) and stored (what fits the segment)
+  const uint32_t found = t < A.nseg_used ? A.segcnt[(int64_t)q * A.nseg + t] : 0u;
+  const uint32_t mine = found < (uint32_t)A.capw ? found : (uint32_t)A.capw;
+  const uint2 so = block_exclusive_sum(mine, wsum);
+  const uint2 sf = block_exclusive_sum(found, wsum);
+  segoff[t] = so.x;
+  if (t == 0) segoff[kSelThreads] = so.y;
+  const int64_t stored = so.y;
+  c = sf.y;
+  const int nsu = A.nseg_used;
+  // entry i of the concatenated segments: the last segment starting at or before i
+  auto at = [&](int64_t i) {
+    int lo = 0, hi = nsu;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)segoff[mid] <= i) lo = mid; else hi = mid;
+    }
+    return qlist[(int64_t)lo * A.capw + (i - segoff[lo])];
+  };
+  __syncthreads();
+  const bool over = stored < c || A.ovf[q] != 0u;
+  const bool shortfall = !over && c < A.k && tu > tb;
+  if (over || shortfall) {
+    if (round > 0) {
+      fallback_scan<CT, D>(A, q, 0ull, cache, sel_buf, S, qv, &nbuf);
+      return;
+    }
+    // Rescue threshold: the proven bound after a shortfall; after an overflow, the k-th
+    // best stored candidate (k real items reach it).
+    uint32_t nt = tb;
+    if (over) {
+      nt = tu;
+      if (stored >= A.k) {
+        const uint32_t kth = (uint32_t)(select_top(at, stored, A.k, S).prefix >> 32);
+        nt = kth > nt ? kth : nt;
+      }
+    }
+    if (t == 0) {
+      const uint32_t slot = atomicAdd(A.nfail, 1u);
+      A.flist[slot] = (uint32_t)q;
+      A.thr[q] = nt;
+      A.ovf[q] = 0u;
+    }
+    return;
+  }
+  const int r = (int)min<int64_t>(c, A.k);
   if (r > 0) {
-    if (cached) {
+    if (c <= kSelCache) {
+      // each thread copies its own segment
+      const uint64_t* seg = qlist + (int64_t)t * A.capw;
+      for (uint32_t i = 0; i < mine; ++i) cache[segoff[t] + i] = seg[i];
       __syncthreads();
       auto get = [&](int64_t i) { return cache[i]; };
       Sel64 sel{0ull, 0ull};
       if (c > r) sel = select_top(get, c, r, S);
       gather_sort(get, c, r, sel, sel_buf, &S.hist[0]);
     } else {
-      auto get = [&](int64_t i) { return list[i]; };
-      const Sel64 sel = select_top(get, c, r, S);
-      gather_sort(get, c, r, sel, sel_buf, &S.hist[0]);
+      const Sel64 sel = select_top(at, c, r, S);
+      gather_sort(at, c, r, sel, sel_buf, &S.hist[0]);
     }
   }
   write_out(A, q, sel_buf, r);
@@ -317,18 +425,23 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
 struct Plan {
   int b, b32, k, d, qdt, cdt;
   int64_t n, n32;
-  int rm, nqf, nqblk, G, rest;
+  int rm, nqf, nqblk, G, rest, nseg;
   bool dense;
-  int64_t cap;
-  size_t off_qtile, off_qexp, off_thr, off_thrb, off_cnt, off_ovf, off_nfail, off_flist, off_del,
-      off_cand, fixed;
+  int64_t capw;  // candidate entries per list segment
+  size_t off_qtile, off_qexp, off_thr, off_thrb, off_ovf, off_nfail, off_flist, off_segcnt,
+      off_del, off_cand, fixed;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static int64_t default_cap(int64_t n32, int k) {
-  const int64_t want = std::max<int64_t>(16 * (int64_t)k, 32768);
-  return std::min<int64_t>(n32 * kFrag, want);
+// Segments per query list: one per corpus slice of a pass (at most one slice per CU).
+static int list_segments() { return std::min(device_cu_count(), kMaxSegments); }
+
+// Default candidate capacity per query: 16 K, at least 32768, at most the corpus, spread
+// over the segments.
+static int64_t default_capw(int64_t n32, int k, int nseg) {
+  const int64_t want = std::min<int64_t>(n32 * kFrag, std::max<int64_t>(16 * (int64_t)k, 32768));
+  return (want + nseg - 1) / nseg;
 }
 
 // Rank of the estimated threshold among the G delegates: the sample holds a fraction
@@ -343,7 +456,8 @@ static int estimate_rank(int64_t n32, int G, int k) {
   return std::max(1, std::min(k, r));
 }
 
-static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt, int64_t cap) {
+// capq: candidate capacity per query (< 0: the default).
+static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt, int64_t capq) {
   p.b = b;
   p.b32 = (b + 31) / 32 * 32;
   p.k = k;
@@ -361,8 +475,9 @@ static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt,
   p.nqf = 1;
   while (p.nqf < per) p.nqf <<= 1;
   p.nqblk = (need + p.nqf - 1) / p.nqf;
-  p.cap = cap < 0 ? default_cap(p.n32, k) : cap;
-  p.dense = p.n32 < 2 * (int64_t)k + 64 && p.n32 * kFrag <= p.cap;
+  p.nseg = list_segments();
+  p.capw = capq < 0 ? default_capw(p.n32, k, p.nseg) : capq / p.nseg;
+  p.dense = p.n32 < 2 * (int64_t)k + 64 && p.n32 * kFrag <= p.nseg * p.capw;
   p.G = p.dense ? 0 : (int)std::min<int64_t>(p.n32, kMaxSample);
   p.rest = p.dense ? 0 : estimate_rank(p.n32, p.G, k);
   const int E = elem_bytes(cdt);
@@ -375,20 +490,21 @@ static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt,
   o = align256(o + (size_t)b * 4);
   p.off_thrb = o;
   o = align256(o + (size_t)b * 4);
-  p.off_cnt = o;
-  o = align256(o + (size_t)b * 4);
   p.off_ovf = o;
   o = align256(o + (size_t)b * 4);
   p.off_nfail = o;
   o = align256(o + 4);
   p.off_flist = o;
   o = align256(o + (size_t)b * 4);
+  p.off_segcnt = o;
+  o = align256(o + (size_t)b * p.nseg * 4);
   p.off_del = o;
-  o = align256(o + (size_t)std::min<int64_t>(p.n32, kMaxSample) * p.b32 * 4);
+  const int64_t gmax = std::min<int64_t>(p.n32, kMaxSample);
+  const int64_t tgroups = ((gmax + p.rm - 1) / p.rm + 15) / 16;
+  o = align256(o + (size_t)tgroups * 16 * p.rm * 2 * p.b32 * 4);
   p.off_cand = o;
   p.fixed = o;
 }
-
 
 template <int CT, int D>
 static int run_topk(const Plan& p, const void* queries, const void* corpus, const float* row_scale,
@@ -398,8 +514,8 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   int* qexp = (int*)(ws + p.off_qexp);
   uint32_t* thr = (uint32_t*)(ws + p.off_thr);
   uint32_t* thrb = (uint32_t*)(ws + p.off_thrb);
-  uint32_t* cnt = (uint32_t*)(ws + p.off_cnt);
   uint32_t* ovf = (uint32_t*)(ws + p.off_ovf);
+  uint32_t* segcnt = (uint32_t*)(ws + p.off_segcnt);
   uint32_t* nfail = (uint32_t*)(ws + p.off_nfail);
   uint32_t* flist = (uint32_t*)(ws + p.off_flist);
   uint32_t* del = (uint32_t*)(ws + p.off_del);
@@ -407,10 +523,10 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
 
   if (p.qdt == MIPS_F32)
     hipLaunchKernelGGL((prep_queries_kernel<CT, MIPS_F32, D>), dim3(p.b32 / 32), dim3(64), 0, s,
-                       queries, p.b, qtile, qexp, cnt, ovf, nfail);
+                       queries, p.b, qtile, qexp, ovf, nfail);
   else
     hipLaunchKernelGGL((prep_queries_kernel<CT, MIPS_BF16, D>), dim3(p.b32 / 32), dim3(64), 0, s,
-                       queries, p.b, qtile, qexp, cnt, ovf, nfail);
+                       queries, p.b, qtile, qexp, ovf, nfail);
   int rc = check_launch();
   if (rc) return rc;
 
@@ -426,15 +542,16 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   A.b32 = p.b32;
   A.nqblk = p.nqblk;
   A.thr = thr;
-  A.cnt = cnt;
+  A.segcnt = segcnt;
   A.ovf = ovf;
   A.cand = cand;
-  A.cap = p.cap;
+  A.capw = p.capw;
+  A.nseg = p.nseg;
   A.del = del;
 
   const int cus = device_cu_count();
   auto slices_for = [&](int64_t ntiles, int nqblk) {
-    int64_t want = std::max<int64_t>(1, cus / nqblk);
+    int64_t want = std::max<int64_t>(1, std::min(cus, p.nseg) / nqblk);
     if (want >= 8) want = want / 8 * 8;
     return (int)std::max<int64_t>(1, std::min<int64_t>(ntiles, want));
   };
@@ -448,10 +565,11 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   S.n = p.n;
   S.b = p.b;
   S.k = p.k;
-  S.cap = p.cap;
+  S.capw = p.capw;
+  S.nseg = p.nseg;
   S.thr = thr;
   S.thrb = thrb;
-  S.cnt = cnt;
+  S.segcnt = segcnt;
   S.ovf = ovf;
   S.cand = cand;
   S.nfail = nfail;
@@ -478,11 +596,12 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   // sample pass and thresholds
   A.dense = 0;
   A.nfrag = p.G;
+  A.sample_step = ((uint64_t)p.n32 << 32) / (uint64_t)p.G;
   A.ntiles = (p.G + p.rm - 1) / p.rm;
   A.nslices = slices_for(A.ntiles, p.nqblk);
   if ((rc = launch_score_nqf<CT, D, MODE_AUX>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
-  hipLaunchKernelGGL(sample_threshold_kernel, dim3(p.b), dim3(kSelThreads), 0, s, del, p.G, p.b32,
-                     p.b, p.k, p.rest, thr, thrb);
+  hipLaunchKernelGGL(sample_threshold_kernel, dim3(p.b), dim3(kSelThreads), 0, s, del, (int)A.ntiles,
+                     2 * p.rm, p.b32, p.b, p.k, p.rest, thr, thrb);
   if ((rc = check_launch())) return rc;
 
   // main pass
@@ -493,6 +612,7 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   if ((rc = launch_score_nqf<CT, D, MODE_MAIN>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
   if (ev1) (void)hipEventRecord(ev1, s);
   S.dense_count = 0;
+  S.nseg_used = A.nslices;
   hipLaunchKernelGGL((final_select_kernel<CT, D>), dim3(p.b), dim3(kSelThreads), 0, s, S, 0);
   if ((rc = check_launch())) return rc;
 
@@ -503,6 +623,7 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   R.nqblk = 1;
   R.nslices = slices_for(A.ntiles, 1);
   if ((rc = launch_score_nqf<CT, D, MODE_MAIN>(p.nqf, R, R.nslices, s))) return rc;
+  S.nseg_used = R.nslices;
   hipLaunchKernelGGL((final_select_kernel<CT, D>), dim3(p.b), dim3(kSelThreads), 0, s, S, 1);
   return check_launch();
 }
@@ -542,7 +663,17 @@ size_t mips_topk_workspace_size(int32_t b, int64_t n, int32_t d, int32_t k, int3
   if (mips::validate_topk(query_dtype, b, corpus_dtype, n, d, k) != MIPS_OK) return 0;
   mips::Plan p;
   mips::make_plan(p, b, n, d, k, query_dtype, corpus_dtype, -1);
-  return p.fixed + (size_t)b * (size_t)p.cap * 8u;
+  return p.fixed + (size_t)b * (size_t)p.nseg * (size_t)p.capw * 8u;
+}
+
+size_t mips_topk_workspace_size_for(int32_t b, int64_t n, int32_t d, int32_t k, int32_t query_dtype,
+                                    int32_t corpus_dtype, int64_t candidates_per_query) {
+  if (mips::validate_topk(query_dtype, b, corpus_dtype, n, d, k) != MIPS_OK) return 0;
+  if (candidates_per_query < 1) return 0;
+  mips::Plan p;
+  mips::make_plan(p, b, n, d, k, query_dtype, corpus_dtype, -1);
+  const int64_t capw = (candidates_per_query + p.nseg - 1) / p.nseg;
+  return p.fixed + (size_t)b * (size_t)p.nseg * (size_t)capw * 8u;
 }
 
 int mips_topk(const void* queries, int32_t query_dtype, int32_t b, const void* corpus,
@@ -560,10 +691,10 @@ int mips_topk(const void* queries, int32_t query_dtype, int32_t b, const void* c
   mips::Plan p;
   mips::make_plan(p, b, n, d, k, query_dtype, corpus_dtype, -1);
   if (workspace_bytes < p.fixed) return MIPS_ERR_WORKSPACE;
-  int64_t cap = (int64_t)((workspace_bytes - p.fixed) / ((size_t)b * 8u));
-  cap = std::min<int64_t>(cap, p.n32 * 32);
-  if (cap < std::min<int64_t>(n, k)) return MIPS_ERR_WORKSPACE;
-  mips::make_plan(p, b, n, d, k, query_dtype, corpus_dtype, cap);
+  // candidate capacity per query: whole segments of what the workspace holds
+  const int64_t capq = (int64_t)((workspace_bytes - p.fixed) / ((size_t)b * 8u));
+  if (capq / p.nseg < 1) return MIPS_ERR_WORKSPACE;
+  mips::make_plan(p, b, n, d, k, query_dtype, corpus_dtype, capq);
   hipStream_t s = (hipStream_t)stream;
   uint8_t* ws = (uint8_t*)workspace;
   switch (corpus_dtype) {

@@ -112,11 +112,24 @@ MIPS_API int mips_prepare_corpus(const float *src, int64_t rows, int64_t row_off
 
 /*
  * mips_topk_workspace_size -- bytes of device workspace mips_topk needs for these
- * sizes with its default candidate capacity. A larger workspace raises the per-query
- * candidate capacity; see mips_topk. Returns 0 for unsupported arguments.
+ * sizes with its default candidate capacity (about max(16 k, 32768) per query, at most
+ * the corpus). A larger workspace raises the per-query candidate capacity; see
+ * mips_topk. Returns 0 for unsupported arguments. The size depends on the current
+ * device's compute-unit count (the candidate lists are split into one segment per
+ * corpus slice, at most one slice per compute unit).
  */
 MIPS_API size_t mips_topk_workspace_size(int32_t b, int64_t n, int32_t d, int32_t k,
                                 int32_t query_dtype, int32_t corpus_dtype);
+
+/*
+ * mips_topk_workspace_size_for -- as mips_topk_workspace_size, for a candidate capacity
+ * of at least candidates_per_query (>= 1) per query instead of the default. A capacity
+ * below the number of candidates a query produces makes mips_topk rescan that query
+ * (slower, same result). Returns 0 for unsupported arguments.
+ */
+MIPS_API size_t mips_topk_workspace_size_for(int32_t b, int64_t n, int32_t d, int32_t k,
+                                    int32_t query_dtype, int32_t corpus_dtype,
+                                    int64_t candidates_per_query);
 
 /*
  * mips_topk -- exact top-k by inner product of every query against every corpus row
@@ -140,9 +153,11 @@ MIPS_API size_t mips_topk_workspace_size(int32_t b, int64_t n, int32_t d, int32_
  *                min(k, eligible) best (score, id) pairs, score descending then id
  *                ascending; remaining slots are (-INFINITY, -1). Scores are fp32
  *                accumulations of the stored operands (no temperature is applied).
- *   workspace    device, 256-byte aligned, at least mips_topk_workspace_size(...) bytes;
- *                its contents are undefined between calls. Calls that share a workspace
- *                must be ordered on one stream.
+ *   workspace    device, 256-byte aligned; the fixed part plus at least one candidate
+ *                per query and list segment (mips_topk_workspace_size gives the default,
+ *                mips_topk_workspace_size_for any other capacity); its contents are
+ *                undefined between calls. Calls that share a workspace must be ordered on
+ *                one stream.
  * Errors: INVALID_ARG (NULL where a buffer is required, b/n/k out of range, fp8 without
  * row_scale, misalignment), UNSUPPORTED (d, k > MIPS_K_MAX, dtype pair), WORKSPACE
  * (workspace_bytes too small), HIP (a launch failed).

@@ -58,6 +58,12 @@ def test_workspace_size(L):
     assert L.mips_topk_workspace_size(4, 100, 128, 1025, BF16, BF16) == 0
     assert L.mips_topk_workspace_size(4, 100, 48, 10, BF16, BF16) == 0
     assert L.mips_topk_workspace_size(4, 100, 128, 10, BF16, F32) == 0  # bf16 queries need a bf16/fp8 corpus
+    # an explicit capacity: more candidates, more bytes; 0 for a capacity below 1
+    small = L.mips_topk_workspace_size_for(256, 10_000_000, 128, 500, BF16, BF16, 1)
+    big = L.mips_topk_workspace_size_for(256, 10_000_000, 128, 500, BF16, BF16, 1 << 16)
+    assert 0 < small < ws < big
+    assert big - small >= 256 * ((1 << 16) - 1024) * 8
+    assert L.mips_topk_workspace_size_for(256, 10_000_000, 128, 500, BF16, BF16, 0) == 0
 
 
 def _topk(L, q=0x1000, qdt=BF16, b=4, corpus=0x2000, scale=None, cdt=BF16, n=1000, d=128,

@@ -185,12 +185,12 @@ def test_all_equal_corpus_ties(n):
 
 
 def test_small_workspace_forces_exact_rescan():
-    """A workspace with room for 64 candidates per query: lists overflow, every query is
-    rescanned exactly, and the result still matches the oracle."""
+    """A workspace with room for one candidate per query and list segment: the lists
+    overflow, the queries are rescued and rescanned exactly, and the result still matches
+    the oracle."""
     n, d, b, k = 30000, 128, 9, 40
-    default_cap = min((n + 31) // 32 * 32, max(16 * k, 32768))
-    fixed = mips.workspace_size(b, n, d, k, "bf16", "bf16") - b * default_cap * 8
-    run_case(n, d, b, k, "bf16", "bf16", seed=12, workspace_bytes=fixed + b * 64 * 8)
+    wsb = mips.workspace_size(b, n, d, k, "bf16", "bf16", candidates_per_query=1)
+    run_case(n, d, b, k, "bf16", "bf16", seed=12, workspace_bytes=wsb)
 
 
 # -------------------------------------------------------------------- invariants
