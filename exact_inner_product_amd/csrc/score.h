@@ -266,24 +266,25 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
           if (__ballot(m[g] >= T) == 0ull) continue;
           const uint32_t w = __builtin_amdgcn_readlane(xwv, g);
           const uint32_t idb = (uint32_t)((j0 + g) * kFrag);
-          // value i of every lane: one ballot of `v >= T`; the rows it covers are rlo (lanes
-          // 0-31) and rlo + 4 (lanes 32-63), so the exclusion bits turn into a lane mask
-          // on the scalar unit; each survivor is read out with readlane and appended by
-          // lane 0 (survivors are rare: usually one per hit block). The loop stays rolled
-          // (a wave-uniform index into the accumulators) to keep this cold code small.
-#pragma unroll 1
-          for (int i = 0; i < 16; ++i) {
-            uint64_t P = __ballot(acc[g][i] >= T);
-            if (P == 0ull) continue;
-            constexpr uint64_t kLo = 0x00000000FFFFFFFFull, kHi = 0xFFFFFFFF00000000ull;
-            const int rlo = 8 * (i >> 2) + (i & 3);
-            P &= ~((((w >> rlo) & 1u) ? kLo : 0ull) | (((w >> (rlo + 4)) & 1u) ? kHi : 0ull));
-            while (P != 0ull) {
-              const int L = __builtin_ctzll(P);
-              P &= P - 1ull;
+          // per lane, a 16-bit mask of its values that pass: bit i <=> value i >= T and
+          // its row (8 (i >> 2) + 4 (lane >> 5) + (i & 3)) is neither excluded nor padding
+          uint32_t pm = 0u;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pm |= (acc[g][i] >= T ? 1u : 0u) << i;
+          const uint32_t wl = w >> (4 * (lane >> 5));
+          pm &= ~((wl & 0xFu) | ((wl >> 4) & 0xF0u) | ((wl >> 8) & 0xF00u) | ((wl >> 12) & 0xF000u));
+          // walk the passing (lane, value) pairs on the scalar unit: usually one
+          uint64_t H = __ballot(pm != 0u);
+          while (H != 0ull) {
+            const int L = __builtin_ctzll(H);
+            H &= H - 1ull;
+            uint32_t pl = (uint32_t)__builtin_amdgcn_readlane((int)pm, L);
+            const int qcol = qf * kFrag + (L & 31);
+            while (pl != 0u) {
+              const int i = __builtin_ctz(pl);
+              pl &= pl - 1u;
               const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[g][i]), L));
-              const uint32_t id = idb + (uint32_t)(rlo + 4 * (L >> 5));
-              const int qcol = qf * kFrag + (L & 31);
+              const uint32_t id = idb + (uint32_t)(8 * (i >> 2) + 4 * (L >> 5) + (i & 3));
               if (st_n < kStageCap) {
                 if (lane == 0) {
                   st_key[st_n] = composite(score_key(v), id);
