@@ -4,6 +4,7 @@
 #pragma once
 
 #include "common.h"
+#include "../../include/mips.h"
 
 namespace mips {
 
@@ -113,32 +114,89 @@ __device__ Sel64 select_top(Get get, int64_t n, int r, SelScratch& S) {
   return Sel64{prefix, mask};
 }
 
-// Descending bitonic sort of p (a power of two) 64-bit keys in LDS.
-__device__ inline void bitonic_desc(uint64_t* s, int p) {
-  for (int size = 2; size <= p; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < (p >> 1); i += kSelThreads) {
-        const int lo = 2 * stride * (i / stride) + (i % stride);
-        const int hi = lo + stride;
-        const bool desc = (lo & size) == 0;
-        const uint64_t x = s[lo], y = s[hi];
-        if ((x < y) == desc) {
-          s[lo] = y;
-          s[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
 __device__ __forceinline__ int pow2_at_least(int x) {
   int p = 1;
   while (p < x) p <<= 1;
   return p;
 }
 
-// Gathers the r selected keys of `get` into out[0..r) and sorts them descending.
+__device__ __forceinline__ void cmp_swap_desc(uint64_t& a, uint64_t& b, bool desc) {
+  const bool sw = desc ? a < b : a > b;
+  const uint64_t x = a;
+  a = sw ? b : a;
+  b = sw ? x : b;
+}
+
+// Sorts s[0..r) descending in place, r <= P (P a power of two, 2 <= P <= MIPS_K_MAX), as
+// a bitonic network held in registers and fully unrolled: element e = t + kSelThreads * h
+// lives in thread t, slot h. Partners less than a wave apart are exchanged by constant
+// shuffles, partners in another slot of the same thread in registers, and only the strides
+// of at least a wave and less than kSelThreads go through LDS (with barriers).
+template <int P>
+__device__ void bitonic_sort_desc_p(uint64_t* s, int r) {
+  constexpr int kPer = (P + kSelThreads - 1) / kSelThreads;
+  const int t = threadIdx.x;
+  uint64_t x[kPer];
+#pragma unroll
+  for (int h = 0; h < kPer; ++h) {
+    const int e = t + kSelThreads * h;
+    x[h] = (e < r) ? s[e] : 0ull;  // padding (0) sinks to the end
+  }
+  __syncthreads();
+#pragma unroll
+  for (int size = 2; size <= P; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride >= kSelThreads) {
+        const int hs = stride / kSelThreads;
+#pragma unroll
+        for (int h = 0; h < kPer; ++h) {
+          if ((h & hs) == 0) {
+            const int e = t + kSelThreads * h;
+            cmp_swap_desc(x[h], x[h | hs], (e & size) == 0);
+          }
+        }
+      } else {
+        uint64_t y[kPer];
+        if (stride >= kWave) {
+#pragma unroll
+          for (int h = 0; h < kPer; ++h) s[t + kSelThreads * h] = x[h];
+          __syncthreads();
+#pragma unroll
+          for (int h = 0; h < kPer; ++h) y[h] = s[(t ^ stride) + kSelThreads * h];
+          __syncthreads();
+        } else {
+#pragma unroll
+          for (int h = 0; h < kPer; ++h) y[h] = shfl_xor_u64(x[h], stride);
+        }
+#pragma unroll
+        for (int h = 0; h < kPer; ++h) {
+          const int e = t + kSelThreads * h;
+          const bool keep_hi = ((e & stride) == 0) == ((e & size) == 0);
+          const uint64_t hi = x[h] > y[h] ? x[h] : y[h];
+          const uint64_t lo = x[h] > y[h] ? y[h] : x[h];
+          x[h] = keep_hi ? hi : lo;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < kPer; ++h) {
+    const int e = t + kSelThreads * h;
+    if (e < r) s[e] = x[h];
+  }
+  __syncthreads();
+}
+
+__device__ inline void bitonic_sort_desc(uint64_t* s, int r) {
+  if (r <= 64) bitonic_sort_desc_p<64>(s, r);
+  else if (r <= 256) bitonic_sort_desc_p<256>(s, r);
+  else if (r <= 512) bitonic_sort_desc_p<512>(s, r);
+  else bitonic_sort_desc_p<1024>(s, r);
+}
+
+// Gathers the r selected keys of `get` into out[0..r) and sorts them descending. The keys
+// are distinct (composite keys carry the id).
 template <typename Get>
 __device__ void gather_sort(Get get, int64_t n, int r, Sel64 sel, uint64_t* out, uint32_t* cnt) {
   if (threadIdx.x == 0) *cnt = 0u;
@@ -151,10 +209,7 @@ __device__ void gather_sort(Get get, int64_t n, int r, Sel64 sel, uint64_t* out,
     }
   }
   __syncthreads();
-  const int p = pow2_at_least(r < 2 ? 2 : r);
-  for (int i = r + threadIdx.x; i < p; i += kSelThreads) out[i] = 0u;
-  __syncthreads();
-  bitonic_desc(out, p);
+  bitonic_sort_desc(out, r);
 }
 
 }  // namespace mips

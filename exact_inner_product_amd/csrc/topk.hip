@@ -19,7 +19,7 @@
 //                    threshold are resolved item by item (exclusion bitmap, threshold) and
 //                    the survivors are appended to the query's candidate list.
 //   final_select     per query, a radix select over 64-bit composite keys (score key << 32 |
-//                    ~id) of its candidates and a bitonic sort: score descending, then id
+//                    ~id) of its candidates and a rank sort: score descending, then id
 //                    ascending. A query whose estimated threshold proved too high (fewer
 //                    than K candidates) or whose list overflowed is queued for a rescue pass
 //                    with a proven threshold, and then selected again.
@@ -41,6 +41,10 @@ namespace mips {
 
 
 // ------------------------------------------------------------------ query prep
+// Queries -> MFMA operand tile (the packed layout of the corpus, 32 queries per block).
+// One workgroup of 64 threads per (32-query block, 1 KiB chunk); thread s writes slot s.
+// For an fp8 corpus each query row is quantised with its own power-of-two scale (the
+// corpus rule), recomputed by every thread that needs it. Clears the per-query flags.
 template <int CT, int QT, int D>
 __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict__ queries, int b,
                                                           uint8_t* __restrict__ qtile,
@@ -49,7 +53,8 @@ __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict
                                                           uint32_t* __restrict__ nfail) {
   constexpr int NCH = chunks_per_block(CT, D);
   const int lane = threadIdx.x;
-  const int q = blockIdx.x * kFrag + (lane & 31);
+  const int qb = blockIdx.x / NCH, c = blockIdx.x % NCH;
+  const int q = qb * kFrag + (lane & 31);
   const bool live = q < b;
   auto val = [&](int dim) -> float {
     if (!live) return 0.0f;
@@ -63,24 +68,21 @@ __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict
     int t = e4m3_scale_exp(m);
     t = t < -126 ? -126 : (t > 127 ? 127 : t);
     sinv = exp2_int(-t);
-    if (lane < 32) qexp[q] = t + 127;
+    if (c == 0 && lane < 32) qexp[q] = t + 127;
   }
-  uint8_t* out = qtile + (int64_t)blockIdx.x * block_bytes(CT, D);
-  for (int c = 0; c < NCH; ++c) {
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (CT == MIPS_F32) {
-      for (int t = 0; t < 4; ++t) v[t] = __float_as_uint(val(slot_dim(CT, c, lane, t)));
-    } else if (CT == MIPS_BF16) {
-      for (int t = 0; t < 8; t += 2)
-        v[t >> 1] = (uint32_t)f32_to_bf16(val(slot_dim(CT, c, lane, t))) |
-                    ((uint32_t)f32_to_bf16(val(slot_dim(CT, c, lane, t + 1))) << 16);
-    } else {
-      for (int t = 0; t < 16; ++t)
-        v[t >> 2] |= (uint32_t)f32_to_e4m3(val(slot_dim(CT, c, lane, t)) * sinv) << (8 * (t & 3));
-    }
-    *(u32x4_t*)(out + (int64_t)c * kChunkBytes + lane * 16) = v;
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (CT == MIPS_F32) {
+    for (int t = 0; t < 4; ++t) v[t] = __float_as_uint(val(slot_dim(CT, c, lane, t)));
+  } else if (CT == MIPS_BF16) {
+    for (int t = 0; t < 8; t += 2)
+      v[t >> 1] = (uint32_t)f32_to_bf16(val(slot_dim(CT, c, lane, t))) |
+                  ((uint32_t)f32_to_bf16(val(slot_dim(CT, c, lane, t + 1))) << 16);
+  } else {
+    for (int t = 0; t < 16; ++t)
+      v[t >> 2] |= (uint32_t)f32_to_e4m3(val(slot_dim(CT, c, lane, t)) * sinv) << (8 * (t & 3));
   }
-  if (lane < 32 && live) ovf[q] = 0u;
+  *(u32x4_t*)(qtile + (int64_t)qb * block_bytes(CT, D) + (int64_t)c * kChunkBytes + lane * 16) = v;
+  if (c == 0 && lane < 32 && live) ovf[q] = 0u;
   if (blockIdx.x == 0 && lane == 0) *nfail = 0u;
 }
 
@@ -405,9 +407,16 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
   const int r = (int)min<int64_t>(c, A.k);
   if (r > 0) {
     if (c <= kSelCache) {
-      // each thread copies its own segment
+      // each thread copies its own segment, 8 entries per round trip
       const uint64_t* seg = qlist + (int64_t)t * A.capw;
-      for (uint32_t i = 0; i < mine; ++i) cache[segoff[t] + i] = seg[i];
+      for (uint32_t i0 = 0; i0 < mine; i0 += 8) {
+        uint64_t v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = i0 + e < mine ? seg[i0 + e] : 0ull;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (i0 + e < mine) cache[segoff[t] + i0 + e] = v[e];
+      }
       __syncthreads();
       auto get = [&](int64_t i) { return cache[i]; };
       Sel64 sel{0ull, 0ull};
@@ -522,10 +531,10 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   uint64_t* cand = (uint64_t*)(ws + p.off_cand);
 
   if (p.qdt == MIPS_F32)
-    hipLaunchKernelGGL((prep_queries_kernel<CT, MIPS_F32, D>), dim3(p.b32 / 32), dim3(64), 0, s,
+    hipLaunchKernelGGL((prep_queries_kernel<CT, MIPS_F32, D>), dim3(p.b32 / 32 * chunks_per_block(CT, D)), dim3(64), 0, s,
                        queries, p.b, qtile, qexp, ovf, nfail);
   else
-    hipLaunchKernelGGL((prep_queries_kernel<CT, MIPS_BF16, D>), dim3(p.b32 / 32), dim3(64), 0, s,
+    hipLaunchKernelGGL((prep_queries_kernel<CT, MIPS_BF16, D>), dim3(p.b32 / 32 * chunks_per_block(CT, D)), dim3(64), 0, s,
                        queries, p.b, qtile, qexp, ovf, nfail);
   int rc = check_launch();
   if (rc) return rc;
