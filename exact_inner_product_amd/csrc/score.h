@@ -87,8 +87,10 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
   // (composite keys, query column).
   int* qid_lds = (int*)(lds + (size_t)QB * D * E);
   uint32_t* seg_lds = (uint32_t*)(qid_lds + QB);  // survivors per query column (this segment)
-  uint64_t* st_key = (uint64_t*)(seg_lds + QB) + wave * kStageCap;
-  uint16_t* st_q = (uint16_t*)((uint64_t*)(seg_lds + QB) + kScoreWaves * kStageCap) + wave * kStageCap;
+  float* thr_lds = (float*)(seg_lds + QB);        // threshold per query column
+  int* sexp_lds = (int*)(thr_lds + QB);           // fp8 query scale exponent per column
+  uint64_t* st_key = (uint64_t*)(sexp_lds + QB) + wave * kStageCap;
+  uint16_t* st_q = (uint16_t*)((uint64_t*)(sexp_lds + QB) + kScoreWaves * kStageCap) + wave * kStageCap;
 
   const int64_t t_begin = (int64_t)slice * A.ntiles / A.nslices;
   const int64_t t_end = (int64_t)(slice + 1) * A.ntiles / A.nslices;
@@ -98,13 +100,29 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
   for (int qb = rescue ? 0 : qblk; qb * QB < nq_total; qb += qstep) {
     const int qbase = qb * QB;
     __syncthreads();
+    // The query tile is NV 16-byte units; each thread moves PER of them, kFillBatch loads
+    // in flight per round trip.
+    constexpr int NV = QB * D * E / 16;
+    constexpr int kFillBatch = 4;
+    constexpr int PER = (NV + kScoreThreads - 1) / kScoreThreads;
     if (!rescue) {
       const int rows = min(QB, A.b32 - qbase);
       const u32x4_t* src = (const u32x4_t*)(A.qtile + (int64_t)qbase * D * E);
       u32x4_t* dst = (u32x4_t*)lds;
       const int n16 = rows * D * E / 16;
-      for (int i = threadIdx.x; i < QB * D * E / 16; i += kScoreThreads)
-        dst[i] = i < n16 ? src[i] : u32x4_t{0u, 0u, 0u, 0u};
+      for (int i0 = 0; i0 < PER; i0 += kFillBatch) {
+        u32x4_t v[kFillBatch];
+#pragma unroll
+        for (int u = 0; u < kFillBatch; ++u) {
+          const int i = (i0 + u) * kScoreThreads + threadIdx.x;
+          v[u] = (i0 + u < PER && i < n16) ? src[i] : u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kFillBatch; ++u) {
+          const int i = (i0 + u) * kScoreThreads + threadIdx.x;
+          if (i0 + u < PER && i < NV) dst[i] = v[u];
+        }
+      }
       for (int i = threadIdx.x; i < QB; i += kScoreThreads) {
         qid_lds[i] = qbase + i < A.b ? qbase + i : -1;
         seg_lds[i] = 0u;
@@ -118,33 +136,47 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
       // gather the queued queries' operand rows: 16-byte slot s of chunk c of column
       // fragment qf comes from slot (q & 31) + 32 (s >> 5) of the same chunk of q's block
       u32x4_t* dst = (u32x4_t*)lds;
-      for (int i = threadIdx.x; i < QB * D * E / 16; i += kScoreThreads) {
-        const int s = i & 63, c = (i >> 6) % NCH, qf = (i >> 6) / NCH;
-        const int q = qid_lds[qf * kFrag + (s & 31)];
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (q >= 0)
-          v = *(const u32x4_t*)(A.qtile + (int64_t)(q >> 5) * BLK + c * kChunkBytes +
-                                ((q & 31) + 32 * (s >> 5)) * 16);
-        dst[i] = v;
+      for (int i0 = 0; i0 < PER; i0 += kFillBatch) {
+        u32x4_t v[kFillBatch];
+#pragma unroll
+        for (int u = 0; u < kFillBatch; ++u) {
+          const int i = (i0 + u) * kScoreThreads + threadIdx.x;
+          v[u] = u32x4_t{0u, 0u, 0u, 0u};
+          if (i0 + u < PER && i < NV) {
+            const int s = i & 63, c = (i >> 6) % NCH, qf = (i >> 6) / NCH;
+            const int q = qid_lds[qf * kFrag + (s & 31)];
+            if (q >= 0)
+              v[u] = *(const u32x4_t*)(A.qtile + (int64_t)(q >> 5) * BLK + c * kChunkBytes +
+                                       ((q & 31) + 32 * (s >> 5)) * 16);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kFillBatch; ++u) {
+          const int i = (i0 + u) * kScoreThreads + threadIdx.x;
+          if (i0 + u < PER && i < NV) dst[i] = v[u];
+        }
       }
     }
     __syncthreads();
 
-    // This lane's query column in each fragment: threshold, fp8 exponent, global id.
-    float Tq[NQF];
-    int sbq[NQF], qgq[NQF];
-#pragma unroll
-    for (int qf = 0; qf < NQF; ++qf) {
-      const int qg = qid_lds[qf * kFrag + (lane & 31)];
-      qgq[qf] = qg;
+    // Per query column: threshold and fp8 exponent, read from LDS once per query fragment
+    // (registers are kept for the corpus stages and accumulators).
+    for (int i = threadIdx.x; i < QB; i += kScoreThreads) {
+      const int qg = qid_lds[i];
       float T = INFINITY;
       if (MODE == MODE_MAIN && qg >= 0) {
         const uint32_t k = A.thr[qg];
         if (k != 0u) T = key_threshold(k);
       }
-      Tq[qf] = T;
-      sbq[qf] = (CT == MIPS_FP8_E4M3 && qg >= 0) ? A.qexp[qg] : 127;
+      thr_lds[i] = T;
+      sexp_lds[i] = (CT == MIPS_FP8_E4M3 && qg >= 0) ? A.qexp[qg] : 127;
     }
+    __syncthreads();
+    auto Tq = [&](int qf) __attribute__((always_inline)) { return thr_lds[qf * kFrag + (lane & 31)]; };
+    auto sbq = [&](int qf) __attribute__((always_inline)) {
+      return CT == MIPS_FP8_E4M3 ? sexp_lds[qf * kFrag + (lane & 31)] : 127;
+    };
+    auto qgq = [&](int qf) __attribute__((always_inline)) { return qid_lds[qf * kFrag + (lane & 31)]; };
 
     int st_n = 0;  // staged survivors of this wave (wave-uniform; may exceed the capacity)
 
@@ -180,7 +212,7 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
 #pragma unroll
       for (int r = 0; r < RM; ++r) {
         const int64_t j = min<int64_t>(j0 + r, A.nfrag - 1);
-        const int64_t fr = (MODE == MODE_AUX && !A.dense) ? (int64_t)(((uint64_t)j * A.sample_step) >> 32) : j;
+        const int64_t fr = (MODE == MODE_SAMPLE) ? (int64_t)(((uint64_t)j * A.sample_step) >> 32) : j;
         // one buffer descriptor per block (scalar base, range = the block's bytes) and a
         // 32-bit lane offset: no per-lane 64-bit addresses to keep live
         const __amdgpu_buffer_rsrc_t rs = block_rsrc(A.corpus + fr * BLK, (int)BLK);
@@ -195,7 +227,7 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
       const int r = lane < RM ? lane : RM - 1;
       const bool live = j0 + r < A.nfrag;
       const int64_t j = live ? j0 + r : A.nfrag - 1;
-      const int64_t fr = (MODE == MODE_AUX && !A.dense) ? (int64_t)(((uint64_t)j * A.sample_step) >> 32) : j;
+      const int64_t fr = (MODE == MODE_SAMPLE) ? (int64_t)(((uint64_t)j * A.sample_step) >> 32) : j;
       // branch-free: without a bitmap, any readable word masked to zero (a conditional
       // load would make the compiler's wait counts conservative at the join)
       const uint32_t* wp = A.exclude ? A.exclude + fr : (const uint32_t*)A.corpus;
@@ -249,7 +281,7 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
     // ballot, branch-free so it interleaves with the next fragment's MFMAs. A block that
     // clears the threshold is resolved on the scalar unit (below).
     auto epi_main = [&](const f32x16_t (&acc)[RM], uint32_t xwv, int64_t j0, int qf) __attribute__((always_inline)) {
-      const float T = Tq[qf];
+      const float T = Tq(qf);
       float m[RM];
       bool any = false;
 #pragma unroll
@@ -308,19 +340,26 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
     // laid out del[tile / 16][query][tile % 16][2 RM], so that each query's delegates lie in
     // runs of 16 slots.
     auto epi_aux = [&](const f32x16_t (&acc)[RM], uint32_t xwv, int64_t j0, int qf) __attribute__((always_inline)) {
-      const int qg = qgq[qf];
-      if (A.dense) {
+      const int qg = qgq(qf);
+      if constexpr (MODE == MODE_DENSE) {
 #pragma unroll
         for (int g = 0; g < RM; ++g) {
           const int64_t j = j0 + g;
           const uint32_t w = __builtin_amdgcn_readlane(xwv, g);
+          // The stores below are per lane (padding query columns are skipped). Their only
+          // inputs are the accumulators, so without this pin the compiler may sink the
+          // MFMAs, and the VALU work that feeds their per-lane scale operand, into the
+          // lane-divergent branch, where inactive lanes leave the operand stale. The
+          // volatile statement keeps the whole product in wave-uniform control flow.
+          f32x16_t v = acc[g];
+          asm volatile("" : "+v"(v));
           if (j < A.nfrag && qg >= 0) {
             uint64_t* dst = A.cand + (int64_t)qg * A.nseg * A.capw + j * kFrag;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int row = acc_row(i, lane);
               dst[row] = ((w >> row) & 1u) ? 0ull
-                                           : composite(score_key(acc[g][i]), (uint32_t)(j * kFrag + row));
+                                           : composite(score_key(v[i]), (uint32_t)(j * kFrag + row));
             }
           }
         }
@@ -336,6 +375,7 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
             mx = ((w >> row) & 1u) ? mx : fmaxf(mx, acc[g][i]);
           }
           d[g] = (mx == -INFINITY) ? 0u : score_key(mx);
+          asm volatile("" : "+v"(d[g]));  // computed in uniform control flow, as above
         }
         const int qc = qbase + qf * kFrag + (lane & 31);
         if (qc < A.b32) {
@@ -355,24 +395,28 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
       f32x16_t acc[2][RM];
       u32x4_t bq[BREG ? 1 : NCH];
       if constexpr (BREG) {
-        mfmas(acc[0], a, sa, breg[0], sbq[0], -1);
+        mfmas(acc[0], a, sa, breg[0], sbq(0), -1);
       } else {
         load_b(bq, 0);
-        mfmas(acc[0], a, sa, bq, sbq[0], NQF > 1 ? 1 : -1);
+        mfmas(acc[0], a, sa, bq, sbq(0), NQF > 1 ? 1 : -1);
       }
       static_for<NQF>([&](auto qfc) __attribute__((always_inline)) {
         constexpr int qf = decltype(qfc)::value;
         constexpr int cur = qf & 1;
         if constexpr (qf + 1 < NQF) {
           if constexpr (BREG)
-            mfmas(acc[cur ^ 1], a, sa, breg[qf + 1], sbq[qf + 1], -1);
+            mfmas(acc[cur ^ 1], a, sa, breg[qf + 1], sbq(qf + 1), -1);
           else
-            mfmas(acc[cur ^ 1], a, sa, bq, sbq[qf + 1], qf + 2 < NQF ? qf + 2 : -1);
+            mfmas(acc[cur ^ 1], a, sa, bq, sbq(qf + 1), qf + 2 < NQF ? qf + 2 : -1);
         }
-        if constexpr (MODE == MODE_MAIN)
+        if constexpr (MODE == MODE_MAIN) {
           epi_main(acc[cur], xwv, j0, qf);
-        else
+        } else {
           epi_aux(acc[cur], xwv, j0, qf);
+          // the auxiliary epilogues have no branch that would bound the scheduler's region;
+          // without this fence it interleaves whole stages and runs out of registers
+          __builtin_amdgcn_sched_barrier(0);
+        }
       });
     };
 
@@ -380,7 +424,7 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
     // tiles): while stage i is multiplied against every query, stages i+1 .. i+NS-1 are in
     // flight. With one wave per SIMD, the bytes in flight per wave set the HBM bandwidth
     // (Little's law at several microseconds of loaded latency), hence NS - 1 = 2 stages.
-    constexpr int NS = kPipeStages;
+    constexpr int NS = pipe_stages(CT, D);
     u32x4_t a[NS][RM][NCH];
     int sa[NS][RM];
     uint32_t xw[NS];
@@ -401,10 +445,15 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
         compute_stage(a[u], sa[u], xw[u], (t + u * kScoreWaves) * RM);
         return t + (u + 1) * kScoreWaves >= t_end;
       };
-      static_assert(NS == 3, "the step chain below is written for three stages");
-      while (!(step(std::integral_constant<int, 0>{}) || step(std::integral_constant<int, 1>{}) ||
-               step(std::integral_constant<int, 2>{})))
-        t += NS * kScoreWaves;
+      static_assert(NS == 2 || NS == 3, "the step chain below is written for two or three stages");
+      if constexpr (NS == 3) {
+        while (!(step(std::integral_constant<int, 0>{}) || step(std::integral_constant<int, 1>{}) ||
+                 step(std::integral_constant<int, 2>{})))
+          t += NS * kScoreWaves;
+      } else {
+        while (!(step(std::integral_constant<int, 0>{}) || step(std::integral_constant<int, 1>{})))
+          t += NS * kScoreWaves;
+      }
     }
     if (MODE == MODE_MAIN) {
       if (st_n > 0) flush();

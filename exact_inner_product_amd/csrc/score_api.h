@@ -16,20 +16,32 @@ constexpr int kStageBurst = 256;    // room kept free before each stage
 constexpr int kStageLds = kScoreWaves * kStageCap * (8 + 2);
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int kMaxSample = 8192;    // sampled 32-row blocks
-constexpr int kPipeStages = 3;      // corpus stages held in registers per wave
+
 constexpr int kMaxSegments = 256;   // list segments per query (corpus slices of a pass)
+#ifndef MIPS_STAGE_BYTES
+#define MIPS_STAGE_BYTES 16384
+#endif
+#ifndef MIPS_PIPE_STAGES
+#define MIPS_PIPE_STAGES 3
+#endif
+constexpr int kStageBytes = MIPS_STAGE_BYTES;    // corpus bytes per wave and pipeline stage
+constexpr int kPipeStagesCfg = MIPS_PIPE_STAGES; // corpus stages in flight + in use per wave
 constexpr int kSelCache = 6144;     // candidates the final select caches in LDS
 
-enum { MODE_MAIN = 0, MODE_AUX = 1 };
+// Passes of the score kernel: the main filter pass (also the rescue pass), the sample pass
+// (delegates of a strided block sample) and the dense pass (every score, small corpora).
+enum { MODE_MAIN = 0, MODE_SAMPLE = 1, MODE_DENSE = 2 };
 
 // Corpus blocks per pipeline stage: 16 KiB of corpus per wave and stage (at most 4 blocks).
 __host__ __device__ constexpr int stage_frags(int ct, int d) {
-  const int r = 16384 / (kFrag * d * elem_bytes(ct));
+  const int r = kStageBytes / (kFrag * d * elem_bytes(ct));
   return r < 1 ? 1 : (r > 4 ? 4 : r);
 }
+// Corpus stages held in registers per wave (the one being multiplied and the prefetched).
+__host__ __device__ constexpr int pipe_stages(int ct, int d) { return kPipeStagesCfg; }
 // LDS of a score workgroup holding 32 * nqf queries.
 __host__ __device__ constexpr int score_lds_bytes(int ct, int d, int nqf) {
-  return kFrag * nqf * (d * elem_bytes(ct) + 8) + kStageLds;
+  return kFrag * nqf * (d * elem_bytes(ct) + 16) + kStageLds;
 }
 __host__ __device__ constexpr bool nqf_fits(int ct, int d, int nqf) {
   return score_lds_bytes(ct, d, nqf) <= kLdsLimit;
@@ -49,7 +61,6 @@ struct ScoreArgs {
   int b32;
   int nqblk;        // query blocks in the grid
   int nslices;      // corpus slices in the grid
-  int dense;        // AUX pass: write every score (1) or the sample delegates (0)
   const uint32_t* thr;    // per-query threshold keys (0: query not scored here)
   uint32_t* segcnt;       // [b][nseg] survivors found per (query, segment)
   uint32_t* ovf;

@@ -9,5 +9,6 @@
 
 namespace mips {
 template int launch_score_nqf<MIPS_CT, MIPS_D, MODE_MAIN>(int, const ScoreArgs&, int, hipStream_t);
-template int launch_score_nqf<MIPS_CT, MIPS_D, MODE_AUX>(int, const ScoreArgs&, int, hipStream_t);
+template int launch_score_nqf<MIPS_CT, MIPS_D, MODE_SAMPLE>(int, const ScoreArgs&, int, hipStream_t);
+template int launch_score_nqf<MIPS_CT, MIPS_D, MODE_DENSE>(int, const ScoreArgs&, int, hipStream_t);
 }  // namespace mips

@@ -7,7 +7,7 @@
 //
 //   prep_queries     queries -> MFMA operand layout (E4M3 + power-of-two scale for an
 //                    fp8 corpus); clears the per-query flags.
-//   score<AUX>       sample pass: scores a strided sample of G 32-row blocks and writes,
+//   score<SAMPLE>    sample pass: scores a strided sample of G 32-row blocks and writes,
 //                    per (block, query), the best eligible score of the block ("delegate").
 //   sample_threshold per query: the K-th largest delegate is a proven lower bound of the
 //                    K-th best score (K distinct blocks hold an item at least that good);
@@ -590,12 +590,11 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   timing_events(&ev0, &ev1);
 
   if (p.dense) {
-    A.dense = 1;
     A.nfrag = p.n32;
     A.ntiles = (p.n32 + p.rm - 1) / p.rm;
     A.nslices = slices_for(A.ntiles, p.nqblk);
     if (ev0) (void)hipEventRecord(ev0, s);
-    if ((rc = launch_score_nqf<CT, D, MODE_AUX>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
+    if ((rc = launch_score_nqf<CT, D, MODE_DENSE>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
     if (ev1) (void)hipEventRecord(ev1, s);
     S.dense_count = p.n32 * kFrag;
     hipLaunchKernelGGL((final_select_kernel<CT, D>), dim3(p.b), dim3(kSelThreads), 0, s, S, 0);
@@ -603,12 +602,11 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   }
 
   // sample pass and thresholds
-  A.dense = 0;
   A.nfrag = p.G;
   A.sample_step = ((uint64_t)p.n32 << 32) / (uint64_t)p.G;
   A.ntiles = (p.G + p.rm - 1) / p.rm;
   A.nslices = slices_for(A.ntiles, p.nqblk);
-  if ((rc = launch_score_nqf<CT, D, MODE_AUX>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
+  if ((rc = launch_score_nqf<CT, D, MODE_SAMPLE>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
   hipLaunchKernelGGL(sample_threshold_kernel, dim3(p.b), dim3(kSelThreads), 0, s, del, (int)A.ntiles,
                      2 * p.rm, p.b32, p.b, p.k, p.rest, thr, thrb);
   if ((rc = check_launch())) return rc;
