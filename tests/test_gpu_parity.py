@@ -35,12 +35,20 @@ def _excl_tensor(bitmap, dev):
     return torch.from_numpy(bitmap.view(np.int32)).to(dev)
 
 
-def run_case(n, d, b, k, cdt, qdt, seed, excl=0.0, workspace_bytes=None, x=None):
+def run_case(n, d, b, k, cdt, qdt, seed, excl=0.0, workspace_bytes=None, x=None, qraw=None,
+             bitmap=None):
     dev = _dev()
     w = _workload(n, d, b, k, cdt, qdt, seed, excl)
     x = w.corpus() if x is None else x
-    qraw = w.queries()
-    bitmap = w.exclude_bitmap()
+    qraw = w.queries() if qraw is None else qraw
+    excluded = None
+    if bitmap is None:
+        bitmap = w.exclude_bitmap()
+        if bitmap is not None:
+            excluded = set(w.excluded_ids().tolist())
+    else:
+        ids = np.arange(n)
+        excluded = set(ids[((bitmap[ids >> 5] >> (ids & 31).astype(np.uint32)) & 1) == 1].tolist())
     corpus, q = _gpu_inputs(w, x, qraw, dev)
     ws = None if workspace_bytes is None else mips.empty_workspace(workspace_bytes, dev)
     print(f"case n={n} d={d} b={b} k={k} {cdt}/{qdt} excl={excl} seed={seed}", flush=True)
@@ -50,8 +58,7 @@ def run_case(n, d, b, k, cdt, qdt, seed, excl=0.0, workspace_bytes=None, x=None)
     c_or, sc_or = oracle.prepare(x, cdt)
     q_or, _ = oracle.prepare(qraw, qdt)
     o_s, o_i = oracle.topk(q_or, qdt, c_or, cdt, k, row_scale=sc_or, exclude=bitmap)
-    excluded = set(w.excluded_ids().tolist()) if bitmap is not None else set()
-    return check_topk(s, i, o_s, o_i, q_or, qdt, c_or, cdt, sc_or, excluded, n, TOL[cdt],
+    return check_topk(s, i, o_s, o_i, q_or, qdt, c_or, cdt, sc_or, excluded or set(), n, TOL[cdt],
                       floor=floor_for(cdt, qdt))
 
 
@@ -191,6 +198,46 @@ def test_small_workspace_forces_exact_rescan():
     n, d, b, k = 30000, 128, 9, 40
     wsb = mips.workspace_size(b, n, d, k, "bf16", "bf16", candidates_per_query=1)
     run_case(n, d, b, k, "bf16", "bf16", seed=12, workspace_bytes=wsb)
+
+
+def _sampled_blocks(n, g_max=8192):
+    """Blocks the sample pass reads: an even integer stride over the 32-row blocks."""
+    n32 = (n + 31) // 32
+    g = min(n32, g_max)
+    step = (n32 << 32) // g
+    return np.array([(j * step) >> 32 for j in range(g)], np.int64)
+
+
+def test_estimate_shortfall_is_rescued():
+    """The estimated threshold sits at a low delegate rank. Planting 40 near-duplicates of
+    the query, one per sampled block, puts that estimate above all but about 40 items of the
+    whole corpus: fewer than K candidates survive the main pass, the query is rescued with
+    the proven bound, and the result is still exact."""
+    n, d, b, k = 2_000_000, 16, 2, 100
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    x[:, 0] *= 0.05  # base items are nearly orthogonal to e_0
+    blocks = _sampled_blocks(n)
+    planted = blocks[:: len(blocks) // 40][:40] * 32
+    x[planted] = 0.0
+    x[planted, 0] = 1.0
+    x[planted, 1:] = 0.02 * rng.standard_normal((40, d - 1)).astype(np.float32)
+    qraw = np.zeros((b, d), np.float32)
+    qraw[:, 0] = 1.0
+    qraw[1, 1] = 0.1
+    st = run_case(n, d, b, k, "f32", "f32", seed=31, x=x, qraw=qraw)
+    assert st["max_err"] <= 1e-5
+
+
+def test_no_sampled_bound_takes_exact_scan():
+    """Fewer than K eligible sampled half-blocks: there is no sampled bound, and the final
+    select rescans the corpus exactly (excluded items never returned, the rest padded)."""
+    n, d, b, k = 400_000, 64, 3, 100
+    keep = np.random.default_rng(32).choice(n, 60, replace=False)
+    bm = np.full((n + 31) // 32, 0xFFFFFFFF, np.uint32)
+    for t in keep:
+        bm[t >> 5] &= ~np.uint32(1 << (t & 31))
+    run_case(n, d, b, k, "bf16", "bf16", seed=32, bitmap=bm)
 
 
 # -------------------------------------------------------------------- invariants
