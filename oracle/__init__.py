@@ -8,13 +8,14 @@ Functions take and return numpy arrays:
 
 * ``prepare(x, dtype)`` -- normalise raw fp32 rows and pack them row-major
   (``"f32"`` -> float32, ``"bf16"`` -> uint16 codes, ``"fp8"`` -> uint8 E4M3 codes plus a
-  float32 per-row power-of-two scale).
+  float32 per-row power-of-two scale, ``"int8"`` -> int8 codes plus a float32 per-row
+  scale max|y|/127).
 * ``normalize(x)`` -- the fp64 normalised rows.
 * ``topk(queries, q_dtype, corpus, c_dtype, k, row_scale=None, exclude=None)`` --
   fp64 scores [b, k] and int32 ids [b, k], sorted by score descending then id ascending.
 * ``scores(...)`` -- exact scores of given (query, id) pairs.
-* ``e4m3_value``, ``bf16_value``, ``bf16_from``, ``e4m3_from``, ``e4m3_row_scale`` -- the
-  scalar format helpers, exposed for the format pins.
+* ``e4m3_value``, ``bf16_value``, ``bf16_from``, ``e4m3_from``, ``e4m3_row_scale``,
+  ``i8_from``, ``i8_row_scale`` -- the scalar format helpers, exposed for the format pins.
 """
 from __future__ import annotations
 
@@ -30,7 +31,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mips_oracle.c")
 _LIB = os.path.join(_HERE, "libmips_oracle.so")
 
-DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
+DTYPES = {"f32": 0, "bf16": 1, "fp8": 2, "int8": 3}
+_CODE_TYPES = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "int8": np.int8}
+_SCALED = ("fp8", "int8")
 _STATUS = {0: "ok", 1: "bad argument", 2: "non-finite input", 3: "out of memory"}
 
 
@@ -65,6 +68,10 @@ def lib():
         L.oracle_e4m3_from_f64.restype = C.c_uint8
         L.oracle_e4m3_row_scale.argtypes = [C.c_double]
         L.oracle_e4m3_row_scale.restype = C.c_double
+        L.oracle_i8_from_f64.argtypes = [C.c_double]
+        L.oracle_i8_from_f64.restype = C.c_int8
+        L.oracle_i8_row_scale.argtypes = [C.c_double]
+        L.oracle_i8_row_scale.restype = C.c_double
         L.oracle_l2_normalize.argtypes = [p, i64, i32, p]
         L.oracle_prepare.argtypes = [p, i64, i32, i32, p, p]
         L.oracle_topk.argtypes = [i32, p, i32, i32, p, p, i64, i32, p, i32, p, p, i32]
@@ -109,15 +116,26 @@ def e4m3_row_scale(amax: float) -> float:
     return lib().oracle_e4m3_row_scale(float(amax))
 
 
+def i8_from(v: float) -> int:
+    return int(lib().oracle_i8_from_f64(float(v)))
+
+
+def i8_row_scale(amax: float) -> float:
+    return lib().oracle_i8_row_scale(float(amax))
+
+
 def decode(codes: np.ndarray, dtype: str, row_scale: Optional[np.ndarray] = None) -> np.ndarray:
-    """fp64 values of stored operands (rows scaled for fp8)."""
+    """fp64 values of stored operands (rows scaled for fp8 and int8)."""
     if dtype == "f32":
         return np.asarray(codes, np.float32).astype(np.float64)
     if dtype == "bf16":
         u = np.asarray(codes, np.uint16).astype(np.uint32) << 16
         return u.view(np.float32).astype(np.float64)
-    table = np.array([e4m3_value(c) for c in range(256)], np.float64)
-    v = table[np.asarray(codes, np.uint8)]
+    if dtype == "int8":
+        v = np.asarray(codes, np.int8).astype(np.float64)
+    else:
+        table = np.array([e4m3_value(c) for c in range(256)], np.float64)
+        v = table[np.asarray(codes, np.uint8)]
     if row_scale is not None:
         v = v * np.asarray(row_scale, np.float64)[:, None]
     return v
@@ -135,8 +153,8 @@ def normalize(x: np.ndarray) -> np.ndarray:
 def prepare(x: np.ndarray, dtype: str) -> Tuple[np.ndarray, Optional[np.ndarray]]:
     x = np.ascontiguousarray(x, np.float32)
     rows, d = x.shape
-    out = np.empty((rows, d), {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dtype])
-    scale = np.empty(rows, np.float32) if dtype == "fp8" else None
+    out = np.empty((rows, d), _CODE_TYPES[dtype])
+    scale = np.empty(rows, np.float32) if dtype in _SCALED else None
     _check(lib().oracle_prepare(_ptr(x), rows, d, DTYPES[dtype], _ptr(out), _ptr(scale)),
            "prepare")
     return out, scale
@@ -145,8 +163,8 @@ def prepare(x: np.ndarray, dtype: str) -> Tuple[np.ndarray, Optional[np.ndarray]
 def prepare_chunks(chunks, n: int, d: int, dtype: str, threads: Optional[int] = None
                    ) -> Tuple[np.ndarray, Optional[np.ndarray]]:
     """prepare() of a corpus given as (row0, raw rows) chunks, in parallel threads."""
-    codes = np.empty((n, d), {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dtype])
-    scale = np.empty(n, np.float32) if dtype == "fp8" else None
+    codes = np.empty((n, d), _CODE_TYPES[dtype])
+    scale = np.empty(n, np.float32) if dtype in _SCALED else None
 
     def work(item):
         r0, blk = item

@@ -18,6 +18,11 @@
  *    round-to-nearest-even onto the format's value grid, derived here from the
  *    format definitions; E4M3 saturates at +-448 and uses one per-row scale,
  *    the smallest power of two 2^t with max|y| <= 448 * 2^t (a zero row gets 1).
+ *  - int8 packing with one scale per row, the rule of the quantised scoring branch
+ *    of `RecsysTwoTowerModel.forward` (its per-user quantisation, which the pages
+ *    show; the index side is taken to follow the same rule): scale =
+ *    max(max|y| / 127, 1e-12) as a float, code = y / scale rounded to nearest
+ *    (ties to even) and clipped to [-127, 127]. The stored value is code * scale.
  *  - scoring: every query against every non-excluded corpus row by dot product
  *    (`RecsysTwoTowerModel.forward`: matmul of the users against the whole index,
  *    masked by one shared type mask; Phoenix README, "How Retrieval Works", step 4).
@@ -38,7 +43,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_E4M3 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_E4M3 = 2, OR_I8 = 3 };
 enum { OR_OK = 0, OR_BAD_ARG = 1, OR_NONFINITE = 2, OR_NOMEM = 3 };
 
 /* ------------------------------------------------------------------ formats */
@@ -149,6 +154,25 @@ double oracle_e4m3_row_scale(double amax)
     return ldexp(1.0, t);
 }
 
+/* int8 per-row scale: the largest magnitude over 127, at least 1e-12, rounded to a
+ * float (the scale is stored as a float). */
+double oracle_i8_row_scale(double amax)
+{
+    return (double)(float)fmax(amax / 127.0, 1e-12);
+}
+
+/* int8 code of v: nearest integer, ties to even (nearbyint in the default rounding
+ * mode), clipped to [-127, 127]. */
+int8_t oracle_i8_from_f64(double v)
+{
+    double r = nearbyint(v);
+    if (r > 127.0)
+        r = 127.0;
+    if (r < -127.0)
+        r = -127.0;
+    return (int8_t)r;
+}
+
 /* ------------------------------------------------------------ normalisation */
 
 /* y[r, :] = x[r, :] / sqrt(max(sum_d x[r, d]^2, 1e-12)), all in fp64. */
@@ -175,13 +199,14 @@ int oracle_l2_normalize(const float *x, int64_t rows, int32_t d, double *y)
  *   OR_F32:  float  [rows, d]  (y rounded to binary32, nearest-even)
  *   OR_BF16: uint16 [rows, d]  (bf16 codes)
  *   OR_E4M3: uint8  [rows, d]  (E4M3 codes of y / scale) and scale[rows] (float)
+ *   OR_I8:   int8   [rows, d]  (int8 codes of y / scale) and scale[rows] (float)
  */
 int oracle_prepare(const float *x, int64_t rows, int32_t d, int32_t dtype, void *out,
                    float *scale)
 {
-    if (!x || !out || rows < 0 || d <= 0 || dtype < OR_F32 || dtype > OR_E4M3)
+    if (!x || !out || rows < 0 || d <= 0 || dtype < OR_F32 || dtype > OR_I8)
         return OR_BAD_ARG;
-    if (dtype == OR_E4M3 && !scale)
+    if ((dtype == OR_E4M3 || dtype == OR_I8) && !scale)
         return OR_BAD_ARG;
     double *y = (double *)malloc(sizeof(double) * (size_t)d);
     if (!y)
@@ -199,7 +224,7 @@ int oracle_prepare(const float *x, int64_t rows, int32_t d, int32_t dtype, void 
         } else if (dtype == OR_BF16) {
             for (int32_t j = 0; j < d; ++j)
                 ((uint16_t *)out)[base + j] = oracle_bf16_from_f64(y[j]);
-        } else {
+        } else if (dtype == OR_E4M3) {
             double amax = 0.0;
             for (int32_t j = 0; j < d; ++j)
                 amax = fmax(amax, fabs(y[j]));
@@ -207,6 +232,14 @@ int oracle_prepare(const float *x, int64_t rows, int32_t d, int32_t dtype, void 
             scale[r] = (float)s;
             for (int32_t j = 0; j < d; ++j)
                 ((uint8_t *)out)[base + j] = oracle_e4m3_from_f64(y[j] / s);
+        } else {
+            double amax = 0.0;
+            for (int32_t j = 0; j < d; ++j)
+                amax = fmax(amax, fabs(y[j]));
+            double s = oracle_i8_row_scale(amax);
+            scale[r] = (float)s;
+            for (int32_t j = 0; j < d; ++j)
+                ((int8_t *)out)[base + j] = oracle_i8_from_f64(y[j] / s);
         }
     }
     free(y);
@@ -222,8 +255,10 @@ static double stored_value(int32_t dtype, const void *base, int64_t idx)
         return (double)((const float *)base)[idx];
     case OR_BF16:
         return oracle_bf16_value(((const uint16_t *)base)[idx]);
-    default:
+    case OR_E4M3:
         return g_e4m3[((const uint8_t *)base)[idx]];
+    default:
+        return (double)((const int8_t *)base)[idx];
     }
 }
 
@@ -232,7 +267,7 @@ static double score_one(const double *q, int32_t c_dtype, const void *corpus,
                         const float *row_scale, int64_t i, int32_t d)
 {
     double s = 0.0;
-    double rs = (c_dtype == OR_E4M3) ? (double)row_scale[i] : 1.0;
+    double rs = (c_dtype == OR_E4M3 || c_dtype == OR_I8) ? (double)row_scale[i] : 1.0;
     for (int32_t j = 0; j < d; ++j)
         s += q[j] * (stored_value(c_dtype, corpus, i * (int64_t)d + j) * rs);
     return s;
@@ -328,8 +363,8 @@ static int check_finite(int32_t dtype, const void *p, int64_t count)
 
 /* Top-k of every query against the whole corpus.
  *   queries:  [b, d] row-major, q_dtype OR_F32 or OR_BF16
- *   corpus:   [n, d] row-major, c_dtype OR_F32, OR_BF16 or OR_E4M3
- *   row_scale:[n] for OR_E4M3, else ignored
+ *   corpus:   [n, d] row-major, c_dtype OR_F32, OR_BF16, OR_E4M3 or OR_I8
+ *   row_scale:[n] for OR_E4M3 and OR_I8, else ignored
  *   exclude:  NULL or uint32[ceil(n/32)], bit (i & 31) of word (i >> 5) excludes id i
  *   out_s:    [b, k] fp64 scores, out_id: [b, k] int32 ids
  */
@@ -342,12 +377,13 @@ int oracle_topk(int32_t q_dtype, const void *queries, int32_t b, int32_t c_dtype
         return OR_BAD_ARG;
     if (q_dtype != OR_F32 && q_dtype != OR_BF16)
         return OR_BAD_ARG;
-    if (c_dtype < OR_F32 || c_dtype > OR_E4M3 || (c_dtype == OR_E4M3 && !row_scale))
+    if (c_dtype < OR_F32 || c_dtype > OR_I8 ||
+        ((c_dtype == OR_E4M3 || c_dtype == OR_I8) && !row_scale))
         return OR_BAD_ARG;
     if (!check_finite(q_dtype, queries, (int64_t)b * d) ||
         !check_finite(c_dtype, corpus, n * (int64_t)d))
         return OR_NONFINITE;
-    if (c_dtype == OR_E4M3)
+    if (c_dtype == OR_E4M3 || c_dtype == OR_I8)
         for (int64_t i = 0; i < n; ++i)
             if (!isfinite(row_scale[i]))
                 return OR_NONFINITE;

@@ -91,6 +91,29 @@ def test_e4m3_row_scale_rule():
         assert np.log2(s) == np.round(np.log2(s))
 
 
+def test_i8_encode_matches_torch_round_and_clip():
+    # nearest integer with ties to even (torch.round), clipped to the symmetric range
+    rng = np.random.default_rng(21)
+    v = np.concatenate([rng.uniform(-140, 140, 5000), np.arange(-130, 131) + 0.5,
+                        np.arange(-130, 131).astype(np.float64)])
+    ref = torch.clamp(torch.round(torch.from_numpy(v)), -127, 127).to(torch.int8).numpy()
+    mine = np.array([oracle.i8_from(x) for x in v], np.int8)
+    assert np.array_equal(ref, mine)
+    assert oracle.i8_from(2.5) == 2 and oracle.i8_from(3.5) == 4 and oracle.i8_from(-2.5) == -2
+    assert oracle.i8_from(127.5) == 127 and oracle.i8_from(-1e9) == -127
+
+
+def test_i8_row_scale_rule():
+    assert oracle.i8_row_scale(127.0) == 1.0
+    assert oracle.i8_row_scale(0.0) == float(np.float32(1e-12))
+    rng = np.random.default_rng(22)
+    for a in rng.uniform(1e-3, 1.0, 300):
+        s = oracle.i8_row_scale(a)
+        assert s == float(np.float32(a / 127))
+        # the largest element maps to +-127 (up to the float rounding of the scale)
+        assert oracle.i8_from(a / s) == 127
+
+
 # ------------------------------------------------------------- normalisation
 def test_normalize_closed_forms():
     y = oracle.normalize(np.array([[3, 4], [0, 0], [1e-7, 1e-7]], np.float32))
@@ -108,7 +131,8 @@ def test_normalize_matches_numpy_norm():
     assert np.allclose(y, ref, rtol=1e-14, atol=0)
 
 
-@pytest.mark.parametrize("dtype,tol", [("f32", 1e-6), ("bf16", 2 ** -7), ("fp8", 2 ** -3)])
+@pytest.mark.parametrize("dtype,tol", [("f32", 1e-6), ("bf16", 2 ** -7), ("fp8", 2 ** -3),
+                                       ("int8", 2 ** -5)])
 def test_prepare_unit_norm_and_elementwise(dtype, tol):
     x = np.random.default_rng(5).standard_normal((300, 64)).astype(np.float32)
     codes, scale = oracle.prepare(x, dtype)
@@ -119,6 +143,11 @@ def test_prepare_unit_norm_and_elementwise(dtype, tol):
         assert np.allclose(v, y, rtol=2 ** -24, atol=0)
     elif dtype == "bf16":
         assert np.all(np.abs(v - y) <= np.abs(y) * 2 ** -8 + 2.0 ** -134)
+    elif dtype == "int8":
+        # half a code step of the row's scale; the largest element of every row is +-127
+        assert np.all(np.abs(v - y) <= scale[:, None].astype(np.float64) * (0.5 + 1e-6))
+        assert np.all(np.abs(codes.astype(np.int32)).max(axis=1) == 127)
+        assert np.all(np.abs(codes.astype(np.int32)) <= 127)
     else:
         step = np.maximum(np.abs(y / scale[:, None]), 2.0 ** -6)
         ulp = 2.0 ** (np.floor(np.log2(step)) - 3)
@@ -142,7 +171,7 @@ def _fraction_topk(qv, cv, k, excluded=()):
 
 
 @pytest.mark.parametrize("c_dtype,q_dtype", [("f32", "f32"), ("bf16", "bf16"), ("fp8", "bf16"),
-                                             ("bf16", "f32")])
+                                             ("bf16", "f32"), ("int8", "bf16"), ("int8", "f32")])
 @pytest.mark.parametrize("with_exclusion", [False, True])
 def test_topk_matches_exact_rational_bruteforce(c_dtype, q_dtype, with_exclusion):
     rng = np.random.default_rng(6)
