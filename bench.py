@@ -26,7 +26,7 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_inner_product_amd", "csrc", f)
                   for f in ("score.h", "score_api.h", "score_inst.hip", "common.h")]
-PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "int8": 5033.2, "f32": 157.3}
 
 
 def log(msg):
@@ -200,10 +200,10 @@ def main():
 
     ms_per_step = wall / args.steps * 1e3
     scores_per_s = w.b * w.n / (ms_per_step / 1e3)
-    E = {"f32": 4, "bf16": 2, "fp8": 1}[w.corpus_dtype]
+    E = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[w.corpus_dtype]
     # Algorithmic bytes of the main score pass: every packed corpus row once (plus its
-    # fp8 scale), the exclusion bitmap and the queries.
-    alg_bytes = w.n * w.d * E + (4 * w.n if w.corpus_dtype == "fp8" else 0)
+    # fp8 or int8 scale), the exclusion bitmap and the queries.
+    alg_bytes = w.n * w.d * E + (4 * w.n if w.corpus_dtype in ("fp8", "int8") else 0)
     alg_bytes += (w.n / 8 if w.exclude_frac > 0 else 0) + w.b * w.d * E
     flops = 2.0 * w.b * w.n * w.d
     main_avg = float(np.mean(main_ms)) / 1e3

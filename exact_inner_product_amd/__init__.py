@@ -17,8 +17,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmips.so")
 
-F32, BF16, FP8_E4M3 = 0, 1, 2
-DTYPE_CODES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+F32, BF16, FP8_E4M3, INT8 = 0, 1, 2, 3
+DTYPE_CODES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "int8": INT8}
+SCALED = ("fp8", "int8")  # packed with one float scale per row
 K_MAX = 1024
 
 EXPORTS = (
@@ -109,7 +110,7 @@ def l2_normalize(x: torch.Tensor, out_dtype: str = "f32") -> torch.Tensor:
 class Corpus:
     """A packed, normalised index in the fragment-tiled layout of include/mips.h."""
     packed: torch.Tensor               # uint8 [mips_corpus_bytes]
-    row_scale: Optional[torch.Tensor]  # float32 [mips_scale_count] (fp8 only)
+    row_scale: Optional[torch.Tensor]  # float32 [mips_scale_count] (fp8 and int8)
     n: int
     d: int
     dtype: str
@@ -129,7 +130,7 @@ def empty_corpus(n: int, d: int, dtype: str, device="cuda") -> Corpus:
         raise MipsError(2, "mips_corpus_bytes")
     packed = torch.empty(nbytes, dtype=torch.uint8, device=device)
     scale = None
-    if dtype == "fp8":
+    if dtype in SCALED:
         scale = torch.empty(int(lib().mips_scale_count(n)), dtype=torch.float32, device=device)
     return Corpus(packed, scale, n, d, dtype)
 

@@ -23,7 +23,8 @@ SOURCES = ["api.hip", "normalize.hip", "topk.hip"]
 # (dtype macro, width) pairs of the score pass; must match corpus_d_supported in host.h
 SCORE_UNITS = ([("MIPS_F32", d) for d in (16, 32, 64, 128)] +
                [("MIPS_BF16", d) for d in (16, 32, 64, 128, 256)] +
-               [("MIPS_FP8_E4M3", d) for d in (64, 128, 256)])
+               [("MIPS_FP8_E4M3", d) for d in (64, 128, 256)] +
+               [("MIPS_INT8", d) for d in (32, 64, 128, 256)])
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

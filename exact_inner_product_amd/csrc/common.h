@@ -9,6 +9,8 @@
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 namespace mips {
@@ -33,6 +35,7 @@ __host__ __device__ inline int slot_dim(int dtype, int c, int s, int t) {
   const int h = s >> 5;
   if (dtype == MIPS_F32) return 8 * c + 2 * t + h;
   if (dtype == MIPS_BF16) return 16 * c + 8 * h + t;
+  if (dtype == MIPS_INT8) return 32 * c + 16 * h + t;
   return 64 * (c >> 1) + 32 * h + 16 * (c & 1) + t;
 }
 
@@ -48,6 +51,10 @@ __host__ __device__ inline int64_t packed_offset(int dtype, int d, int64_t row, 
     c = dim >> 4;
     h = (dim >> 3) & 1;
     t = dim & 7;
+  } else if (dtype == MIPS_INT8) {
+    c = dim >> 5;
+    h = (dim >> 4) & 1;
+    t = dim & 15;
   } else {
     const int w = dim & 63;
     c = 2 * (dim >> 6) + ((w >> 4) & 1);
@@ -128,6 +135,14 @@ __device__ __forceinline__ int e4m3_scale_exp(float amax) {
   const int e = (int)(u >> 23) - 126;                 // amax = f * 2^e, f in [0.5, 1)
   const uint32_t frac = u & 0x7FFFFFu;                // f = (1 + frac/2^23) / 2
   return (frac <= 0x600000u) ? e - 9 : e - 8;         // f <= 0.875 <=> frac <= 0.75 * 2^23
+}
+
+// int8 codes with one float scale per row: scale = max(amax / 127, 1e-12), code =
+// nearest integer to v / scale (ties to even), clipped to [-127, 127].
+__device__ __forceinline__ float i8_scale(float amax) { return fmaxf(amax / 127.0f, 1e-12f); }
+__device__ __forceinline__ uint32_t f32_to_i8(float v) {
+  const float r = fminf(fmaxf(rintf(v), -127.0f), 127.0f);
+  return (uint32_t)(int)r & 0xFFu;
 }
 
 __device__ __forceinline__ float exp2_int(int t) {  // 2^t for |t| <= 126

@@ -27,6 +27,7 @@ inline bool corpus_d_supported(int dtype, int d) {
   if (dtype == MIPS_FP8_E4M3) return d == 64 || d == 128 || d == 256;
   if (dtype == MIPS_F32) return d == 16 || d == 32 || d == 64 || d == 128;
   if (dtype == MIPS_BF16) return d == 16 || d == 32 || d == 64 || d == 128 || d == 256;
+  if (dtype == MIPS_INT8) return d == 32 || d == 64 || d == 128 || d == 256;
   return false;
 }
 

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void l2_normalize_kernel(const float* __restri
 }
 
 // One workgroup (4 waves) per packed 32-row block. Phase 1: each wave normalises 8
-// rows' norms (and, for E4M3, the row's power-of-two scale). Phase 2: the block's
+// rows' norms (and, for E4M3, the row's power-of-two scale; for int8, max|y| / 127). Phase 2: the block's
 // 1 KiB chunks are written, one 16-byte slot per lane, so stores are fully coalesced.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void prepare_kernel(const float* __restrict__ src, int64_t rows,
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(const float* __restrict__ 
       for (int j = lane; j < D; j += kWave) ss = fmaf(x[j], x[j], ss);
       ss = wave_sum(ss);
       nrm = sqrtf(fmaxf(ss, kNormEps));
-      if (DT == MIPS_FP8_E4M3) {
+      if (DT == MIPS_FP8_E4M3 || DT == MIPS_INT8) {
         float m = 0.0f;
         for (int j = lane; j < D; j += kWave) m = fmaxf(m, fabsf(x[j] / nrm));
         amax = wave_max(m);
@@ -81,6 +81,10 @@ __global__ __launch_bounds__(256) void prepare_kernel(const float* __restrict__ 
         t = t < -126 ? -126 : t;
         s_scale_inv[r] = exp2_int(-t);
         row_scale[(block0 + blk) * kFrag + r] = exp2_int(t);
+      } else if (DT == MIPS_INT8) {
+        const float sc = i8_scale(amax);
+        s_scale_inv[r] = sc;  // int8 divides by the scale itself
+        row_scale[(block0 + blk) * kFrag + r] = sc;
       }
     }
   }
@@ -107,6 +111,13 @@ __global__ __launch_bounds__(256) void prepare_kernel(const float* __restrict__ 
         const float y1 = live ? x[slot_dim(DT, c, lane, t + 1)] / nrm : 0.0f;
         v[t >> 1] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
       }
+    } else if (DT == MIPS_INT8) {
+      const float sc = s_scale_inv[r];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const float y = live ? (x[slot_dim(DT, c, lane, t)] / nrm) / sc : 0.0f;
+        v[t >> 2] |= f32_to_i8(y) << (8 * (t & 3));
+      }
     } else {
       const float sinv = s_scale_inv[r];
 #pragma unroll
@@ -132,7 +143,7 @@ template <int DT>
 static int dispatch_prepare_d(const float* src, int64_t rows, int64_t row_offset, int d,
                               void* dst, float* row_scale, hipStream_t s) {
   switch (d) {
-    case 16: if constexpr (DT != MIPS_FP8_E4M3) return launch_prepare<DT, 16>(src, rows, row_offset, dst, row_scale, s); break;
+    case 16: if constexpr (DT != MIPS_FP8_E4M3 && DT != MIPS_INT8) return launch_prepare<DT, 16>(src, rows, row_offset, dst, row_scale, s); break;
     case 32: if constexpr (DT != MIPS_FP8_E4M3) return launch_prepare<DT, 32>(src, rows, row_offset, dst, row_scale, s); break;
     case 64: return launch_prepare<DT, 64>(src, rows, row_offset, dst, row_scale, s);
     case 128: return launch_prepare<DT, 128>(src, rows, row_offset, dst, row_scale, s);
@@ -175,10 +186,10 @@ int mips_prepare_corpus(const float* src, int64_t rows, int64_t row_offset, int3
                         int32_t dtype, void* dst, float* row_scale, void* stream) {
   if (!src || !dst || rows < 1 || row_offset < 0 || (row_offset % 32) != 0)
     return MIPS_ERR_INVALID_ARG;
-  if (dtype != MIPS_F32 && dtype != MIPS_BF16 && dtype != MIPS_FP8_E4M3)
+  if (dtype != MIPS_F32 && dtype != MIPS_BF16 && dtype != MIPS_FP8_E4M3 && dtype != MIPS_INT8)
     return MIPS_ERR_UNSUPPORTED;
   if (!mips::corpus_d_supported(dtype, d)) return MIPS_ERR_UNSUPPORTED;
-  if (dtype == MIPS_FP8_E4M3 && !row_scale) return MIPS_ERR_INVALID_ARG;
+  if ((dtype == MIPS_FP8_E4M3 || dtype == MIPS_INT8) && !row_scale) return MIPS_ERR_INVALID_ARG;
   if (!mips::aligned(src, 4) || !mips::aligned(dst, 16) ||
       (row_scale && !mips::aligned(row_scale, 4)))
     return MIPS_ERR_INVALID_ARG;
@@ -189,6 +200,8 @@ int mips_prepare_corpus(const float* src, int64_t rows, int64_t row_offset, int3
       return mips::dispatch_prepare_d<MIPS_F32>(src, rows, row_offset, d, dst, row_scale, s);
     case MIPS_BF16:
       return mips::dispatch_prepare_d<MIPS_BF16>(src, rows, row_offset, d, dst, row_scale, s);
+    case MIPS_INT8:
+      return mips::dispatch_prepare_d<MIPS_INT8>(src, rows, row_offset, d, dst, row_scale, s);
     default:
       return mips::dispatch_prepare_d<MIPS_FP8_E4M3>(src, rows, row_offset, d, dst, row_scale, s);
   }

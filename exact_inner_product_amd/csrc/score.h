@@ -25,6 +25,12 @@ __device__ __forceinline__ void mfma_step(f32x16_t& acc, const u32x4_t* a, const
       bv[4 + j] = (int)b[2 * s + 1][j];
     }
     acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, sa, 0, sb);
+  } else if constexpr (CT == MIPS_INT8) {
+    // int32 accumulation; the accumulator registers hold the integer bits
+    acc = __builtin_bit_cast(
+        f32x16_t, __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, a[s]),
+                                                        __builtin_bit_cast(i32x4_t, b[s]),
+                                                        __builtin_bit_cast(i32x16_t, acc), 0, 0, 0));
   } else {
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[s >> 2][s & 3]),
                                                __uint_as_float(b[s >> 2][s & 3]), acc, 0, 0, 0);
@@ -59,7 +65,10 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
   constexpr int E = elem_bytes(CT);
   constexpr int NCH = chunks_per_block(CT, D);
   constexpr int RM = stage_frags(CT, D);
-  constexpr int KSTEPS = (CT == MIPS_F32) ? D / 2 : (CT == MIPS_BF16 ? D / 16 : D / 64);
+  constexpr int KSTEPS = (CT == MIPS_F32) ? D / 2
+                        : (CT == MIPS_BF16 ? D / 16 : (CT == MIPS_INT8 ? D / 32 : D / 64));
+  // int8: per stage block, the scales of the 16 rows a lane's accumulators cover
+  constexpr int SCN = CT == MIPS_INT8 ? 16 : 1;
   constexpr int64_t BLK = block_bytes(CT, D);
   constexpr int QB = kFrag * NQF;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -88,7 +97,7 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
   int* qid_lds = (int*)(lds + (size_t)QB * D * E);
   uint32_t* seg_lds = (uint32_t*)(qid_lds + QB);  // survivors per query column (this segment)
   float* thr_lds = (float*)(seg_lds + QB);        // threshold per query column
-  int* sexp_lds = (int*)(thr_lds + QB);           // fp8 query scale exponent per column
+  int* sexp_lds = (int*)(thr_lds + QB);           // fp8 exponent / int8 scale per column
   uint64_t* st_key = (uint64_t*)(sexp_lds + QB) + wave * kStageCap;
   uint16_t* st_q = (uint16_t*)((uint64_t*)(sexp_lds + QB) + kScoreWaves * kStageCap) + wave * kStageCap;
 
@@ -169,12 +178,19 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
         if (k != 0u) T = key_threshold(k);
       }
       thr_lds[i] = T;
-      sexp_lds[i] = (CT == MIPS_FP8_E4M3 && qg >= 0) ? A.qexp[qg] : 127;
+      int e = CT == MIPS_INT8 ? __float_as_int(1.0f) : 127;
+      if ((CT == MIPS_FP8_E4M3 || CT == MIPS_INT8) && qg >= 0) e = A.qexp[qg];
+      sexp_lds[i] = e;
     }
     __syncthreads();
     auto Tq = [&](int qf) __attribute__((always_inline)) { return thr_lds[qf * kFrag + (lane & 31)]; };
     auto sbq = [&](int qf) __attribute__((always_inline)) {
       return CT == MIPS_FP8_E4M3 ? sexp_lds[qf * kFrag + (lane & 31)] : 127;
+    };
+    // int8: a score is (int32 dot product * row scale) * query scale, in that order. The
+    // query scale is positive, so it can be applied after a max (rounding is monotone).
+    auto qscale = [&](int qf) __attribute__((always_inline)) {
+      return CT == MIPS_INT8 ? __int_as_float(sexp_lds[qf * kFrag + (lane & 31)]) : 1.0f;
     };
     auto qgq = [&](int qf) __attribute__((always_inline)) { return qid_lds[qf * kFrag + (lane & 31)]; };
 
@@ -208,7 +224,8 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
     // A stage's loads are unconditional: blocks past the end of the pass read the last
     // block again and are masked out, so the compiler's wait counts stay exact. Lane r < RM
     // also loads the exclusion word of block r, with the rows past n set.
-    auto load_stage = [&](u32x4_t (&a)[RM][NCH], int (&sa)[RM], uint32_t& xwv, int64_t j0) __attribute__((always_inline)) {
+    auto load_stage = [&](u32x4_t (&a)[RM][NCH], int (&sa)[RM], float (&sc)[RM][SCN], uint32_t& xwv,
+                          int64_t j0) __attribute__((always_inline)) {
 #pragma unroll
       for (int r = 0; r < RM; ++r) {
         const int64_t j = min<int64_t>(j0 + r, A.nfrag - 1);
@@ -223,6 +240,17 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
         sa[r] = 127;
         if (CT == MIPS_FP8_E4M3)
           sa[r] = (int)((__float_as_uint(A.row_scale[fr * kFrag + (lane & 31)]) >> 23) & 0xFFu);
+        if constexpr (CT == MIPS_INT8) {
+          // rows 8q + 4 (lane >> 5) + (0..3) for q = 0..3: accumulator registers 4q..4q+3
+          const __amdgpu_buffer_rsrc_t rsc = block_rsrc(A.row_scale + fr * kFrag, kFrag * 4);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x4_t v = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsc, (lane >> 5) * 16, q * 32, 0));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc[r][4 * q + e] = __uint_as_float(v[e]);
+          }
+        }
       }
       const int r = lane < RM ? lane : RM - 1;
       const bool live = j0 + r < A.nfrag;
@@ -255,9 +283,9 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
 #pragma unroll
         for (int g = 0; g < RM; ++g) mfma_step<CT>(acc[g], a[g], bq, sa[g], sb, s);
         if (next >= 0) {
-          // chunks whose last use was step s: bf16 chunk s; fp8 chunks 2s, 2s+1; f32 chunk
-          // s/4 after its fourth step
-          if constexpr (CT == MIPS_BF16) {
+          // chunks whose last use was step s: bf16 and int8 chunk s; fp8 chunks 2s, 2s+1;
+          // f32 chunk s/4 after its fourth step
+          if constexpr (CT == MIPS_BF16 || CT == MIPS_INT8) {
             bq[s] = bsrc[s * (kChunkBytes / 16)];
           } else if constexpr (CT == MIPS_FP8_E4M3) {
             bq[2 * s] = bsrc[2 * s * (kChunkBytes / 16)];
@@ -268,29 +296,40 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
         }
       }
     };
-    // Query operand held in registers for the whole q-block when it fits (up to 256
-    // registers: 256 queries at 256 bytes per row); otherwise streamed from LDS.
-    constexpr bool BREG = false;
-    u32x4_t breg[BREG ? NQF : 1][NCH];
-    if constexpr (BREG) {
+    // A lane's 16 values of block g before the query scale: the accumulators, or for int8
+    // the integer dot products times their rows' scales.
+    auto vals = [&](const f32x16_t& acc, const float (&sc)[SCN], float (&x)[16]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int qf = 0; qf < NQF; ++qf) load_b(breg[qf], qf);
-    }
+      for (int i = 0; i < 16; ++i) {
+        if constexpr (CT == MIPS_INT8)
+          x[i] = (float)__float_as_int(acc[i]) * sc[i];  // (a bit cast of a vector element
+                                                        // lvalue would read element 0)
+        else
+          x[i] = acc[i];
+      }
+    };
+    auto post = [&](float x, float sq) __attribute__((always_inline)) {
+      return CT == MIPS_INT8 ? x * sq : x;
+    };
 
     // Main epilogue of one query fragment: one max per block (16 scores per lane) and one
     // ballot, branch-free so it interleaves with the next fragment's MFMAs. A block that
     // clears the threshold is resolved on the scalar unit (below).
-    auto epi_main = [&](const f32x16_t (&acc)[RM], uint32_t xwv, int64_t j0, int qf) __attribute__((always_inline)) {
+    auto epi_main = [&](const f32x16_t (&acc)[RM], const float (&sc)[RM][SCN], uint32_t xwv,
+                        int64_t j0, int qf) __attribute__((always_inline)) {
       const float T = Tq(qf);
+      const float sq = qscale(qf);
       float m[RM];
       bool any = false;
 #pragma unroll
       for (int g = 0; g < RM; ++g) {
-        float x = acc[g][0];
+        float xv[16];
+        vals(acc[g], sc[g], xv);
+        float x = xv[0];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) x = fmaxf(x, acc[g][i]);
-        m[g] = x;
-        any = any || (x >= T);
+        for (int i = 1; i < 16; ++i) x = fmaxf(x, xv[i]);
+        m[g] = post(x, sq);
+        any = any || (m[g] >= T);
       }
       if (__builtin_expect(__ballot(any) != 0ull, 0)) {
 #pragma unroll
@@ -298,11 +337,15 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
           if (__ballot(m[g] >= T) == 0ull) continue;
           const uint32_t w = __builtin_amdgcn_readlane(xwv, g);
           const uint32_t idb = (uint32_t)((j0 + g) * kFrag);
+          float y[16];
+          vals(acc[g], sc[g], y);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) y[i] = post(y[i], sq);
           // per lane, a 16-bit mask of its values that pass: bit i <=> value i >= T and
           // its row (8 (i >> 2) + 4 (lane >> 5) + (i & 3)) is neither excluded nor padding
           uint32_t pm = 0u;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) pm |= (acc[g][i] >= T ? 1u : 0u) << i;
+          for (int i = 0; i < 16; ++i) pm |= (y[i] >= T ? 1u : 0u) << i;
           const uint32_t wl = w >> (4 * (lane >> 5));
           pm &= ~((wl & 0xFu) | ((wl >> 4) & 0xF0u) | ((wl >> 8) & 0xF00u) | ((wl >> 12) & 0xF000u));
           // walk the passing (lane, value) pairs on the scalar unit: usually one
@@ -315,7 +358,7 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
             while (pl != 0u) {
               const int i = __builtin_ctz(pl);
               pl &= pl - 1u;
-              const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[g][i]), L));
+              const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(y[i]), L));
               const uint32_t id = idb + (uint32_t)(8 * (i >> 2) + 4 * (L >> 5) + (i & 3));
               if (st_n < kStageCap) {
                 if (lane == 0) {
@@ -339,8 +382,10 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
     // written by the two lanes of the query's column (no cross-lane reduction). Slots are
     // laid out del[tile / 16][query][tile % 16][2 RM], so that each query's delegates lie in
     // runs of 16 slots.
-    auto epi_aux = [&](const f32x16_t (&acc)[RM], uint32_t xwv, int64_t j0, int qf) __attribute__((always_inline)) {
+    auto epi_aux = [&](const f32x16_t (&acc)[RM], const float (&sc)[RM][SCN], uint32_t xwv,
+                       int64_t j0, int qf) __attribute__((always_inline)) {
       const int qg = qgq(qf);
+      const float sq = qscale(qf);
       if constexpr (MODE == MODE_DENSE) {
 #pragma unroll
         for (int g = 0; g < RM; ++g) {
@@ -354,12 +399,15 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
           f32x16_t v = acc[g];
           asm volatile("" : "+v"(v));
           if (j < A.nfrag && qg >= 0) {
+            float x[16];
+            vals(v, sc[g], x);
             uint64_t* dst = A.cand + (int64_t)qg * A.nseg * A.capw + j * kFrag;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int row = acc_row(i, lane);
-              dst[row] = ((w >> row) & 1u) ? 0ull
-                                           : composite(score_key(v[i]), (uint32_t)(j * kFrag + row));
+              dst[row] = ((w >> row) & 1u)
+                             ? 0ull
+                             : composite(score_key(post(x[i], sq)), (uint32_t)(j * kFrag + row));
             }
           }
         }
@@ -368,13 +416,15 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
 #pragma unroll
         for (int g = 0; g < RM; ++g) {
           const uint32_t w = __builtin_amdgcn_readlane(xwv, g);
+          float x[16];
+          vals(acc[g], sc[g], x);
           float mx = -INFINITY;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int row = acc_row(i, lane);
-            mx = ((w >> row) & 1u) ? mx : fmaxf(mx, acc[g][i]);
+            mx = ((w >> row) & 1u) ? mx : fmaxf(mx, x[i]);
           }
-          d[g] = (mx == -INFINITY) ? 0u : score_key(mx);
+          d[g] = (mx == -INFINITY) ? 0u : score_key(post(mx, sq));
           asm volatile("" : "+v"(d[g]));  // computed in uniform control flow, as above
         }
         const int qc = qbase + qf * kFrag + (lane & 31);
@@ -390,29 +440,22 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
     // One stage against every query fragment, software-pipelined: the MFMAs of fragment
     // qf+1 are issued before the epilogue of fragment qf, so the epilogue (and its rare
     // path) runs while the matrix pipe works on the next fragment.
-    auto compute_stage = [&](const u32x4_t (&a)[RM][NCH], const int (&sa)[RM], uint32_t xwv,
+    auto compute_stage = [&](const u32x4_t (&a)[RM][NCH], const int (&sa)[RM],
+                             const float (&sc)[RM][SCN], uint32_t xwv,
                              int64_t j0) __attribute__((always_inline)) {
       f32x16_t acc[2][RM];
-      u32x4_t bq[BREG ? 1 : NCH];
-      if constexpr (BREG) {
-        mfmas(acc[0], a, sa, breg[0], sbq(0), -1);
-      } else {
-        load_b(bq, 0);
-        mfmas(acc[0], a, sa, bq, sbq(0), NQF > 1 ? 1 : -1);
-      }
+      u32x4_t bq[NCH];
+      load_b(bq, 0);
+      mfmas(acc[0], a, sa, bq, sbq(0), NQF > 1 ? 1 : -1);
       static_for<NQF>([&](auto qfc) __attribute__((always_inline)) {
         constexpr int qf = decltype(qfc)::value;
         constexpr int cur = qf & 1;
-        if constexpr (qf + 1 < NQF) {
-          if constexpr (BREG)
-            mfmas(acc[cur ^ 1], a, sa, breg[qf + 1], sbq(qf + 1), -1);
-          else
-            mfmas(acc[cur ^ 1], a, sa, bq, sbq(qf + 1), qf + 2 < NQF ? qf + 2 : -1);
-        }
+        if constexpr (qf + 1 < NQF)
+          mfmas(acc[cur ^ 1], a, sa, bq, sbq(qf + 1), qf + 2 < NQF ? qf + 2 : -1);
         if constexpr (MODE == MODE_MAIN) {
-          epi_main(acc[cur], xwv, j0, qf);
+          epi_main(acc[cur], sc, xwv, j0, qf);
         } else {
-          epi_aux(acc[cur], xwv, j0, qf);
+          epi_aux(acc[cur], sc, xwv, j0, qf);
           // the auxiliary epilogues have no branch that would bound the scheduler's region;
           // without this fence it interleaves whole stages and runs out of registers
           __builtin_amdgcn_sched_barrier(0);
@@ -424,36 +467,32 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
     // tiles): while stage i is multiplied against every query, stages i+1 .. i+NS-1 are in
     // flight. With one wave per SIMD, the bytes in flight per wave set the HBM bandwidth
     // (Little's law at several microseconds of loaded latency), hence NS - 1 = 2 stages.
-    constexpr int NS = pipe_stages(CT, D);
+    constexpr int NS = kPipeStages;
     u32x4_t a[NS][RM][NCH];
     int sa[NS][RM];
+    float sc[NS][RM][SCN];
     uint32_t xw[NS];
     int64_t t = t_begin + wave;
     auto tile = [&](int64_t tt) __attribute__((always_inline)) { return tt < t_end ? tt * RM : A.nfrag; };
     if (t < t_end) {
       static_for<NS - 1>([&](auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
-        load_stage(a[u], sa[u], xw[u], tile(t + u * kScoreWaves));
+        load_stage(a[u], sa[u], sc[u], xw[u], tile(t + u * kScoreWaves));
       });
       // one pipeline step; returns true after the wave's last stage. The steps are chained
       // with || so that the exits are plain branches and every wait count stays exact.
       auto step = [&](auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
         constexpr int ld = (u + NS - 1) % NS;
-        load_stage(a[ld], sa[ld], xw[ld], tile(t + (u + NS - 1) * kScoreWaves));
+        load_stage(a[ld], sa[ld], sc[ld], xw[ld], tile(t + (u + NS - 1) * kScoreWaves));
         if (MODE == MODE_MAIN && st_n > kStageCap - kStageBurst) flush();
-        compute_stage(a[u], sa[u], xw[u], (t + u * kScoreWaves) * RM);
+        compute_stage(a[u], sa[u], sc[u], xw[u], (t + u * kScoreWaves) * RM);
         return t + (u + 1) * kScoreWaves >= t_end;
       };
-      static_assert(NS == 2 || NS == 3, "the step chain below is written for two or three stages");
-      if constexpr (NS == 3) {
-        while (!(step(std::integral_constant<int, 0>{}) || step(std::integral_constant<int, 1>{}) ||
-                 step(std::integral_constant<int, 2>{})))
-          t += NS * kScoreWaves;
-      } else {
-        while (!(step(std::integral_constant<int, 0>{}) || step(std::integral_constant<int, 1>{})))
-          t += NS * kScoreWaves;
-      }
+      static_assert(NS == 3, "the step chain below is written for three stages");
+      while (!(step(std::integral_constant<int, 0>{}) || step(std::integral_constant<int, 1>{}) ||
+               step(std::integral_constant<int, 2>{})))
+        t += NS * kScoreWaves;
     }
     if (MODE == MODE_MAIN) {
       if (st_n > 0) flush();

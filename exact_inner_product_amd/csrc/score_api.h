@@ -18,27 +18,22 @@ constexpr int kLdsLimit = 160 * 1024;
 constexpr int kMaxSample = 8192;    // sampled 32-row blocks
 
 constexpr int kMaxSegments = 256;   // list segments per query (corpus slices of a pass)
-#ifndef MIPS_STAGE_BYTES
-#define MIPS_STAGE_BYTES 16384
-#endif
-#ifndef MIPS_PIPE_STAGES
-#define MIPS_PIPE_STAGES 3
-#endif
-constexpr int kStageBytes = MIPS_STAGE_BYTES;    // corpus bytes per wave and pipeline stage
-constexpr int kPipeStagesCfg = MIPS_PIPE_STAGES; // corpus stages in flight + in use per wave
+constexpr int kStageBytes = 16384;  // corpus bytes per wave and pipeline stage
+constexpr int kPipeStages = 3;      // corpus stages per wave: one in use, two in flight
 constexpr int kSelCache = 6144;     // candidates the final select caches in LDS
 
 // Passes of the score kernel: the main filter pass (also the rescue pass), the sample pass
 // (delegates of a strided block sample) and the dense pass (every score, small corpora).
 enum { MODE_MAIN = 0, MODE_SAMPLE = 1, MODE_DENSE = 2 };
 
-// Corpus blocks per pipeline stage: 16 KiB of corpus per wave and stage (at most 4 blocks).
+// Corpus blocks per pipeline stage: 16 KiB of corpus per wave and stage (at most 4
+// blocks). An int8 stage also holds 16 row scales per lane and block, so it is capped at
+// 8 KiB and 2 blocks.
 __host__ __device__ constexpr int stage_frags(int ct, int d) {
-  const int r = kStageBytes / (kFrag * d * elem_bytes(ct));
-  return r < 1 ? 1 : (r > 4 ? 4 : r);
+  const int cap = ct == MIPS_INT8 ? 2 : 4;
+  const int r = (ct == MIPS_INT8 ? kStageBytes / 2 : kStageBytes) / (kFrag * d * elem_bytes(ct));
+  return r < 1 ? 1 : (r > cap ? cap : r);
 }
-// Corpus stages held in registers per wave (the one being multiplied and the prefetched).
-__host__ __device__ constexpr int pipe_stages(int ct, int d) { return kPipeStagesCfg; }
 // LDS of a score workgroup holding 32 * nqf queries.
 __host__ __device__ constexpr int score_lds_bytes(int ct, int d, int nqf) {
   return kFrag * nqf * (d * elem_bytes(ct) + 16) + kStageLds;

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict
     if (QT == MIPS_F32) return ((const float*)queries)[(int64_t)q * D + dim];
     return bf16_to_f32(((const uint16_t*)queries)[(int64_t)q * D + dim]);
   };
-  float sinv = 1.0f;
+  float sinv = 1.0f, sq = 1.0f;
   if (CT == MIPS_FP8_E4M3) {
     float m = 0.0f;
     for (int j = 0; j < D; ++j) m = fmaxf(m, fabsf(val(j)));
@@ -69,6 +69,11 @@ __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict
     t = t < -126 ? -126 : (t > 127 ? 127 : t);
     sinv = exp2_int(-t);
     if (c == 0 && lane < 32) qexp[q] = t + 127;
+  } else if (CT == MIPS_INT8) {
+    float m = 0.0f;
+    for (int j = 0; j < D; ++j) m = fmaxf(m, fabsf(val(j)));
+    sq = i8_scale(m);
+    if (c == 0 && lane < 32) qexp[q] = __float_as_int(sq);
   }
   u32x4_t v = {0u, 0u, 0u, 0u};
   if (CT == MIPS_F32) {
@@ -77,6 +82,9 @@ __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict
     for (int t = 0; t < 8; t += 2)
       v[t >> 1] = (uint32_t)f32_to_bf16(val(slot_dim(CT, c, lane, t))) |
                   ((uint32_t)f32_to_bf16(val(slot_dim(CT, c, lane, t + 1))) << 16);
+  } else if (CT == MIPS_INT8) {
+    for (int t = 0; t < 16; ++t)
+      v[t >> 2] |= f32_to_i8(val(slot_dim(CT, c, lane, t)) / sq) << (8 * (t & 3));
   } else {
     for (int t = 0; t < 16; ++t)
       v[t >> 2] |= (uint32_t)f32_to_e4m3(val(slot_dim(CT, c, lane, t)) * sinv) << (8 * (t & 3));
@@ -230,6 +238,8 @@ __device__ void fallback_scan(const SelectArgs& A, int q, uint64_t thr, uint64_t
       v = *(const float*)(A.qtile + off);
     else if (CT == MIPS_BF16)
       v = bf16_to_f32(*(const uint16_t*)(A.qtile + off));
+    else if (CT == MIPS_INT8)
+      v = (float)(int8_t)A.qtile[off];  // the query scale is applied to the sum
     else
       v = e4m3_to_f32(A.qtile[off]) * exp2_int(A.qexp[q] - 127);
     qv[j] = v;
@@ -260,11 +270,16 @@ __device__ void fallback_scan(const SelectArgs& A, int q, uint64_t thr, uint64_t
           c = *(const float*)(A.corpus + off);
         else if (CT == MIPS_BF16)
           c = bf16_to_f32(*(const uint16_t*)(A.corpus + off));
+        else if (CT == MIPS_INT8)
+          c = (float)(int8_t)A.corpus[off];
         else
           c = e4m3_to_f32(A.corpus[off]);
         s = fmaf(qv[j], c, s);
       }
       if (CT == MIPS_FP8_E4M3) s *= A.row_scale[i];
+      // int8: the sum of code products is an integer below 2^24, exact in fp32 as in the
+      // MFMA path; then the row scale and the query scale, in the score pass's order
+      if (CT == MIPS_INT8) s = (s * A.row_scale[i]) * __int_as_float(A.qexp[q]);
       const uint64_t key = composite(score_key(s), (uint32_t)i);
       if (key >= thr) buf[atomicAdd(nbuf_p, 1u)] = key;
     }
@@ -641,7 +656,7 @@ static int dispatch_d(const Plan& p, const void* queries, const void* corpus,
                       int32_t* out_ids, uint8_t* ws, hipStream_t s) {
 #define MIPS_RUN(DD) return run_topk<CT, DD>(p, queries, corpus, row_scale, exclude, out_scores, out_ids, ws, s)
   switch (p.d) {
-    case 16: if constexpr (CT != MIPS_FP8_E4M3) { MIPS_RUN(16); } break;
+    case 16: if constexpr (CT != MIPS_FP8_E4M3 && CT != MIPS_INT8) { MIPS_RUN(16); } break;
     case 32: if constexpr (CT != MIPS_FP8_E4M3) { MIPS_RUN(32); } break;
     case 64: MIPS_RUN(64);
     case 128: MIPS_RUN(128);
@@ -653,7 +668,8 @@ static int dispatch_d(const Plan& p, const void* queries, const void* corpus,
 
 static int validate_topk(int32_t qdt, int32_t b, int32_t cdt, int64_t n, int32_t d, int32_t k) {
   if (qdt != MIPS_F32 && qdt != MIPS_BF16) return MIPS_ERR_UNSUPPORTED;
-  if (cdt != MIPS_F32 && cdt != MIPS_BF16 && cdt != MIPS_FP8_E4M3) return MIPS_ERR_UNSUPPORTED;
+  if (cdt != MIPS_F32 && cdt != MIPS_BF16 && cdt != MIPS_FP8_E4M3 && cdt != MIPS_INT8)
+    return MIPS_ERR_UNSUPPORTED;
   if (cdt == MIPS_F32 && qdt != MIPS_F32) return MIPS_ERR_UNSUPPORTED;
   if (b < 1 || n < 1 || n > (int64_t)0x7FFFFFFF - 64 || k < 1) return MIPS_ERR_INVALID_ARG;
   if (k > MIPS_K_MAX) return MIPS_ERR_UNSUPPORTED;
@@ -690,7 +706,8 @@ int mips_topk(const void* queries, int32_t query_dtype, int32_t b, const void* c
   if (!queries || !corpus || !out_scores || !out_ids || !workspace) return MIPS_ERR_INVALID_ARG;
   const int rc0 = mips::validate_topk(query_dtype, b, corpus_dtype, n, d, k);
   if (rc0 != MIPS_OK) return rc0;
-  if (corpus_dtype == MIPS_FP8_E4M3 && !row_scale) return MIPS_ERR_INVALID_ARG;
+  if ((corpus_dtype == MIPS_FP8_E4M3 || corpus_dtype == MIPS_INT8) && !row_scale)
+    return MIPS_ERR_INVALID_ARG;
   if (!mips::aligned(queries, 4) || !mips::aligned(corpus, 16) || !mips::aligned(workspace, 256) ||
       !mips::aligned(out_scores, 4) || !mips::aligned(out_ids, 4) ||
       (exclude && !mips::aligned(exclude, 4)) || (row_scale && !mips::aligned(row_scale, 4)))
@@ -709,6 +726,8 @@ int mips_topk(const void* queries, int32_t query_dtype, int32_t b, const void* c
       return mips::dispatch_d<MIPS_F32>(p, queries, corpus, row_scale, exclude, out_scores, out_ids, ws, s);
     case MIPS_BF16:
       return mips::dispatch_d<MIPS_BF16>(p, queries, corpus, row_scale, exclude, out_scores, out_ids, ws, s);
+    case MIPS_INT8:
+      return mips::dispatch_d<MIPS_INT8>(p, queries, corpus, row_scale, exclude, out_scores, out_ids, ws, s);
     default:
       return mips::dispatch_d<MIPS_FP8_E4M3>(p, queries, corpus, row_scale, exclude, out_scores, out_ids, ws, s);
   }

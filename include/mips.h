@@ -21,7 +21,8 @@
  *  - Inputs must be finite. NaN and infinities are not supported.
  *  - Element types: MIPS_F32 (IEEE binary32), MIPS_BF16 (the upper 16 bits of a
  *    binary32), MIPS_FP8_E4M3 (OCP 8-bit float E4M3: bias 7, 3 mantissa bits, no
- *    infinities, max 448), the last always with one float scale per row.
+ *    infinities, max 448) and MIPS_INT8 (two's complement, -127..127), the last two
+ *    always with one float scale per row.
  */
 #ifndef MIPS_H
 #define MIPS_H
@@ -39,6 +40,7 @@ extern "C" {
 #define MIPS_F32 0
 #define MIPS_BF16 1
 #define MIPS_FP8_E4M3 2
+#define MIPS_INT8 3
 
 #define MIPS_OK 0
 #define MIPS_ERR_INVALID_ARG 1
@@ -58,10 +60,11 @@ extern "C" {
  *   MIPS_F32      (4 per slot):  dim = 8c + 2t + h
  *   MIPS_BF16     (8 per slot):  dim = 16c + 8h + t
  *   MIPS_FP8_E4M3 (16 per slot): dim = 64(c >> 1) + 32h + 16(c & 1) + t
+ *   MIPS_INT8     (16 per slot): dim = 32c + 16h + t
  * Every 16-byte slot is exactly one lane's operand of the gfx950 32x32 MFMA, so the
  * score kernel streams the corpus from HBM with fully coalesced 1 KiB wave loads and
- * no LDS transpose. For MIPS_FP8_E4M3 the per-row scale array has one float per padded
- * row; every scale is a power of two (see mips_prepare_corpus).
+ * no LDS transpose. For MIPS_FP8_E4M3 and MIPS_INT8 the per-row scale array has one
+ * float per padded row (see mips_prepare_corpus); fp8 scales are powers of two.
  */
 
 /* Bytes of a packed corpus of n rows (n >= 1) and width d; -1 if unsupported. */
@@ -96,16 +99,19 @@ MIPS_API int mips_l2_normalize(const float *src, int64_t rows, int32_t d, int32_
  *   rows        >= 1. If rows is not a multiple of 32, this must be the last chunk: the
  *               rest of the last block is written as zero rows (scale 1).
  *   d           16, 32, 64, 128 or 256 (MIPS_F32: up to 128; MIPS_FP8_E4M3: 64, 128,
- *               256).
- *   dtype       MIPS_F32 (rounded to nearest), MIPS_BF16 (nearest even) or
+ *               256; MIPS_INT8: 32 .. 256).
+ *   dtype       MIPS_F32 (rounded to nearest), MIPS_BF16 (nearest even),
  *               MIPS_FP8_E4M3: per row, scale s = the smallest power of two with
  *               max|y| <= 448 s (1 for a zero row) and codes = E4M3(y / s), nearest even,
- *               saturating.
+ *               saturating; or MIPS_INT8: per row, scale s = max(max|y| / 127, 1e-12)
+ *               and codes = y / s rounded to nearest (ties to even), clipped to
+ *               [-127, 127] -- the per-row rule of the quantised scoring branch of
+ *               `RecsysTwoTowerModel.forward` (recsys_two_tower_model.py).
  *   dst         device, packed corpus of at least mips_corpus_bytes(row_offset + rows).
- *   row_scale   device float [mips_scale_count(row_offset + rows)] for MIPS_FP8_E4M3
- *               (entries row_offset.. are written), NULL otherwise.
+ *   row_scale   device float [mips_scale_count(row_offset + rows)] for MIPS_FP8_E4M3 and
+ *               MIPS_INT8 (entries row_offset.. are written), NULL otherwise.
  * Errors: INVALID_ARG (NULL, rows < 1, row_offset < 0 or not a multiple of 32, dst not
- * 16-byte aligned, row_scale missing for fp8), UNSUPPORTED (d or dtype).
+ * 16-byte aligned, row_scale missing for fp8 or int8), UNSUPPORTED (d or dtype).
  */
 MIPS_API int mips_prepare_corpus(const float *src, int64_t rows, int64_t row_offset, int32_t d,
                         int32_t dtype, void *dst, float *row_scale, void *stream);
@@ -140,11 +146,15 @@ MIPS_API size_t mips_topk_workspace_size_for(int32_t b, int64_t n, int32_t d, in
  *   b            >= 1.
  *   corpus       device, packed by mips_prepare_corpus (n rows, width d, corpus_dtype);
  *                16-byte aligned.
- *   row_scale    device, per-row scales for MIPS_FP8_E4M3 (NULL otherwise).
+ *   row_scale    device, per-row scales for MIPS_FP8_E4M3 and MIPS_INT8 (NULL
+ *                otherwise).
  *   corpus_dtype with query_dtype: F32/F32, BF16 with F32 or BF16 queries (queries are
  *                rounded to bf16), FP8_E4M3 with F32 or BF16 queries (each query row is
  *                quantised to E4M3 with its own power-of-two scale, the rule of
- *                mips_prepare_corpus).
+ *                mips_prepare_corpus), INT8 with F32 or BF16 queries (each query row is
+ *                quantised to int8 with its own scale max|q| / 127, as the quantised
+ *                branch of `RecsysTwoTowerModel.forward` does; the int32 dot product of
+ *                the codes is scaled by the row scale, then by the query scale).
  *   n            1 .. 2^31 - 64.  d: as mips_prepare_corpus.
  *   exclude      device or NULL: uint32 [ceil(n/32)]; bit (i & 31) of word (i >> 5) set
  *                means id i is never returned. One bitmap serves the whole batch.
@@ -158,8 +168,8 @@ MIPS_API size_t mips_topk_workspace_size_for(int32_t b, int64_t n, int32_t d, in
  *                mips_topk_workspace_size_for any other capacity); its contents are
  *                undefined between calls. Calls that share a workspace must be ordered on
  *                one stream.
- * Errors: INVALID_ARG (NULL where a buffer is required, b/n/k out of range, fp8 without
- * row_scale, misalignment), UNSUPPORTED (d, k > MIPS_K_MAX, dtype pair), WORKSPACE
+ * Errors: INVALID_ARG (NULL where a buffer is required, b/n/k out of range, fp8 or int8
+ * without row_scale, misalignment), UNSUPPORTED (d, k > MIPS_K_MAX, dtype pair), WORKSPACE
  * (workspace_bytes too small), HIP (a launch failed).
  */
 MIPS_API int mips_topk(const void *queries, int32_t query_dtype, int32_t b, const void *corpus,

@@ -110,7 +110,7 @@ def test_normalize_and_prepare_validation(L):
 def test_untile_inverts_the_documented_layout():
     """The test-side decoder against a hand-placed element, per dtype."""
     import numpy as np
-    for dtype, E in (("f32", 4), ("bf16", 2), ("fp8", 1)):
+    for dtype, E in (("f32", 4), ("bf16", 2), ("fp8", 1), ("int8", 1)):
         d, n = 128, 40
         codes = np.arange(n * d, dtype=np.int64).reshape(n, d)
         buf = np.zeros(2 * 32 * d * E, np.uint8)
@@ -125,6 +125,9 @@ def test_untile_inverts_the_documented_layout():
                 elif dtype == "bf16":
                     c, rem = divmod(dim, 16)
                     h, t = divmod(rem, 8)
+                elif dtype == "int8":
+                    c, rem = divmod(dim, 32)
+                    h, t = divmod(rem, 16)
                 else:
                     j, w = divmod(dim, 64)
                     h, w2 = divmod(w, 32)
@@ -137,4 +140,6 @@ def test_untile_inverts_the_documented_layout():
         want = codes % (1 << (8 * E))
         if dtype == "f32":
             got = got.view(np.uint32)
+        if dtype == "int8":
+            got = got.view(np.uint8)
         assert np.array_equal(got.astype(np.int64), want)

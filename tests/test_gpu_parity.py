@@ -64,7 +64,8 @@ def run_case(n, d, b, k, cdt, qdt, seed, excl=0.0, workspace_bytes=None, x=None,
 
 # --------------------------------------------------------------- prepare parity
 @pytest.mark.parametrize("dtype,d", [("f32", 16), ("f32", 64), ("bf16", 32), ("bf16", 128),
-                                     ("bf16", 256), ("fp8", 64), ("fp8", 256)])
+                                     ("bf16", 256), ("fp8", 64), ("fp8", 256), ("int8", 32),
+                                     ("int8", 128), ("int8", 256)])
 def test_prepare_matches_oracle_codes(dtype, d):
     dev = _dev()
     rng = np.random.default_rng(d)
@@ -89,6 +90,18 @@ def test_prepare_matches_oracle_codes(dtype, d):
         assert np.all(same | edge)
         assert gs[5] == 1.0
         assert np.all(corpus.row_scale.cpu().numpy()[n:] == 1.0)   # padding rows
+    if dtype == "int8":
+        gs = corpus.row_scale.cpu().numpy()[:n]
+        # scale = max|y| / 127 in fp32 on the GPU, from the fp64 row in the oracle
+        assert np.all(np.abs(gs / scale - 1) <= 1e-6)
+        assert gs[5] == np.float32(1e-12)
+        # every code within one step; the reconstruction within half a step (plus the
+        # difference of the two scales)
+        assert np.all(np.abs(got.astype(np.int32) - want.astype(np.int32)) <= 1)
+        assert np.mean(got == want) > 0.999
+        gv = oracle.decode(got, dtype, gs)
+        assert np.all(np.abs(gv - y) <= gs[:, None] * (0.5 + 1e-4) + 1e-7)
+        return
     gv = oracle.decode(got, dtype, gs)
     ov = oracle.decode(want, dtype, scale)
     exact = np.mean(got == want)
@@ -126,7 +139,8 @@ def test_l2_normalize_matches_oracle(out):
 # ----------------------------------------------------------------- top-k parity
 DTYPES = [("f32", "f32", 16), ("f32", "f32", 64), ("bf16", "bf16", 128), ("bf16", "bf16", 64),
           ("bf16", "f32", 32), ("bf16", "bf16", 256), ("fp8", "bf16", 256), ("fp8", "bf16", 64),
-          ("fp8", "f32", 128)]
+          ("fp8", "f32", 128), ("int8", "bf16", 128), ("int8", "f32", 64), ("int8", "bf16", 256),
+          ("int8", "bf16", 32)]
 SHAPES = [(1, 1, 1), (63, 5, 10), (64, 33, 64), (65, 3, 100), (1000, 40, 10), (9000, 7, 1024),
           (40000, 37, 100)]
 
@@ -138,7 +152,7 @@ def test_topk_parity(cdt, qdt, d, n, b, k):
 
 
 @pytest.mark.parametrize("cdt,qdt,d", [("bf16", "bf16", 128), ("fp8", "bf16", 128),
-                                       ("f32", "f32", 32)])
+                                       ("f32", "f32", 32), ("int8", "bf16", 128)])
 def test_topk_with_exclusion(cdt, qdt, d):
     run_case(70001, d, 45, 300, cdt, qdt, seed=5, excl=0.05)
     run_case(3000, d, 6, 50, cdt, qdt, seed=6, excl=0.5)

@@ -19,8 +19,9 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 def build_both(w, dev):
     """One pass over the raw chunks feeds both sides: GPU prepare and oracle prepare."""
     corpus = mips.empty_corpus(w.n, w.d, w.corpus_dtype, dev)
-    codes = np.empty((w.n, w.d), {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[w.corpus_dtype])
-    scale = np.empty(w.n, np.float32) if w.corpus_dtype == "fp8" else None
+    codes = np.empty((w.n, w.d), {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8,
+                                  "int8": np.int8}[w.corpus_dtype])
+    scale = np.empty(w.n, np.float32) if w.corpus_dtype in ("fp8", "int8") else None
 
     def cpu(r0, blk):
         c, s = oracle.prepare(blk, w.corpus_dtype)
@@ -59,7 +60,9 @@ def run_workload(name, sample):
     s, i = s.cpu().numpy(), i.cpu().numpy()
     excluded = set(w.excluded_ids().tolist()) if bm is not None else set()
     # every query: well-formed and within the unit bound
-    delta = {"f32": 2 ** -23, "bf16": 2 ** -8, "fp8": 2 ** -4}[w.corpus_dtype]
+    # relative rounding of a stored unit row: int8 moves each element by at most
+    # max|y| / 254, i.e. the row by at most sqrt(D) / 254 (< 2^-4 for D <= 256)
+    delta = {"f32": 2 ** -23, "bf16": 2 ** -8, "fp8": 2 ** -4, "int8": 2 ** -4}[w.corpus_dtype]
     kk = min(w.k, w.n - len(excluded))
     assert np.all(i[:, :kk] >= 0) and np.all(i[:, :kk] < w.n)
     assert np.all(s[:, :-1] >= s[:, 1:])
@@ -97,5 +100,9 @@ def test_fp8_n10m():
 
 
 @pytest.mark.timeout(1200)
+def test_int8_n10m():
+    run_workload("int8_n10m_d128_b256_excl5", [0, 1, 63, 64, 127, 200, 254, 255])
+
+
 def test_bf16_n100m():
     run_workload("bf16_n100m_d64_b1024", [0, 1023])

@@ -52,7 +52,7 @@ class Workload:
     d: int               # embedding width
     b: int               # queries per batch
     k: int               # results per query
-    corpus_dtype: str    # "f32", "bf16" or "fp8"
+    corpus_dtype: str    # "f32", "bf16", "fp8" or "int8"
     query_dtype: str     # "f32" or "bf16"
     clusters: int = 8
     exclude_frac: float = 0.0
@@ -70,7 +70,7 @@ class Workload:
 
     @property
     def corpus_elem_bytes(self) -> int:
-        return {"f32": 4, "bf16": 2, "fp8": 1}[self.corpus_dtype]
+        return {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[self.corpus_dtype]
 
     # ------------------------------------------------------------ clustered parts
     def centres(self) -> np.ndarray:
@@ -218,6 +218,11 @@ WORKLOADS = {
     "fp8_n10m_d256_b4096": Workload("fp8_n10m_d256_b4096", "clustered", n=10_000_000, d=256,
                                     b=4096, k=200, corpus_dtype="fp8", query_dtype="bf16",
                                     clusters=16384),
+    # the headline shape with the int8 index of the quantised scoring path
+    "int8_n10m_d128_b256_excl5": Workload("int8_n10m_d128_b256_excl5", "clustered",
+                                          n=10_000_000, d=128, b=256, k=500,
+                                          corpus_dtype="int8", query_dtype="bf16",
+                                          clusters=16384, exclude_frac=0.05),
 }
 
 # Seeds: each workload gets its own base seed so their streams never coincide.
