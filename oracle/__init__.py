@@ -14,6 +14,8 @@ Functions take and return numpy arrays:
 * ``topk(queries, q_dtype, corpus, c_dtype, k, row_scale=None, exclude=None)`` --
   fp64 scores [b, k] and int32 ids [b, k], sorted by score descending then id ascending.
 * ``scores(...)`` -- exact scores of given (query, id) pairs.
+* ``merge_topk(scores, ids, offsets, k)`` -- merge of per-index sorted result lists
+  ([p, b, k_in]) into one top-k per query, ids shifted by each index's offset.
 * ``e4m3_value``, ``bf16_value``, ``bf16_from``, ``e4m3_from``, ``e4m3_row_scale``,
   ``i8_from``, ``i8_row_scale`` -- the scalar format helpers, exposed for the format pins.
 """
@@ -76,7 +78,9 @@ def lib():
         L.oracle_prepare.argtypes = [p, i64, i32, i32, p, p]
         L.oracle_topk.argtypes = [i32, p, i32, i32, p, p, i64, i32, p, i32, p, p, i32]
         L.oracle_scores.argtypes = [i32, p, i32, i32, p, p, i64, i32, p, p, i64, p]
-        for f in (L.oracle_l2_normalize, L.oracle_prepare, L.oracle_topk, L.oracle_scores):
+        L.oracle_merge_topk.argtypes = [p, p, p, i32, i32, i32, i32, p, p]
+        for f in (L.oracle_l2_normalize, L.oracle_prepare, L.oracle_topk, L.oracle_scores,
+                  L.oracle_merge_topk):
             f.restype = C.c_int
         _lib = L
     return _lib
@@ -222,3 +226,17 @@ def scores(queries: np.ndarray, q_dtype: str, corpus: np.ndarray, c_dtype: str,
                                _ptr(row_scale), n, d, _ptr(qidx), _ptr(ids), qidx.size,
                                _ptr(out)), "scores")
     return out
+
+
+def merge_topk(scores: np.ndarray, ids: np.ndarray, offsets, k: int) -> Tuple[np.ndarray, np.ndarray]:
+    """scores float32 / ids int32 [p, b, k_in]; offsets int64 [p]."""
+    scores = np.ascontiguousarray(scores, np.float32)
+    ids = np.ascontiguousarray(ids, np.int32)
+    p, b, k_in = scores.shape
+    offsets = np.ascontiguousarray(offsets, np.int64)
+    assert offsets.size == p and ids.shape == scores.shape
+    out_s = np.empty((b, k), np.float32)
+    out_i = np.empty((b, k), np.int32)
+    _check(lib().oracle_merge_topk(_ptr(scores), _ptr(ids), _ptr(offsets), p, b, k_in, k,
+                                   _ptr(out_s), _ptr(out_i)), "merge_topk")
+    return out_s, out_i

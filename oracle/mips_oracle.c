@@ -35,6 +35,12 @@
  *    entries (`local_top_k` takes min(k, N)). Missing entries are padded with
  *    (-inf, -1). Excluded ids are never returned.
  *
+ *  - merging: the per-query union of several sorted (score, id) lists -- the
+ *    results of separate indexes, each id shifted by its index's offset -- cut to
+ *    the best k by the same order ("Two-Tower Retrieval at Industrial Scale",
+ *    engineeringmaxxing.com: the fresh shard searched beside the base index and
+ *    the two result lists merged by score). Padding entries (id -1) are skipped.
+ *
  * Non-finite inputs are not supported; the entry points reject them.
  */
 #include <math.h>
@@ -441,5 +447,45 @@ int oracle_scores(int32_t q_dtype, const void *queries, int32_t b, int32_t c_dty
         out[t] = score_one(q, c_dtype, corpus, row_scale, ids[t], d);
     }
     free(q);
+    return OR_OK;
+}
+
+/* Merge of p sorted lists per query: in_s/in_id are [p, b, k_in] (list-major), a
+ * list's ids are shifted by offsets[list]; entries with id < 0 are padding. The
+ * result per query is the first k_out of all real entries sorted by score
+ * descending, then id ascending, padded with (-inf, -1). */
+int oracle_merge_topk(const float *in_s, const int32_t *in_id, const int64_t *offsets,
+                      int32_t p, int32_t b, int32_t k_in, int32_t k_out, float *out_s,
+                      int32_t *out_id)
+{
+    if (!in_s || !in_id || !offsets || !out_s || !out_id || p < 1 || b < 0 || k_in < 1 ||
+        k_out < 1)
+        return OR_BAD_ARG;
+    pair_t *pairs = (pair_t *)malloc(sizeof(pair_t) * (size_t)p * (size_t)k_in);
+    if (!pairs)
+        return OR_NOMEM;
+    for (int32_t q = 0; q < b; ++q) {
+        int64_t m = 0;
+        for (int32_t l = 0; l < p; ++l)
+            for (int32_t j = 0; j < k_in; ++j) {
+                int64_t o = ((int64_t)l * b + q) * k_in + j;
+                if (in_id[o] < 0)
+                    continue;
+                if (!isfinite(in_s[o])) {
+                    free(pairs);
+                    return OR_NONFINITE;
+                }
+                pairs[m].s = (double)in_s[o];
+                pairs[m].id = (int32_t)(in_id[o] + offsets[l]);
+                ++m;
+            }
+        qsort(pairs, (size_t)m, sizeof(pair_t), cmp_pair);
+        for (int32_t t = 0; t < k_out; ++t) {
+            int64_t o = (int64_t)q * k_out + t;
+            out_s[o] = t < m ? (float)pairs[t].s : -INFINITY;
+            out_id[o] = t < m ? pairs[t].id : -1;
+        }
+    }
+    free(pairs);
     return OR_OK;
 }

@@ -318,3 +318,31 @@ def test_tiny_workload_groups():
     g = w.query_clusters()
     assert np.mean(ids % 8 == g[:, None]) > 0.95
     assert np.all(s[:, :-1] >= s[:, 1:])
+
+
+# ------------------------------------------------------------------ merging
+@pytest.mark.parametrize("cuts", [(0, 130, 131, 400), (0, 7, 400), (0, 200, 260, 300, 399, 400)])
+def test_merge_of_shard_topk_equals_full_topk(cuts):
+    """Top-k decomposes over a row partition: merging the shards' own top-k lists (ids
+    shifted by each shard's first row) gives the whole corpus's top-k, ties included."""
+    rng = np.random.default_rng(23)
+    n, d, b, k = 400, 8, 5, 40
+    c16, q16, _, _ = _grid_inputs(rng, n, d, b)   # many exact ties across shards
+    full_s, full_i = oracle.topk(q16, "bf16", c16, "bf16", k)
+    lists_s, lists_i = [], []
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        s, i = oracle.topk(q16, "bf16", c16[lo:hi], "bf16", k)
+        lists_s.append(s.astype(np.float32))
+        lists_i.append(i)
+    ms, mi = oracle.merge_topk(np.stack(lists_s), np.stack(lists_i), np.array(cuts[:-1]), k)
+    assert np.array_equal(mi, full_i)
+    assert np.array_equal(ms, full_s.astype(np.float32))
+
+
+def test_merge_pads_and_skips_padding():
+    s = np.array([[[0.5, -np.inf, -np.inf]], [[0.7, 0.5, -np.inf]]], np.float32)
+    i = np.array([[[3, -1, -1]], [[0, 1, -1]]], np.int32)
+    ms, mi = oracle.merge_topk(s, i, np.array([0, 100]), 5)
+    assert mi[0].tolist() == [100, 3, 101, -1, -1]      # 0.7, then the 0.5 tie by id
+    assert ms[0, :3].tolist() == [np.float32(0.7), 0.5, 0.5]
+    assert np.all(np.isneginf(ms[0, 3:]))
