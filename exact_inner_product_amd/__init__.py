@@ -25,8 +25,9 @@ K_MAX = 1024
 EXPORTS = (
     "mips_corpus_bytes", "mips_scale_count", "mips_l2_normalize", "mips_prepare_corpus",
     "mips_topk_workspace_size", "mips_topk_workspace_size_for", "mips_topk",
-    "mips_set_timing_events", "mips_status_string", "mips_last_hip_error",
+    "mips_merge_topk", "mips_set_timing_events", "mips_status_string", "mips_last_hip_error",
 )
+MERGE_MAX_LISTS = 64
 
 
 class MipsError(RuntimeError):
@@ -36,6 +37,11 @@ class MipsError(RuntimeError):
         if status == 4:
             msg += f" (hip error {lib().mips_last_hip_error()})"
         super().__init__(f"{what}: {msg}")
+
+
+class VersionSkew(RuntimeError):
+    """Queries from one model version against an index built by another: the scores would
+    be noise, so the call is refused before any work is enqueued."""
 
 
 _lib = None
@@ -61,11 +67,12 @@ def lib() -> C.CDLL:
         L.mips_topk_workspace_size_for.argtypes = [i32, i64, i32, i32, i32, i32, i64]
         L.mips_topk_workspace_size_for.restype = sz
         L.mips_topk.argtypes = [p, i32, i32, p, p, i32, i64, i32, p, i32, p, p, p, sz, p]
+        L.mips_merge_topk.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p]
         L.mips_set_timing_events.argtypes = [p, p]
         L.mips_status_string.argtypes = [C.c_int]
         L.mips_status_string.restype = C.c_char_p
         L.mips_last_hip_error.argtypes = []
-        for f in (L.mips_l2_normalize, L.mips_prepare_corpus, L.mips_topk,
+        for f in (L.mips_l2_normalize, L.mips_prepare_corpus, L.mips_topk, L.mips_merge_topk,
                   L.mips_set_timing_events, L.mips_last_hip_error):
             f.restype = C.c_int
         _lib = L
@@ -114,6 +121,7 @@ class Corpus:
     n: int
     d: int
     dtype: str
+    model_version: Optional[str] = None  # the item tower that produced the rows
 
     @property
     def code(self) -> int:
@@ -124,7 +132,8 @@ def corpus_bytes(n: int, d: int, dtype: str) -> int:
     return int(lib().mips_corpus_bytes(n, d, DTYPE_CODES[dtype]))
 
 
-def empty_corpus(n: int, d: int, dtype: str, device="cuda") -> Corpus:
+def empty_corpus(n: int, d: int, dtype: str, device="cuda",
+                 model_version: Optional[str] = None) -> Corpus:
     nbytes = corpus_bytes(n, d, dtype)
     if nbytes < 0:
         raise MipsError(2, "mips_corpus_bytes")
@@ -132,7 +141,7 @@ def empty_corpus(n: int, d: int, dtype: str, device="cuda") -> Corpus:
     scale = None
     if dtype in SCALED:
         scale = torch.empty(int(lib().mips_scale_count(n)), dtype=torch.float32, device=device)
-    return Corpus(packed, scale, n, d, dtype)
+    return Corpus(packed, scale, n, d, dtype, model_version)
 
 
 def prepare_rows(corpus: Corpus, x: torch.Tensor, row_offset: int) -> None:
@@ -144,9 +153,9 @@ def prepare_rows(corpus: Corpus, x: torch.Tensor, row_offset: int) -> None:
                                      _stream(x.device)), "mips_prepare_corpus")
 
 
-def prepare_corpus(x: torch.Tensor, dtype: str) -> Corpus:
+def prepare_corpus(x: torch.Tensor, dtype: str, model_version: Optional[str] = None) -> Corpus:
     """Normalise and pack a whole raw corpus (float32 [n, d] on the GPU)."""
-    c = empty_corpus(x.shape[0], x.shape[1], dtype, x.device)
+    c = empty_corpus(x.shape[0], x.shape[1], dtype, x.device, model_version)
     prepare_rows(c, x, 0)
     return c
 
@@ -167,16 +176,27 @@ def empty_workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+def check_version(corpus: Corpus, model_version: Optional[str]) -> None:
+    """Fails closed: once either side names a model version, both must name the same."""
+    if (model_version is not None or corpus.model_version is not None) and \
+            model_version != corpus.model_version:
+        raise VersionSkew(f"index built by model {corpus.model_version!r}, "
+                          f"queries from model {model_version!r}")
+
+
 def topk(queries: torch.Tensor, corpus: Corpus, k: int, exclude: Optional[torch.Tensor] = None,
          workspace: Optional[torch.Tensor] = None,
-         out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None
+         out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+         model_version: Optional[str] = None
          ) -> Tuple[torch.Tensor, torch.Tensor]:
     """Top-k by inner product: (scores float32 [b, k], ids int32 [b, k]).
 
     queries: float32 or bfloat16 [b, d] on the GPU, L2-normalised.
     exclude: optional int32/uint32-bit bitmap [ceil(n/32)] on the GPU (bit i of the corpus
     set => id i is never returned).
+    model_version: the user tower that produced the queries; see check_version.
     """
+    check_version(corpus, model_version)
     assert queries.is_cuda and queries.dim() == 2 and queries.shape[1] == corpus.d
     queries = queries.contiguous()
     b = queries.shape[0]
@@ -200,6 +220,44 @@ def topk(queries: torch.Tensor, corpus: Corpus, k: int, exclude: Optional[torch.
                            _ptr(ids), _ptr(workspace), workspace.numel(),
                            _stream(queries.device)), "mips_topk")
     return scores, ids
+
+
+def merge_topk(scores: torch.Tensor, ids: torch.Tensor, offsets, k: int
+               ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Merge p sorted result lists per query (scores float32 / ids int32 [p, b, k_in] on the
+    GPU, list l's ids shifted by offsets[l]) into one top-k: (scores [b, k], ids [b, k])."""
+    assert scores.is_cuda and scores.dtype == torch.float32 and scores.dim() == 3
+    assert ids.shape == scores.shape and ids.dtype == torch.int32 and ids.device == scores.device
+    p, b, k_in = scores.shape
+    offs = (C.c_int64 * p)(*[int(o) for o in offsets])
+    scores, ids = scores.contiguous(), ids.contiguous()
+    out_s = torch.empty((b, k), dtype=torch.float32, device=scores.device)
+    out_i = torch.empty((b, k), dtype=torch.int32, device=scores.device)
+    _check(lib().mips_merge_topk(_ptr(scores), _ptr(ids), C.cast(offs, C.c_void_p), p, b, k_in, k,
+                                 _ptr(out_s), _ptr(out_i), _stream(scores.device)),
+           "mips_merge_topk")
+    return out_s, out_i
+
+
+def search_shards(queries: torch.Tensor, shards, k: int, offsets=None,
+                  excludes=None, model_version: Optional[str] = None
+                  ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Top-k over several indexes (a base index and a fresh shard, or the row shards of one
+    corpus): each is searched on its own and the lists are merged. offsets[l] is the id of
+    shard l's first row (default: the shards' row counts, cumulated). Every shard must carry
+    the queries' model version (check_version), checked before any work is enqueued."""
+    for c in shards:
+        check_version(c, model_version)
+    if offsets is None:
+        offsets, o = [], 0
+        for c in shards:
+            offsets.append(o)
+            o += c.n
+    lists = [topk(queries, c, k, None if excludes is None else excludes[l],
+                  model_version=model_version) for l, c in enumerate(shards)]
+    s = torch.stack([t[0] for t in lists])
+    i = torch.stack([t[1] for t in lists])
+    return merge_topk(s, i, offsets, k)
 
 
 def set_timing_events(before, after) -> None:

@@ -178,6 +178,30 @@ MIPS_API int mips_topk(const void *queries, int32_t query_dtype, int32_t b, cons
               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * mips_merge_topk -- merge of p sorted result lists per query into one top-k_out: the
+ * fresh-shard pattern of "Two-Tower Retrieval at Industrial Scale" (engineeringmaxxing.com:
+ * a small fresh index is searched beside the base index and the result lists are merged
+ * by score), and the exchange step of a corpus split by rows across devices.
+ *   in_scores    device float [p, b, k_in] (list-major): list l, query q, rank j.
+ *   in_ids       device int32 [p, b, k_in]: ids local to list l's index; id < 0 is
+ *                padding and is skipped (as mips_topk pads with (-INFINITY, -1)).
+ *   offsets      host int64 [p], each in [0, 2^31): list l's ids are shifted by
+ *                offsets[l]. Shifted ids must be distinct across lists (disjoint
+ *                indexes) and below 2^31.
+ *   p            1 .. 64 lists; b >= 1 queries; k_in >= 1; k_out 1 .. MIPS_K_MAX.
+ *   out_scores   device float [b, k_out]; out_ids device int32 [b, k_out]: per query the
+ *                k_out best real entries of all lists, score descending then id
+ *                ascending, then (-INFINITY, -1). Exact for its inputs: when each list is
+ *                its index's exact top-k_out, the result is the exact top-k_out of the
+ *                union of the indexes.
+ * Errors: INVALID_ARG (NULL, p/b/k out of range, an offset out of range, misaligned
+ * pointers), UNSUPPORTED (k_out > MIPS_K_MAX), HIP (the launch failed).
+ */
+MIPS_API int mips_merge_topk(const float *in_scores, const int32_t *in_ids, const int64_t *offsets,
+                             int32_t p, int32_t b, int32_t k_in, int32_t k_out, float *out_scores,
+                             int32_t *out_ids, void *stream);
+
+/*
  * mips_set_timing_events -- profiling hook (host, per calling thread). When both are
  * non-NULL, later mips_topk calls on this thread record `before` (a hipEvent_t)
  * immediately before and `after` immediately after the launch of the main score

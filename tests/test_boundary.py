@@ -13,7 +13,7 @@ from tests.mips_check import untile
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mips.h")
 
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, INT8 = 0, 1, 2, 3
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
 
 
@@ -48,6 +48,8 @@ def test_corpus_bytes(L):
     assert L.mips_corpus_bytes(100, 48, BF16) == -1
     assert L.mips_corpus_bytes(0, 128, BF16) == -1
     assert L.mips_scale_count(1) == 32 and L.mips_scale_count(64) == 64
+    assert L.mips_corpus_bytes(100, 32, INT8) == 128 * 32
+    assert L.mips_corpus_bytes(100, 16, INT8) == -1     # int8 needs d in {32, .., 256}
 
 
 def test_workspace_size(L):
@@ -143,3 +145,39 @@ def test_untile_inverts_the_documented_layout():
         if dtype == "int8":
             got = got.view(np.uint8)
         assert np.array_equal(got.astype(np.int64), want)
+
+
+def test_merge_rejects_bad_arguments_before_launch(L):
+    vp = C.c_void_p
+    offs = (C.c_int64 * 2)(0, 100)
+    args = lambda **kw: dict(dict(s=vp(0x1000), i=vp(0x2000), o=C.cast(offs, vp), p=2, b=3,
+                                  kin=10, kout=10, os=vp(0x3000), oi=vp(0x4000)), **kw)
+    call = lambda a: L.mips_merge_topk(a["s"], a["i"], a["o"], a["p"], a["b"], a["kin"],
+                                       a["kout"], a["os"], a["oi"], None)
+    assert call(args(s=None)) == INVALID
+    assert call(args(o=None)) == INVALID
+    assert call(args(p=0)) == INVALID
+    assert call(args(p=65)) == INVALID
+    assert call(args(b=0)) == INVALID
+    assert call(args(kin=0)) == INVALID
+    assert call(args(kout=1025)) == UNSUPPORTED
+    assert call(args(s=vp(0x1002))) == INVALID            # misaligned
+    bad = (C.c_int64 * 2)(0, -5)
+    assert call(args(o=C.cast(bad, vp))) == INVALID
+
+
+def test_version_guard_fails_closed():
+    import torch
+    c = mips.Corpus(torch.empty(0, dtype=torch.uint8), None, 10, 16, "f32", model_version="v2")
+    mips.check_version(c, "v2")
+    for wrong in ("v1", None):
+        with pytest.raises(mips.VersionSkew):
+            mips.check_version(c, wrong)
+        with pytest.raises(mips.VersionSkew):   # refused before any device work
+            mips.topk(torch.empty(1, 16), c, 5, model_version=wrong)
+    unversioned = mips.Corpus(torch.empty(0, dtype=torch.uint8), None, 10, 16, "f32")
+    mips.check_version(unversioned, None)
+    with pytest.raises(mips.VersionSkew):
+        mips.check_version(unversioned, "v2")
+    with pytest.raises(mips.VersionSkew):
+        mips.search_shards(torch.empty(1, 16), [unversioned, c], 5, model_version="v2")

@@ -308,3 +308,52 @@ def test_planted_item_exclusion_shift_and_k_prefix():
         bm = bitmap_from_ids(np.array([planted[qi]]), w.n)
         s3, i3 = _scores_ids(q[qi:qi + 1], corpus, 50, torch.from_numpy(bm.view(np.int32)).to(dev))
         assert np.array_equal(i3[0], i[qi, 1:51])
+
+
+# ------------------------------------------------------------------ merging
+@pytest.mark.parametrize("cdt,qdt,d", [("bf16", "bf16", 128), ("int8", "bf16", 64)])
+def test_row_shards_merged_equal_one_pass(cdt, qdt, d):
+    """A corpus split by rows into separately packed shards (cuts not multiples of 32),
+    each searched alone and the lists merged: the same ids and bitwise the same scores as
+    one pass over the whole corpus, and the oracle's top-k."""
+    dev = _dev()
+    n, b, k = 50000, 37, 300
+    w = _workload(n, d, b, k, cdt, qdt, 41)
+    x, qraw = w.corpus(), w.queries()
+    cuts = [0, 12345, 30001, 30002, n]
+    whole, q = _gpu_inputs(w, x, qraw, dev)
+    shards = [mips.prepare_corpus(torch.from_numpy(x[lo:hi]).to(dev), cdt, model_version="m7")
+              for lo, hi in zip(cuts[:-1], cuts[1:])]
+    s1, i1 = _scores_ids(q, whole, k)
+    s2, i2 = mips.search_shards(q, shards, k, model_version="m7")
+    torch.cuda.synchronize()
+    s2, i2 = s2.cpu().numpy(), i2.cpu().numpy()
+    assert np.array_equal(i1, i2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    c_or, sc_or = oracle.prepare(x, cdt)
+    q_or, _ = oracle.prepare(qraw, qdt)
+    o_s, o_i = oracle.topk(q_or, qdt, c_or, cdt, k, row_scale=sc_or)
+    check_topk(s2, i2, o_s, o_i, q_or, qdt, c_or, cdt, sc_or, set(), n, TOL[cdt],
+               floor=floor_for(cdt, qdt))
+
+
+def test_fresh_shard_merge_matches_oracle_merge():
+    """A base index's top-k and a fresh index's shorter list (padded), merged on the GPU,
+    against the oracle's merge of the same lists (exact for its inputs: bitwise)."""
+    dev = _dev()
+    d, b, k = 64, 20, 200
+    wb = _workload(30000, d, b, k, "bf16", "bf16", 42)
+    wf = _workload(700, d, b, k, "bf16", "bf16", 43)
+    base, q = _gpu_inputs(wb, wb.corpus(), wb.queries(), dev)
+    fresh, _ = _gpu_inputs(wf, wf.corpus(), wb.queries(), dev)
+    sb, ib = mips.topk(q, base, k)
+    sf, i_f = mips.topk(q, fresh, k // 10)
+    pad_s = torch.full((b, k), float("-inf"), device=dev)
+    pad_i = torch.full((b, k), -1, dtype=torch.int32, device=dev)
+    pad_s[:, : k // 10], pad_i[:, : k // 10] = sf, i_f
+    ls, li = torch.stack([sb, pad_s]), torch.stack([ib, pad_i])
+    for kout in (k, 7, 1024):
+        ms, mi = mips.merge_topk(ls, li, [0, wb.n], kout)
+        torch.cuda.synchronize()
+        os_, oi = oracle.merge_topk(ls.cpu().numpy(), li.cpu().numpy(), [0, wb.n], kout)
+        assert np.array_equal(mi.cpu().numpy(), oi)
+        assert np.array_equal(ms.cpu().numpy().view(np.uint32), os_.view(np.uint32))
