@@ -24,7 +24,7 @@ K_MAX = 1024
 
 EXPORTS = (
     "mips_corpus_bytes", "mips_scale_count", "mips_l2_normalize", "mips_prepare_corpus",
-    "mips_topk_workspace_size", "mips_topk_workspace_size_for", "mips_topk",
+    "mips_topk_workspace_size", "mips_topk_workspace_size_for", "mips_topk", "mips_topk_ranges",
     "mips_merge_topk", "mips_set_timing_events", "mips_status_string", "mips_last_hip_error",
 )
 MERGE_MAX_LISTS = 64
@@ -67,12 +67,15 @@ def lib() -> C.CDLL:
         L.mips_topk_workspace_size_for.argtypes = [i32, i64, i32, i32, i32, i32, i64]
         L.mips_topk_workspace_size_for.restype = sz
         L.mips_topk.argtypes = [p, i32, i32, p, p, i32, i64, i32, p, i32, p, p, p, sz, p]
+        L.mips_topk_ranges.argtypes = [p, i32, i32, p, p, i32, i64, i32, p, p, i32, i32, p, p, p,
+                                       sz, p]
         L.mips_merge_topk.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p]
         L.mips_set_timing_events.argtypes = [p, p]
         L.mips_status_string.argtypes = [C.c_int]
         L.mips_status_string.restype = C.c_char_p
         L.mips_last_hip_error.argtypes = []
-        for f in (L.mips_l2_normalize, L.mips_prepare_corpus, L.mips_topk, L.mips_merge_topk,
+        for f in (L.mips_l2_normalize, L.mips_prepare_corpus, L.mips_topk, L.mips_topk_ranges,
+                  L.mips_merge_topk,
                   L.mips_set_timing_events, L.mips_last_hip_error):
             f.restype = C.c_int
         _lib = L
@@ -219,6 +222,38 @@ def topk(queries: torch.Tensor, corpus: Corpus, k: int, exclude: Optional[torch.
                            corpus.code, corpus.n, corpus.d, _ptr(exclude), k, _ptr(scores),
                            _ptr(ids), _ptr(workspace), workspace.numel(),
                            _stream(queries.device)), "mips_topk")
+    return scores, ids
+
+
+def topk_ranges(queries: torch.Tensor, corpus: Corpus, ranges, k: int,
+                exclude: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                model_version: Optional[str] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Top-k per id range [start, end): (scores float32 [r, b, k], ids int32 [r, b, k]), ids
+    absolute. One pass per range over the blocks that hold its rows."""
+    check_version(corpus, model_version)
+    assert queries.is_cuda and queries.dim() == 2 and queries.shape[1] == corpus.d
+    queries = queries.contiguous()
+    b = queries.shape[0]
+    qc = _qcode(queries)
+    flat = [int(v) for rg in ranges for v in rg]
+    nr = len(flat) // 2
+    rg = (C.c_int64 * len(flat))(*flat)
+    if workspace is None:
+        nbytes = lib().mips_topk_workspace_size(b, corpus.n, corpus.d, k, qc, corpus.code)
+        if nbytes == 0:
+            raise MipsError(2, "mips_topk_workspace_size")
+        workspace = empty_workspace(nbytes, queries.device)
+    scores = torch.empty((nr, b, k), dtype=torch.float32, device=queries.device)
+    ids = torch.empty((nr, b, k), dtype=torch.int32, device=queries.device)
+    if exclude is not None:
+        assert exclude.is_cuda and exclude.dtype in (torch.int32, torch.uint32)
+        assert exclude.numel() >= (corpus.n + 31) // 32
+        exclude = exclude.contiguous()
+    _check(lib().mips_topk_ranges(_ptr(queries), qc, b, _ptr(corpus.packed),
+                                  _ptr(corpus.row_scale), corpus.code, corpus.n, corpus.d,
+                                  _ptr(exclude), C.cast(rg, C.c_void_p), nr, k, _ptr(scores),
+                                  _ptr(ids), _ptr(workspace), workspace.numel(),
+                                  _stream(queries.device)), "mips_topk_ranges")
     return scores, ids
 
 

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
 #pragma unroll
       for (int r = 0; r < RM; ++r) {
         const int64_t j = min<int64_t>(j0 + r, A.nfrag - 1);
-        const int64_t fr = (MODE == MODE_SAMPLE) ? (int64_t)(((uint64_t)j * A.sample_step) >> 32) : j;
+        const int64_t fr = A.blk0 + ((MODE == MODE_SAMPLE) ? (int64_t)(((uint64_t)j * A.sample_step) >> 32) : j);
         // one buffer descriptor per block (scalar base, range = the block's bytes) and a
         // 32-bit lane offset: no per-lane 64-bit addresses to keep live
         const __amdgpu_buffer_rsrc_t rs = block_rsrc(A.corpus + fr * BLK, (int)BLK);
@@ -255,13 +255,15 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
       const int r = lane < RM ? lane : RM - 1;
       const bool live = j0 + r < A.nfrag;
       const int64_t j = live ? j0 + r : A.nfrag - 1;
-      const int64_t fr = (MODE == MODE_SAMPLE) ? (int64_t)(((uint64_t)j * A.sample_step) >> 32) : j;
+      const int64_t fr = A.blk0 + ((MODE == MODE_SAMPLE) ? (int64_t)(((uint64_t)j * A.sample_step) >> 32) : j);
       // branch-free: without a bitmap, any readable word masked to zero (a conditional
       // load would make the compiler's wait counts conservative at the join)
       const uint32_t* wp = A.exclude ? A.exclude + fr : (const uint32_t*)A.corpus;
       uint32_t w = *wp & (A.exclude ? ~0u : 0u);
       const int64_t rows = A.n - fr * kFrag;
       if (rows < kFrag) w |= ~0u << rows;
+      const int64_t below = A.lo - fr * kFrag;  // rows before the start of the id range
+      if (below > 0) w |= below >= kFrag ? ~0u : (1u << below) - 1u;
       xwv = live ? w : ~0u;
     };
 
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
         for (int g = 0; g < RM; ++g) {
           if (__ballot(m[g] >= T) == 0ull) continue;
           const uint32_t w = __builtin_amdgcn_readlane(xwv, g);
-          const uint32_t idb = (uint32_t)((j0 + g) * kFrag);
+          const uint32_t idb = (uint32_t)((A.blk0 + j0 + g) * kFrag);
           float y[16];
           vals(acc[g], sc[g], y);
 #pragma unroll
@@ -407,7 +409,8 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
               const int row = acc_row(i, lane);
               dst[row] = ((w >> row) & 1u)
                              ? 0ull
-                             : composite(score_key(post(x[i], sq)), (uint32_t)(j * kFrag + row));
+                             : composite(score_key(post(x[i], sq)),
+                                         (uint32_t)((A.blk0 + j) * kFrag + row));
             }
           }
         }

@@ -48,8 +48,10 @@ struct ScoreArgs {
   const uint32_t* exclude;
   const uint8_t* qtile;
   const int* qexp;
-  int64_t n;
-  int64_t n32;      // 32-row blocks in the corpus
+  int64_t n;        // rows below n take part (the end of the id range)
+  int64_t lo;       // rows at or above lo take part (the start of the id range)
+  int64_t blk0;     // first block of the pass (lo / 32); block ids are absolute
+  int64_t n32;      // 32-row blocks in the pass
   int64_t nfrag;    // blocks this pass covers: n32, or G sampled blocks (strided)
   int64_t ntiles;   // stage tiles of the pass
   int b;

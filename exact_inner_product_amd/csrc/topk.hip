@@ -193,7 +193,8 @@ struct SelectArgs {
   const uint32_t* exclude;
   const uint8_t* qtile;
   const int* qexp;
-  int64_t n;
+  int64_t n;            // rows [lo, n) take part
+  int64_t lo;
   int b;
   int k;
   int64_t capw;         // entries per list segment
@@ -247,7 +248,7 @@ __device__ void fallback_scan(const SelectArgs& A, int q, uint64_t thr, uint64_t
   if (threadIdx.x == 0) *nbuf_p = 0u;
   __syncthreads();
   constexpr int kRound = kSelThreads * 4;
-  for (int64_t base = 0; base < A.n; base += kRound) {
+  for (int64_t base = A.lo; base < A.n; base += kRound) {
     if (*nbuf_p + (uint32_t)kRound > (uint32_t)kSelCache) {
       // Compact to the k best and raise the threshold to their lower bound.
       const int m = (int)*nbuf_p;
@@ -448,7 +449,7 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
 // ------------------------------------------------------------------- planning
 struct Plan {
   int b, b32, k, d, qdt, cdt;
-  int64_t n, n32;
+  int64_t n, n32, lo, blk0;  // rows [lo, n); n32 blocks from blk0
   int rm, nqf, nqblk, G, rest, nseg;
   bool dense;
   int64_t capw;  // candidate entries per list segment
@@ -481,7 +482,9 @@ static int estimate_rank(int64_t n32, int G, int k) {
 }
 
 // capq: candidate capacity per query (< 0: the default).
-static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt, int64_t capq) {
+// The pass covers rows [lo, n): the blocks from lo / 32 to the one holding row n - 1.
+static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt, int64_t capq,
+                      int64_t lo = 0) {
   p.b = b;
   p.b32 = (b + 31) / 32 * 32;
   p.k = k;
@@ -489,7 +492,9 @@ static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt,
   p.qdt = qdt;
   p.cdt = cdt;
   p.n = n;
-  p.n32 = (n + 31) / 32;
+  p.lo = lo;
+  p.blk0 = lo / 32;
+  p.n32 = (n + 31) / 32 - p.blk0;
   p.rm = stage_frags(cdt, d);
   int nqf_max = 16;
   while (nqf_max > 1 && !nqf_fits(cdt, d, nqf_max)) nqf_max >>= 1;
@@ -561,6 +566,8 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   A.qtile = qtile;
   A.qexp = qexp;
   A.n = p.n;
+  A.lo = p.lo;
+  A.blk0 = p.blk0;
   A.n32 = p.n32;
   A.b = p.b;
   A.b32 = p.b32;
@@ -587,6 +594,7 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   S.qtile = qtile;
   S.qexp = qexp;
   S.n = p.n;
+  S.lo = p.lo;
   S.b = p.b;
   S.k = p.k;
   S.capw = p.capw;
@@ -703,34 +711,61 @@ int mips_topk(const void* queries, int32_t query_dtype, int32_t b, const void* c
               const float* row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
               const uint32_t* exclude, int32_t k, float* out_scores, int32_t* out_ids,
               void* workspace, size_t workspace_bytes, void* stream) {
-  if (!queries || !corpus || !out_scores || !out_ids || !workspace) return MIPS_ERR_INVALID_ARG;
+  const int64_t whole[2] = {0, n};
+  return mips_topk_ranges(queries, query_dtype, b, corpus, row_scale, corpus_dtype, n, d, exclude,
+                          whole, 1, k, out_scores, out_ids, workspace, workspace_bytes, stream);
+}
+
+int mips_topk_ranges(const void* queries, int32_t query_dtype, int32_t b, const void* corpus,
+                     const float* row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
+                     const uint32_t* exclude, const int64_t* ranges, int32_t nranges, int32_t k,
+                     float* out_scores, int32_t* out_ids, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (!queries || !corpus || !out_scores || !out_ids || !workspace || !ranges)
+    return MIPS_ERR_INVALID_ARG;
   const int rc0 = mips::validate_topk(query_dtype, b, corpus_dtype, n, d, k);
   if (rc0 != MIPS_OK) return rc0;
+  if (nranges < 1) return MIPS_ERR_INVALID_ARG;
+  for (int r = 0; r < nranges; ++r)
+    if (ranges[2 * r] < 0 || ranges[2 * r] >= ranges[2 * r + 1] || ranges[2 * r + 1] > n)
+      return MIPS_ERR_INVALID_ARG;
   if ((corpus_dtype == MIPS_FP8_E4M3 || corpus_dtype == MIPS_INT8) && !row_scale)
     return MIPS_ERR_INVALID_ARG;
   if (!mips::aligned(queries, 4) || !mips::aligned(corpus, 16) || !mips::aligned(workspace, 256) ||
       !mips::aligned(out_scores, 4) || !mips::aligned(out_ids, 4) ||
       (exclude && !mips::aligned(exclude, 4)) || (row_scale && !mips::aligned(row_scale, 4)))
     return MIPS_ERR_INVALID_ARG;
+  // the whole corpus's plan bounds every range's fixed part and capacity
   mips::Plan p;
   mips::make_plan(p, b, n, d, k, query_dtype, corpus_dtype, -1);
   if (workspace_bytes < p.fixed) return MIPS_ERR_WORKSPACE;
   // candidate capacity per query: whole segments of what the workspace holds
   const int64_t capq = (int64_t)((workspace_bytes - p.fixed) / ((size_t)b * 8u));
   if (capq / p.nseg < 1) return MIPS_ERR_WORKSPACE;
-  mips::make_plan(p, b, n, d, k, query_dtype, corpus_dtype, capq);
   hipStream_t s = (hipStream_t)stream;
   uint8_t* ws = (uint8_t*)workspace;
-  switch (corpus_dtype) {
-    case MIPS_F32:
-      return mips::dispatch_d<MIPS_F32>(p, queries, corpus, row_scale, exclude, out_scores, out_ids, ws, s);
-    case MIPS_BF16:
-      return mips::dispatch_d<MIPS_BF16>(p, queries, corpus, row_scale, exclude, out_scores, out_ids, ws, s);
-    case MIPS_INT8:
-      return mips::dispatch_d<MIPS_INT8>(p, queries, corpus, row_scale, exclude, out_scores, out_ids, ws, s);
-    default:
-      return mips::dispatch_d<MIPS_FP8_E4M3>(p, queries, corpus, row_scale, exclude, out_scores, out_ids, ws, s);
+  for (int r = 0; r < nranges; ++r) {
+    mips::make_plan(p, b, ranges[2 * r + 1], d, k, query_dtype, corpus_dtype, capq, ranges[2 * r]);
+    float* os = out_scores + (int64_t)r * b * k;
+    int32_t* oi = out_ids + (int64_t)r * b * k;
+    int rc;
+    switch (corpus_dtype) {
+      case MIPS_F32:
+        rc = mips::dispatch_d<MIPS_F32>(p, queries, corpus, row_scale, exclude, os, oi, ws, s);
+        break;
+      case MIPS_BF16:
+        rc = mips::dispatch_d<MIPS_BF16>(p, queries, corpus, row_scale, exclude, os, oi, ws, s);
+        break;
+      case MIPS_INT8:
+        rc = mips::dispatch_d<MIPS_INT8>(p, queries, corpus, row_scale, exclude, os, oi, ws, s);
+        break;
+      default:
+        rc = mips::dispatch_d<MIPS_FP8_E4M3>(p, queries, corpus, row_scale, exclude, os, oi, ws, s);
+        break;
+    }
+    if (rc != MIPS_OK) return rc;
   }
+  return MIPS_OK;
 }
 
 }  // extern "C"

@@ -178,6 +178,29 @@ MIPS_API int mips_topk(const void *queries, int32_t query_dtype, int32_t b, cons
               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * mips_topk_ranges -- mips_topk restricted to id ranges, one result set per range: for
+ * range r = [ranges[2r], ranges[2r+1]), the exact top-k of the non-excluded rows with ids
+ * in the range (the dataset_ranges path of `RecsysTwoTowerModel.forward` in
+ * recsys_two_tower_model.py, which slices the scores to [start, end), takes a sorted
+ * top-k and adds start to the indices). Each range's pass reads only the blocks that hold
+ * its rows, so disjoint ranges read the corpus once in all.
+ *   ranges       host int64 [nranges][2]: 0 <= start < end <= n; ranges may overlap.
+ *   nranges      >= 1.
+ *   out_scores   device float [nranges, b, k]; out_ids device int32 [nranges, b, k]:
+ *                range r's result, as mips_topk's, with absolute ids.
+ *   The other arguments, the ordering, the padding and the workspace are as mips_topk's
+ *   (the workspace for the whole corpus serves every range; ranges run one after the
+ *   other on the stream).
+ * Errors: as mips_topk, plus INVALID_ARG for a NULL ranges, nranges < 1 or a range outside
+ * [0, n) or empty.
+ */
+MIPS_API int mips_topk_ranges(const void *queries, int32_t query_dtype, int32_t b, const void *corpus,
+                              const float *row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
+                              const uint32_t *exclude, const int64_t *ranges, int32_t nranges,
+                              int32_t k, float *out_scores, int32_t *out_ids, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
  * mips_merge_topk -- merge of p sorted result lists per query into one top-k_out: the
  * fresh-shard pattern of "Two-Tower Retrieval at Industrial Scale" (engineeringmaxxing.com:
  * a small fresh index is searched beside the base index and the result lists are merged

@@ -181,3 +181,20 @@ def test_version_guard_fails_closed():
         mips.check_version(unversioned, "v2")
     with pytest.raises(mips.VersionSkew):
         mips.search_shards(torch.empty(1, 16), [unversioned, c], 5, model_version="v2")
+
+
+def test_topk_ranges_rejects_bad_ranges_before_launch(L):
+    vp = C.c_void_p
+
+    def call(rg, nr=None):
+        arr = (C.c_int64 * max(1, len(rg)))(*rg) if rg else None
+        return L.mips_topk_ranges(vp(0x1000), BF16, 4, vp(0x2000), None, BF16, 1000, 128, None,
+                                  None if arr is None else C.cast(arr, vp),
+                                  len(rg) // 2 if nr is None else nr, 10, vp(0x3000), vp(0x4000),
+                                  vp(0x5000), 1 << 30, None)
+    assert call([]) == INVALID                    # no ranges
+    assert call([0, 10], nr=0) == INVALID
+    assert call([10, 10]) == INVALID              # empty
+    assert call([5, 1001]) == INVALID             # past the corpus
+    assert call([-1, 5]) == INVALID
+    assert call([0, 10, 20, 15]) == INVALID       # second range inverted

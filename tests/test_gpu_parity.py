@@ -357,3 +357,43 @@ def test_fresh_shard_merge_matches_oracle_merge():
         os_, oi = oracle.merge_topk(ls.cpu().numpy(), li.cpu().numpy(), [0, wb.n], kout)
         assert np.array_equal(mi.cpu().numpy(), oi)
         assert np.array_equal(ms.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+
+
+# ------------------------------------------------------------------ id ranges
+def _range_bitmap(n, lo, hi, base_bitmap=None):
+    """Exclusion bitmap that also masks every id outside [lo, hi): the oracle's reading of
+    a range's top-k is the top-k of the non-excluded rows inside the range."""
+    ids = np.concatenate([np.arange(0, lo), np.arange(hi, n)])
+    bm = bitmap_from_ids(ids, n)
+    if base_bitmap is not None:
+        bm = bm | base_bitmap
+    return bm
+
+
+@pytest.mark.parametrize("cdt,qdt,d,n", [("bf16", "bf16", 128, 20000), ("int8", "bf16", 64, 20000),
+                                         ("bf16", "bf16", 64, 400000)])
+def test_topk_ranges_match_masked_oracle(cdt, qdt, d, n):
+    dev = _dev()
+    b, k = 9, 50
+    w = _workload(n, d, b, k, cdt, qdt, 51, excl=0.05)
+    x, qraw = w.corpus(), w.queries()
+    corpus, q = _gpu_inputs(w, x, qraw, dev)
+    bm = w.exclude_bitmap()
+    ranges = [(0, n), (5, 37), (33, 1000), (1000, n - 1), (12345, 12346), (64, 96),
+              (n // 3, n // 3 + 40), (7, n)]
+    s, i = mips.topk_ranges(q, corpus, ranges, k, _excl_tensor(bm, dev))
+    torch.cuda.synchronize()
+    s, i = s.cpu().numpy(), i.cpu().numpy()
+    c_or, sc_or = oracle.prepare(x, cdt)
+    q_or, _ = oracle.prepare(qraw, qdt)
+    for r, (lo, hi) in enumerate(ranges):
+        print(f"range {r}: [{lo}, {hi})", flush=True)
+        rbm = _range_bitmap(n, lo, hi, bm)
+        o_s, o_i = oracle.topk(q_or, qdt, c_or, cdt, k, row_scale=sc_or, exclude=rbm)
+        ids = np.arange(n)
+        excluded = set(ids[((rbm[ids >> 5] >> (ids & 31).astype(np.uint32)) & 1) == 1].tolist())
+        check_topk(s[r], i[r], o_s, o_i, q_or, qdt, c_or, cdt, sc_or, excluded, n, TOL[cdt],
+                   floor=floor_for(cdt, qdt))
+    # the whole-corpus range is mips_topk itself, bitwise
+    s0, i0 = _scores_ids(q, corpus, k, _excl_tensor(bm, dev))
+    assert np.array_equal(i0, i[0]) and np.array_equal(s0.view(np.uint32), s[0].view(np.uint32))
