@@ -16,6 +16,8 @@ Functions take and return numpy arrays:
 * ``scores(...)`` -- exact scores of given (query, id) pairs.
 * ``merge_topk(scores, ids, offsets, k)`` -- merge of per-index sorted result lists
   ([p, b, k_in]) into one top-k per query, ids shifted by each index's offset.
+* ``maxsim_topk(queries [b, m, d], ...)`` -- top-k of users with m interest vectors each,
+  an item scored by its best match over the user's vectors.
 * ``e4m3_value``, ``bf16_value``, ``bf16_from``, ``e4m3_from``, ``e4m3_row_scale``,
   ``i8_from``, ``i8_row_scale`` -- the scalar format helpers, exposed for the format pins.
 """
@@ -79,8 +81,9 @@ def lib():
         L.oracle_topk.argtypes = [i32, p, i32, i32, p, p, i64, i32, p, i32, p, p, i32]
         L.oracle_scores.argtypes = [i32, p, i32, i32, p, p, i64, i32, p, p, i64, p]
         L.oracle_merge_topk.argtypes = [p, p, p, i32, i32, i32, i32, p, p]
+        L.oracle_maxsim_topk.argtypes = [i32, p, i32, i32, i32, p, p, i64, i32, p, i32, p, p, i32]
         for f in (L.oracle_l2_normalize, L.oracle_prepare, L.oracle_topk, L.oracle_scores,
-                  L.oracle_merge_topk):
+                  L.oracle_merge_topk, L.oracle_maxsim_topk):
             f.restype = C.c_int
         _lib = L
     return _lib
@@ -239,4 +242,25 @@ def merge_topk(scores: np.ndarray, ids: np.ndarray, offsets, k: int) -> Tuple[np
     out_i = np.empty((b, k), np.int32)
     _check(lib().oracle_merge_topk(_ptr(scores), _ptr(ids), _ptr(offsets), p, b, k_in, k,
                                    _ptr(out_s), _ptr(out_i)), "merge_topk")
+    return out_s, out_i
+
+
+def maxsim_topk(queries: np.ndarray, q_dtype: str, corpus: np.ndarray, c_dtype: str, k: int,
+                row_scale: Optional[np.ndarray] = None, exclude: Optional[np.ndarray] = None,
+                threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """queries [b, m, d]: fp64 max-over-vectors scores [b, k] and ids [b, k]."""
+    queries = np.ascontiguousarray(queries)
+    corpus = np.ascontiguousarray(corpus)
+    b, m, d = queries.shape
+    n = corpus.shape[0]
+    if row_scale is not None:
+        row_scale = np.ascontiguousarray(row_scale, np.float32)
+    if exclude is not None:
+        exclude = np.ascontiguousarray(exclude, np.uint32)
+    out_s = np.empty((b, k), np.float64)
+    out_i = np.empty((b, k), np.int32)
+    _check(lib().oracle_maxsim_topk(DTYPES[q_dtype], _ptr(queries), b, m, DTYPES[c_dtype],
+                                    _ptr(corpus), _ptr(row_scale), n, d, _ptr(exclude), k,
+                                    _ptr(out_s), _ptr(out_i), threads or default_threads()),
+           "maxsim_topk")
     return out_s, out_i

@@ -301,7 +301,7 @@ static int cmp_pair(const void *a, const void *b)
 }
 
 typedef struct {
-    int32_t q_dtype, c_dtype, d, k, b;
+    int32_t q_dtype, c_dtype, d, k, b, m; /* m query rows per result row (interests) */
     const void *queries, *corpus;
     const float *row_scale;
     const uint32_t *exclude;
@@ -317,7 +317,7 @@ static void *topk_worker(void *arg)
 {
     topk_job_t *J = (topk_job_t *)arg;
     pair_t *pairs = (pair_t *)malloc(sizeof(pair_t) * (size_t)(J->n > 0 ? J->n : 1));
-    double *q = (double *)malloc(sizeof(double) * (size_t)J->d);
+    double *q = (double *)malloc(sizeof(double) * (size_t)J->d * (size_t)J->m);
     if (!pairs || !q) {
         pthread_mutex_lock(&J->lock);
         J->status = OR_NOMEM;
@@ -332,13 +332,21 @@ static void *topk_worker(void *arg)
         pthread_mutex_unlock(&J->lock);
         if (b >= J->b)
             break;
-        for (int32_t j = 0; j < J->d; ++j)
-            q[j] = stored_value(J->q_dtype, J->queries, (int64_t)b * J->d + j);
+        /* result row b: query rows b*m .. b*m+m-1; an item scores its best match */
+        for (int64_t j = 0; j < (int64_t)J->d * J->m; ++j)
+            q[j] = stored_value(J->q_dtype, J->queries, (int64_t)b * J->m * J->d + j);
         int64_t m = 0;
         for (int64_t i = 0; i < J->n; ++i) {
             if (excluded(J->exclude, i))
                 continue;
-            pairs[m].s = score_one(q, J->c_dtype, J->corpus, J->row_scale, i, J->d);
+            double best = score_one(q, J->c_dtype, J->corpus, J->row_scale, i, J->d);
+            for (int32_t v = 1; v < J->m; ++v) {
+                double sv = score_one(q + (int64_t)v * J->d, J->c_dtype, J->corpus,
+                                      J->row_scale, i, J->d);
+                if (sv > best)
+                    best = sv;
+            }
+            pairs[m].s = best;
             pairs[m].id = (int32_t)i;
             ++m;
         }
@@ -374,10 +382,38 @@ static int check_finite(int32_t dtype, const void *p, int64_t count)
  *   exclude:  NULL or uint32[ceil(n/32)], bit (i & 31) of word (i >> 5) excludes id i
  *   out_s:    [b, k] fp64 scores, out_id: [b, k] int32 ids
  */
+static int topk_m(int32_t q_dtype, const void *queries, int32_t b, int32_t mq, int32_t c_dtype,
+                  const void *corpus, const float *row_scale, int64_t n, int32_t d,
+                  const uint32_t *exclude, int32_t k, double *out_s, int32_t *out_id,
+                  int32_t threads);
+
 int oracle_topk(int32_t q_dtype, const void *queries, int32_t b, int32_t c_dtype,
                 const void *corpus, const float *row_scale, int64_t n, int32_t d,
                 const uint32_t *exclude, int32_t k, double *out_s, int32_t *out_id,
                 int32_t threads)
+{
+    return topk_m(q_dtype, queries, b, 1, c_dtype, corpus, row_scale, n, d, exclude, k, out_s,
+                  out_id, threads);
+}
+
+/* Top-k of b users with m query vectors each (queries [b * m, d], user-major): an item's
+ * score is its best dot product over the user's vectors (the max over interest vectors
+ * of "Two-Tower Retrieval at Industrial Scale", section "Beyond Dot Products"). */
+int oracle_maxsim_topk(int32_t q_dtype, const void *queries, int32_t b, int32_t m,
+                       int32_t c_dtype, const void *corpus, const float *row_scale, int64_t n,
+                       int32_t d, const uint32_t *exclude, int32_t k, double *out_s,
+                       int32_t *out_id, int32_t threads)
+{
+    if (m < 1)
+        return OR_BAD_ARG;
+    return topk_m(q_dtype, queries, b, m, c_dtype, corpus, row_scale, n, d, exclude, k, out_s,
+                  out_id, threads);
+}
+
+static int topk_m(int32_t q_dtype, const void *queries, int32_t b, int32_t mq, int32_t c_dtype,
+                  const void *corpus, const float *row_scale, int64_t n, int32_t d,
+                  const uint32_t *exclude, int32_t k, double *out_s, int32_t *out_id,
+                  int32_t threads)
 {
     if (!queries || !corpus || !out_s || !out_id || b < 0 || n < 0 || d <= 0 || k <= 0)
         return OR_BAD_ARG;
@@ -386,7 +422,7 @@ int oracle_topk(int32_t q_dtype, const void *queries, int32_t b, int32_t c_dtype
     if (c_dtype < OR_F32 || c_dtype > OR_I8 ||
         ((c_dtype == OR_E4M3 || c_dtype == OR_I8) && !row_scale))
         return OR_BAD_ARG;
-    if (!check_finite(q_dtype, queries, (int64_t)b * d) ||
+    if (!check_finite(q_dtype, queries, (int64_t)b * mq * d) ||
         !check_finite(c_dtype, corpus, n * (int64_t)d))
         return OR_NONFINITE;
     if (c_dtype == OR_E4M3 || c_dtype == OR_I8)
@@ -401,6 +437,7 @@ int oracle_topk(int32_t q_dtype, const void *queries, int32_t b, int32_t c_dtype
     J.d = d;
     J.k = k;
     J.b = b;
+    J.m = mq;
     J.queries = queries;
     J.corpus = corpus;
     J.row_scale = row_scale;

@@ -346,3 +346,47 @@ def test_merge_pads_and_skips_padding():
     assert mi[0].tolist() == [100, 3, 101, -1, -1]      # 0.7, then the 0.5 tie by id
     assert ms[0, :3].tolist() == [np.float32(0.7), 0.5, 0.5]
     assert np.all(np.isneginf(ms[0, 3:]))
+
+
+# ------------------------------------------------------------ multi-interest
+def test_maxsim_reduces_to_topk():
+    """One interest vector is the plain top-k; a user whose vectors repeat one query is
+    that query's top-k (the max of equal scores)."""
+    w, corpus, queries = _small_clustered(seed=24)
+    s1, i1 = oracle.topk(queries, "bf16", corpus, "bf16", 25)
+    s2, i2 = oracle.maxsim_topk(queries[:, None, :], "bf16", corpus, "bf16", 25)
+    assert np.array_equal(i1, i2) and np.array_equal(s1, s2)
+    rep = np.repeat(queries[:, None, :], 3, axis=1)
+    s3, i3 = oracle.maxsim_topk(rep, "bf16", corpus, "bf16", 25)
+    assert np.array_equal(i1, i3) and np.array_equal(s1, s3)
+
+
+def test_maxsim_closed_form_two_interests():
+    """Interests e_0 and e_1 over axis-aligned items: the items of both axes come first,
+    ordered by their own coordinate, ties by id."""
+    d = 4
+    corpus = np.zeros((8, d), np.float32)
+    vals = [0.9, 0.5, 0.7, 0.3]
+    for j, v in enumerate(vals):
+        corpus[j, 0] = v           # ids 0..3 on axis 0
+        corpus[4 + j, 1] = v       # ids 4..7 on axis 1
+    corpus[:, 2] = 0.1             # every item also has a small third coordinate
+    q = np.zeros((1, 2, d), np.float32)
+    q[0, 0, 0] = 1.0
+    q[0, 1, 1] = 1.0
+    s, ids = oracle.maxsim_topk(q, "f32", corpus, "f32", 8)
+    assert ids[0].tolist() == [0, 4, 2, 6, 1, 5, 3, 7]
+    assert np.allclose(s[0], [0.9, 0.9, 0.7, 0.7, 0.5, 0.5, 0.3, 0.3])
+
+
+def test_maxsim_equals_brute_force_max():
+    rng = np.random.default_rng(25)
+    n, d, b, m, k = 200, 12, 3, 4, 30
+    corpus, _ = oracle.prepare(rng.standard_normal((n, d)).astype(np.float32), "bf16")
+    q, _ = oracle.prepare(rng.standard_normal((b * m, d)).astype(np.float32), "bf16")
+    s, ids = oracle.maxsim_topk(q.reshape(b, m, d), "bf16", corpus, "bf16", k)
+    cv, qv = oracle.decode(corpus, "bf16"), oracle.decode(q, "bf16").reshape(b, m, d)
+    for u in range(b):
+        best = (qv[u] @ cv.T).max(axis=0)
+        order = sorted(range(n), key=lambda i: (-best[i], i))[:k]
+        assert ids[u].tolist() == order
