@@ -25,7 +25,7 @@ K_MAX = 1024
 EXPORTS = (
     "mips_corpus_bytes", "mips_scale_count", "mips_l2_normalize", "mips_prepare_corpus",
     "mips_topk_workspace_size", "mips_topk_workspace_size_for", "mips_topk", "mips_topk_ranges",
-    "mips_merge_topk", "mips_set_timing_events", "mips_status_string", "mips_last_hip_error",
+    "mips_merge_topk", "mips_merge_interests", "mips_set_timing_events", "mips_status_string", "mips_last_hip_error",
 )
 MERGE_MAX_LISTS = 64
 
@@ -70,12 +70,13 @@ def lib() -> C.CDLL:
         L.mips_topk_ranges.argtypes = [p, i32, i32, p, p, i32, i64, i32, p, p, i32, i32, p, p, p,
                                        sz, p]
         L.mips_merge_topk.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p]
+        L.mips_merge_interests.argtypes = [p, p, i32, i32, i32, i32, p, p, p]
         L.mips_set_timing_events.argtypes = [p, p]
         L.mips_status_string.argtypes = [C.c_int]
         L.mips_status_string.restype = C.c_char_p
         L.mips_last_hip_error.argtypes = []
         for f in (L.mips_l2_normalize, L.mips_prepare_corpus, L.mips_topk, L.mips_topk_ranges,
-                  L.mips_merge_topk,
+                  L.mips_merge_topk, L.mips_merge_interests,
                   L.mips_set_timing_events, L.mips_last_hip_error):
             f.restype = C.c_int
         _lib = L
@@ -293,6 +294,24 @@ def search_shards(queries: torch.Tensor, shards, k: int, offsets=None,
     s = torch.stack([t[0] for t in lists])
     i = torch.stack([t[1] for t in lists])
     return merge_topk(s, i, offsets, k)
+
+
+def topk_multi_interest(queries: torch.Tensor, corpus: Corpus, k: int,
+                        exclude: Optional[torch.Tensor] = None,
+                        k_per_vector: Optional[int] = None,
+                        model_version: Optional[str] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Top-k of users with m interest vectors each (queries [b, m, d], L2-normalised rows):
+    an item scores its best match over the user's vectors. Each vector is searched for
+    k_per_vector results (default k: exact), then each user's lists are merged."""
+    assert queries.dim() == 3
+    b, m, d = queries.shape
+    kv = k if k_per_vector is None else k_per_vector
+    s, i = topk(queries.reshape(b * m, d), corpus, kv, exclude, model_version=model_version)
+    out_s = torch.empty((b, k), dtype=torch.float32, device=queries.device)
+    out_i = torch.empty((b, k), dtype=torch.int32, device=queries.device)
+    _check(lib().mips_merge_interests(_ptr(s), _ptr(i), b, m, kv, k, _ptr(out_s), _ptr(out_i),
+                                      _stream(queries.device)), "mips_merge_interests")
+    return out_s, out_i
 
 
 def set_timing_events(before, after) -> None:

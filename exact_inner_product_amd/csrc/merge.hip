@@ -66,9 +66,99 @@ __global__ __launch_bounds__(kSelThreads) void merge_topk_kernel(MergeArgs A) {
   }
 }
 
+// ----------------------------------------------------------- multi-interest merge
+// A user with m interest vectors scores an item by its best match over them (the max of
+// "Two-Tower Retrieval at Industrial Scale", section "Beyond Dot Products": K interest
+// vectors, K searches, results merged). Each interest's own top-k list is merged per user:
+// an id that several interests return keeps its highest score, then the best k_out ids are
+// kept. When every list is its interest's exact top-k_out, the result is the exact top-k_out
+// by max score (an item in the max-score top-k is in the top-k of its best interest).
+constexpr int kInterestEntries = 2048;  // m * k_in per user
+constexpr int kInterestHash = 4096;     // open-addressing table, load at most 1/2
+constexpr uint32_t kEmptyId = 0xFFFFFFFFu;
+
+struct InterestArgs {
+  const float* in_s;     // [b, m, k_in]
+  const int32_t* in_id;  // [b, m, k_in]; id < 0 is padding
+  int b, m, k_in, k_out;
+  float* out_s;          // [b, k_out]
+  int32_t* out_id;
+};
+
+__global__ __launch_bounds__(kSelThreads) void merge_interests_kernel(InterestArgs A) {
+  __shared__ uint32_t hid[kInterestHash];
+  __shared__ uint32_t hkey[kInterestHash];
+  __shared__ uint64_t sel_buf[MIPS_K_MAX];
+  __shared__ SelScratch S;
+  __shared__ uint32_t nvalid;
+  const int q = blockIdx.x;
+  const int t = threadIdx.x;
+  for (int i = t; i < kInterestHash; i += kSelThreads) {
+    hid[i] = kEmptyId;
+    hkey[i] = 0u;
+  }
+  if (t == 0) nvalid = 0u;
+  __syncthreads();
+  const int64_t base = (int64_t)q * A.m * A.k_in;
+  const int m = A.m * A.k_in;
+  for (int e = t; e < m; e += kSelThreads) {
+    const int32_t id = A.in_id[base + e];
+    if (id < 0) continue;
+    const uint32_t key = score_key(A.in_s[base + e]);
+    uint32_t slot = ((uint32_t)id * 2654435761u) & (kInterestHash - 1);  // Knuth's multiplier
+    for (;;) {  // at most m < kInterestHash distinct ids: a free or matching slot exists
+      const uint32_t prev = atomicCAS(&hid[slot], kEmptyId, (uint32_t)id);
+      if (prev == kEmptyId || prev == (uint32_t)id) {
+        atomicMax(&hkey[slot], key);
+        break;
+      }
+      slot = (slot + 1u) & (kInterestHash - 1);
+    }
+  }
+  __syncthreads();
+  auto get = [&](int64_t i) -> uint64_t {
+    return hid[i] == kEmptyId ? 0ull : composite(hkey[i], hid[i]);
+  };
+  uint32_t mine = 0u;
+  for (int i = t; i < kInterestHash; i += kSelThreads) mine += hid[i] != kEmptyId;
+  atomicAdd(&nvalid, mine);
+  __syncthreads();
+  const int r = (int)min<uint32_t>(nvalid, (uint32_t)A.k_out);
+  if (r > 0) {
+    Sel64 sel{0ull, 0ull};
+    if (kInterestHash > r) sel = select_top(get, kInterestHash, r, S);
+    gather_sort(get, kInterestHash, r, sel, sel_buf, &S.hist[0]);
+  }
+  for (int j = t; j < A.k_out; j += kSelThreads) {
+    float sc = -INFINITY;
+    int32_t id = -1;
+    if (j < r) {
+      sc = key_score((uint32_t)(sel_buf[j] >> 32));
+      id = (int32_t)composite_id(sel_buf[j]);
+    }
+    A.out_s[(int64_t)q * A.k_out + j] = sc;
+    A.out_id[(int64_t)q * A.k_out + j] = id;
+  }
+}
+
 }  // namespace mips
 
 extern "C" {
+
+int mips_merge_interests(const float* in_scores, const int32_t* in_ids, int32_t b, int32_t m,
+                         int32_t k_in, int32_t k_out, float* out_scores, int32_t* out_ids,
+                         void* stream) {
+  if (!in_scores || !in_ids || !out_scores || !out_ids) return MIPS_ERR_INVALID_ARG;
+  if (b < 1 || m < 1 || k_in < 1 || k_out < 1) return MIPS_ERR_INVALID_ARG;
+  if (k_out > MIPS_K_MAX || (int64_t)m * k_in > mips::kInterestEntries) return MIPS_ERR_UNSUPPORTED;
+  if (!mips::aligned(in_scores, 4) || !mips::aligned(in_ids, 4) || !mips::aligned(out_scores, 4) ||
+      !mips::aligned(out_ids, 4))
+    return MIPS_ERR_INVALID_ARG;
+  mips::InterestArgs A{in_scores, in_ids, b, m, k_in, k_out, out_scores, out_ids};
+  hipLaunchKernelGGL(mips::merge_interests_kernel, dim3(b), dim3(mips::kSelThreads), 0,
+                     (hipStream_t)stream, A);
+  return mips::check_launch();
+}
 
 int mips_merge_topk(const float* in_scores, const int32_t* in_ids, const int64_t* offsets,
                     int32_t p, int32_t b, int32_t k_in, int32_t k_out, float* out_scores,

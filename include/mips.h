@@ -225,6 +225,27 @@ MIPS_API int mips_merge_topk(const float *in_scores, const int32_t *in_ids, cons
                              int32_t *out_ids, void *stream);
 
 /*
+ * mips_merge_interests -- per user, the merge of its m interest vectors' result lists:
+ * a user with several interest vectors matches an item by the best of them ("Two-Tower
+ * Retrieval at Industrial Scale", engineeringmaxxing.com, section "Beyond Dot Products":
+ * one search per interest vector, results merged by the maximum). An id returned for
+ * several of the user's vectors keeps its highest score; the best k_out ids follow, score
+ * descending then id ascending, then (-INFINITY, -1). When each list is its vector's exact
+ * top-k_out (mips_topk over the b * m vectors), the result is the exact top-k_out by the
+ * maximum over the user's vectors.
+ *   in_scores    device float [b, m, k_in] (user-major: rows u*m .. u*m+m-1 of a mips_topk
+ *                output); in_ids device int32 [b, m, k_in], id < 0 is padding.
+ *   b >= 1 users, m >= 1 vectors per user, k_in >= 1 with m * k_in <= 2048,
+ *   k_out 1 .. MIPS_K_MAX.
+ *   out_scores   device float [b, k_out]; out_ids device int32 [b, k_out].
+ * Errors: INVALID_ARG (NULL, b/m/k < 1, misaligned pointers), UNSUPPORTED (m * k_in > 2048
+ * or k_out > MIPS_K_MAX), HIP (the launch failed).
+ */
+MIPS_API int mips_merge_interests(const float *in_scores, const int32_t *in_ids, int32_t b, int32_t m,
+                                  int32_t k_in, int32_t k_out, float *out_scores, int32_t *out_ids,
+                                  void *stream);
+
+/*
  * mips_set_timing_events -- profiling hook (host, per calling thread). When both are
  * non-NULL, later mips_topk calls on this thread record `before` (a hipEvent_t)
  * immediately before and `after` immediately after the launch of the main score

@@ -198,3 +198,14 @@ def test_topk_ranges_rejects_bad_ranges_before_launch(L):
     assert call([5, 1001]) == INVALID             # past the corpus
     assert call([-1, 5]) == INVALID
     assert call([0, 10, 20, 15]) == INVALID       # second range inverted
+
+
+def test_merge_interests_rejects_bad_arguments_before_launch(L):
+    vp = C.c_void_p
+    call = lambda b=2, m=4, kin=10, kout=10, s=vp(0x1000): L.mips_merge_interests(
+        s, vp(0x2000), b, m, kin, kout, vp(0x3000), vp(0x4000), None)
+    assert call(s=None) == INVALID
+    assert call(b=0) == INVALID and call(m=0) == INVALID and call(kin=0) == INVALID
+    assert call(m=4, kin=513) == UNSUPPORTED      # 2052 entries per user
+    assert call(kout=1025) == UNSUPPORTED
+    assert call(s=vp(0x1001)) == INVALID

@@ -397,3 +397,41 @@ def test_topk_ranges_match_masked_oracle(cdt, qdt, d, n):
     # the whole-corpus range is mips_topk itself, bitwise
     s0, i0 = _scores_ids(q, corpus, k, _excl_tensor(bm, dev))
     assert np.array_equal(i0, i[0]) and np.array_equal(s0.view(np.uint32), s[0].view(np.uint32))
+
+
+# ------------------------------------------------------------ multi-interest
+@pytest.mark.parametrize("cdt,m,k", [("bf16", 4, 100), ("int8", 2, 500), ("bf16", 8, 256)])
+def test_multi_interest_matches_maxsim_oracle(cdt, m, k):
+    """Users with m interest vectors: mips_topk over every vector (k each), then the
+    per-user merge keeping each id's best score, against the oracle's top-k by the maximum
+    over the user's vectors."""
+    dev = _dev()
+    n, d, b = 30000, 64, 11
+    w = _workload(n, d, b * m, k, cdt, "bf16", 61, excl=0.05)
+    x, qraw = w.corpus(), w.queries()
+    corpus, q = _gpu_inputs(w, x, qraw, dev)
+    bm = w.exclude_bitmap()
+    s, i = mips.topk_multi_interest(q.reshape(b, m, d), corpus, k, _excl_tensor(bm, dev))
+    torch.cuda.synchronize()
+    s, i = s.cpu().numpy(), i.cpu().numpy()
+    c_or, sc_or = oracle.prepare(x, cdt)
+    q_or, _ = oracle.prepare(qraw, "bf16")
+    o_s, o_i = oracle.maxsim_topk(q_or.reshape(b, m, d), "bf16", c_or, cdt, k, row_scale=sc_or,
+                                  exclude=bm)
+    excluded = set(w.excluded_ids().tolist())
+    # the acceptance rule per user, with the score of an id its best over the user's vectors
+    for u in range(b):
+        gi = i[u][i[u] >= 0]
+        assert len(set(gi.tolist())) == gi.size and not (set(gi.tolist()) & excluded)
+        assert np.all(s[u][:-1] >= s[u][1:])
+        e = np.max([oracle.scores(q_or[u * m:(u + 1) * m], "bf16", c_or, cdt,
+                                  np.full(gi.size, v), gi, row_scale=sc_or) for v in range(m)],
+                   axis=0)
+        assert np.abs(s[u][: gi.size] - e).max() <= TOL[cdt]
+        assert np.abs(s[u] - o_s[u].astype(np.float32)).max() <= TOL[cdt]
+        diff = set(gi.tolist()) ^ set(o_i[u].tolist())
+        kth = o_s[u, k - 1]
+        for t in diff:
+            et = np.max(oracle.scores(q_or[u * m:(u + 1) * m], "bf16", c_or, cdt,
+                                      np.arange(m), np.full(m, t), row_scale=sc_or))
+            assert abs(et - kth) <= TOL[cdt], (u, t, et, kth)
