@@ -25,7 +25,7 @@ K_MAX = 1024
 EXPORTS = (
     "mips_corpus_bytes", "mips_scale_count", "mips_l2_normalize", "mips_prepare_corpus",
     "mips_topk_workspace_size", "mips_topk_workspace_size_for", "mips_topk", "mips_topk_ranges",
-    "mips_merge_topk", "mips_merge_interests", "mips_set_timing_events", "mips_status_string", "mips_last_hip_error",
+    "mips_merge_topk", "mips_merge_interests", "mips_type_bitmap", "mips_set_timing_events", "mips_status_string", "mips_last_hip_error",
 )
 MERGE_MAX_LISTS = 64
 
@@ -71,12 +71,13 @@ def lib() -> C.CDLL:
                                        sz, p]
         L.mips_merge_topk.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p]
         L.mips_merge_interests.argtypes = [p, p, i32, i32, i32, i32, p, p, p]
+        L.mips_type_bitmap.argtypes = [p, i64, i32, p, p, p]
         L.mips_set_timing_events.argtypes = [p, p]
         L.mips_status_string.argtypes = [C.c_int]
         L.mips_status_string.restype = C.c_char_p
         L.mips_last_hip_error.argtypes = []
         for f in (L.mips_l2_normalize, L.mips_prepare_corpus, L.mips_topk, L.mips_topk_ranges,
-                  L.mips_merge_topk, L.mips_merge_interests,
+                  L.mips_merge_topk, L.mips_merge_interests, L.mips_type_bitmap,
                   L.mips_set_timing_events, L.mips_last_hip_error):
             f.restype = C.c_int
         _lib = L
@@ -312,6 +313,59 @@ def topk_multi_interest(queries: torch.Tensor, corpus: Corpus, k: int,
     _check(lib().mips_merge_interests(_ptr(s), _ptr(i), b, m, kv, k, _ptr(out_s), _ptr(out_i),
                                       _stream(queries.device)), "mips_merge_interests")
     return out_s, out_i
+
+
+def topk_types(queries: torch.Tensor, corpus: Corpus, item_types: torch.Tensor, targets, k: int,
+               exclude: Optional[torch.Tensor] = None, return_validity: bool = False,
+               model_version: Optional[str] = None):
+    """One top-k per target item type: a tuple with, per target, (ids [b, k], scores [b, k])
+    or (ids, scores, validity) with return_validity. Items of other types are never returned,
+    so validity is ids >= 0 (padding marks a type with fewer than k eligible items)."""
+    check_version(corpus, model_version)
+    assert item_types.is_cuda and item_types.dtype == torch.int32 and item_types.numel() == corpus.n
+    words = (corpus.n + 31) // 32
+    if exclude is not None:
+        exclude = exclude.contiguous()
+    ws = None
+    results = []
+    for t in targets:
+        bm = torch.empty(words, dtype=torch.int32, device=item_types.device)
+        _check(lib().mips_type_bitmap(_ptr(item_types.contiguous()), corpus.n, int(t),
+                                      _ptr(exclude), _ptr(bm), _stream(item_types.device)),
+               "mips_type_bitmap")
+        if ws is None:
+            nbytes = lib().mips_topk_workspace_size(queries.shape[0], corpus.n, corpus.d, k,
+                                                    _qcode(queries), corpus.code)
+            if nbytes == 0:
+                raise MipsError(2, "mips_topk_workspace_size")
+            ws = empty_workspace(nbytes, queries.device)
+        s, i = topk(queries, corpus, k, bm, workspace=ws, model_version=model_version)
+        results.append((i, s, i >= 0) if return_validity else (i, s))
+    return tuple(results)
+
+
+def recall_at_k(approx_ids, exact_ids) -> "np.ndarray":
+    """Per query, the fraction of the exact result's ids (padding -1 ignored) that the
+    approximate result contains, in any order."""
+    import numpy as np
+    a = np.asarray(approx_ids)
+    e = np.asarray(exact_ids)
+    out = np.empty(e.shape[0])
+    for q in range(e.shape[0]):
+        want = e[q][e[q] >= 0]
+        out[q] = 1.0 if want.size == 0 else np.isin(want, a[q][a[q] >= 0]).mean()
+    return out
+
+
+def recall_vs_exact(approx_ids, queries: torch.Tensor, corpus: Corpus, k: int,
+                    exclude: Optional[torch.Tensor] = None,
+                    model_version: Optional[str] = None) -> "np.ndarray":
+    """Recall@k of an approximate index's ids [b, >= k] against this library's exact top-k
+    of the same queries: measures the index apart from the model (exact neighbours by brute
+    force on a query sample, then the fraction an ANN structure returns; "Two-Tower Retrieval
+    at Industrial Scale", section on evaluation)."""
+    _, ids = topk(queries, corpus, k, exclude, model_version=model_version)
+    return recall_at_k(approx_ids, ids.cpu().numpy())
 
 
 def set_timing_events(before, after) -> None:

@@ -141,9 +141,42 @@ __global__ __launch_bounds__(kSelThreads) void merge_interests_kernel(InterestAr
   }
 }
 
+// ------------------------------------------------------------------ type masks
+// Bitmap of the ids a type-restricted search must skip: id i is excluded when its type is
+// not the target (the per-type mask of `RecsysTwoTowerModel.forward`, dataset_types ==
+// target) or when the base bitmap excludes it. One thread per 32-id word.
+__global__ __launch_bounds__(256) void type_bitmap_kernel(const int32_t* __restrict__ types,
+                                                          int64_t n, int32_t target,
+                                                          const uint32_t* __restrict__ base,
+                                                          uint32_t* __restrict__ out) {
+  const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (w >= (n + 31) / 32) return;
+  uint32_t bits = base ? base[w] : 0u;
+  for (int r = 0; r < 32; ++r) {
+    const int64_t i = w * 32 + r;
+    if (i >= n || types[i] != target) bits |= 1u << r;
+  }
+  out[w] = bits;
+}
+
 }  // namespace mips
 
 extern "C" {
+
+int mips_type_bitmap(const int32_t* item_types, int64_t n, int32_t target,
+                     const uint32_t* exclude, uint32_t* out_bitmap, void* stream) {
+  if (!item_types || !out_bitmap || n < 1) return MIPS_ERR_INVALID_ARG;
+  if (!mips::aligned(item_types, 4) || !mips::aligned(out_bitmap, 4) ||
+      (exclude && !mips::aligned(exclude, 4)))
+    return MIPS_ERR_INVALID_ARG;
+  const int64_t words = (n + 31) / 32;
+  const int64_t grid = (words + 255) / 256;
+  if (grid > 0x7FFFFFFF) return MIPS_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(mips::type_bitmap_kernel, dim3((unsigned)grid), dim3(256), 0,
+                     (hipStream_t)stream, item_types, n, target, exclude, out_bitmap);
+  return mips::check_launch();
+}
+
 
 int mips_merge_interests(const float* in_scores, const int32_t* in_ids, int32_t b, int32_t m,
                          int32_t k_in, int32_t k_out, float* out_scores, int32_t* out_ids,

@@ -201,6 +201,20 @@ MIPS_API int mips_topk_ranges(const void *queries, int32_t query_dtype, int32_t 
                               size_t workspace_bytes, void *stream);
 
 /*
+ * mips_type_bitmap -- the exclusion bitmap of a search restricted to one item type: id i
+ * is excluded when item_types[i] != target or exclude marks it (the per-type mask of
+ * `RecsysTwoTowerModel.forward`, recsys_two_tower_model.py, one result set per target
+ * type). Feed the result to mips_topk; excluded ids are never returned, so every id a
+ * type-restricted search returns has that type.
+ *   item_types   device int32 [n]; n >= 1.
+ *   exclude      device uint32 [ceil(n/32)] or NULL: ids excluded in any case.
+ *   out_bitmap   device uint32 [ceil(n/32)]; bits of ids >= n are set. May alias exclude.
+ * Errors: INVALID_ARG (NULL, n < 1, misaligned pointers), HIP (the launch failed).
+ */
+MIPS_API int mips_type_bitmap(const int32_t *item_types, int64_t n, int32_t target,
+                              const uint32_t *exclude, uint32_t *out_bitmap, void *stream);
+
+/*
  * mips_merge_topk -- merge of p sorted result lists per query into one top-k_out: the
  * fresh-shard pattern of "Two-Tower Retrieval at Industrial Scale" (engineeringmaxxing.com:
  * a small fresh index is searched beside the base index and the result lists are merged

@@ -209,3 +209,17 @@ def test_merge_interests_rejects_bad_arguments_before_launch(L):
     assert call(m=4, kin=513) == UNSUPPORTED      # 2052 entries per user
     assert call(kout=1025) == UNSUPPORTED
     assert call(s=vp(0x1001)) == INVALID
+
+
+def test_recall_at_k_counts_exact_ids_found():
+    import numpy as np
+    exact = np.array([[1, 2, 3, 4], [5, 6, -1, -1], [-1, -1, -1, -1]])
+    approx = np.array([[4, 9, 2, 7, 1], [6, 5, 0, 0, 0], [3, 3, 3, 3, 3]])
+    assert mips.recall_at_k(approx, exact).tolist() == [0.75, 1.0, 1.0]
+
+
+def test_type_bitmap_rejects_bad_arguments_before_launch(L):
+    vp = C.c_void_p
+    assert L.mips_type_bitmap(None, 10, 1, None, vp(0x1000), None) == INVALID
+    assert L.mips_type_bitmap(vp(0x1000), 0, 1, None, vp(0x2000), None) == INVALID
+    assert L.mips_type_bitmap(vp(0x1002), 10, 1, None, vp(0x2000), None) == INVALID

@@ -435,3 +435,42 @@ def test_multi_interest_matches_maxsim_oracle(cdt, m, k):
             et = np.max(oracle.scores(q_or[u * m:(u + 1) * m], "bf16", c_or, cdt,
                                       np.arange(m), np.full(m, t), row_scale=sc_or))
             assert abs(et - kth) <= TOL[cdt], (u, t, et, kth)
+
+
+def test_recall_harness_against_exact():
+    dev = _dev()
+    w = _workload(20000, 64, 16, 100, "bf16", "bf16", 71)
+    corpus, q = _gpu_inputs(w, w.corpus(), w.queries(), dev)
+    _, exact = _scores_ids(q, corpus, 100)
+    assert np.all(mips.recall_vs_exact(exact, q, corpus, 100) == 1.0)
+    half = exact.copy()
+    half[:, 1::2] = -1                                   # an "index" that loses every other hit
+    assert np.allclose(mips.recall_vs_exact(half, q, corpus, 100), 0.5)
+    assert np.all(mips.recall_vs_exact(exact[:, :10], q, corpus, 100) == 0.1)
+
+
+def test_topk_per_item_type():
+    """One result set per target type, against the oracle's top-k with the other types
+    masked (and the base exclusion); validity marks padding only."""
+    dev = _dev()
+    n, d, b, k = 30000, 128, 7, 200
+    w = _workload(n, d, b, k, "bf16", "bf16", 81, excl=0.05)
+    x, qraw = w.corpus(), w.queries()
+    corpus, q = _gpu_inputs(w, x, qraw, dev)
+    bm = w.exclude_bitmap()
+    types = np.random.default_rng(82).integers(0, 3, n).astype(np.int32)
+    types[:150] = 7                     # a rare type: fewer eligible items than k
+    res = mips.topk_types(q, corpus, torch.from_numpy(types).to(dev), [0, 2, 7], k,
+                          _excl_tensor(bm, dev), return_validity=True)
+    c_or, sc_or = oracle.prepare(x, "bf16")
+    q_or, _ = oracle.prepare(qraw, "bf16")
+    for t, (i, s, v) in zip([0, 2, 7], res):
+        i, s, v = i.cpu().numpy(), s.cpu().numpy(), v.cpu().numpy()
+        other = np.nonzero(types != t)[0]
+        tbm = bitmap_from_ids(other, n) | bm
+        o_s, o_i = oracle.topk(q_or, "bf16", c_or, "bf16", k, exclude=tbm)
+        excluded = set(other.tolist()) | set(w.excluded_ids().tolist())
+        check_topk(s, i, o_s, o_i, q_or, "bf16", c_or, "bf16", None, excluded, n, TOL["bf16"],
+                   floor=floor_for("bf16", "bf16"))
+        assert np.array_equal(v, i >= 0)
+        assert np.all(types[i[i >= 0]] == t)
