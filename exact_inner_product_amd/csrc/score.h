@@ -54,14 +54,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* p, int 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
 }
 
-// One workgroup = 4 waves (one per SIMD) = one corpus slice x one block of 32 * NQF
-// queries. Each wave streams stage tiles of RM 32-row blocks (16 KiB) into registers, two
-// stages in flight, and multiplies each stage against every query fragment of the block
-// in LDS. The query-fragment loop is unrolled and software-pipelined: the MFMAs of
+// One workgroup = 4 or 8 waves (one or two per SIMD) = one corpus slice x one block of
+// 32 * NQF queries. Each wave streams stage tiles of RM 32-row blocks (16 KiB per SIMD)
+// into registers, two stages in flight, and multiplies each stage against every query
+// fragment of the block in LDS. The query-fragment loop is unrolled and software-pipelined: the MFMAs of
 // fragment qf+1 and the LDS reads of fragment qf+2's operand are issued before the
 // epilogue of fragment qf.
 template <int CT, int D, int NQF, int MODE>
-__global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void score_kernel(ScoreArgs A) {
+__global__ __launch_bounds__(score_threads(CT, D))
+__attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void score_kernel(ScoreArgs A) {
+  constexpr int kScoreThreads = score_threads(CT, D);
+  constexpr int kScoreWaves = score_waves(CT, D);
   constexpr int E = elem_bytes(CT);
   constexpr int NCH = chunks_per_block(CT, D);
   constexpr int RM = stage_frags(CT, D);
@@ -468,9 +471,11 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
 
     // NS-stage software pipeline over this wave's stage tiles (a stage every kScoreWaves
     // tiles): while stage i is multiplied against every query, stages i+1 .. i+NS-1 are in
-    // flight. With one wave per SIMD, the bytes in flight per wave set the HBM bandwidth
-    // (Little's law at several microseconds of loaded latency), hence NS - 1 = 2 stages.
-    constexpr int NS = kPipeStages;
+    // flight. The bytes in flight per SIMD set the HBM bandwidth (Little's law at several
+    // microseconds of loaded latency), hence NS - 1 = 2 stages of 16 KiB per SIMD. The
+    // sample and dense passes hold one stage less with two waves per SIMD: their epilogues
+    // need the registers, and they run few stages per wave.
+    constexpr int NS = (MODE != MODE_MAIN && score_wps(CT, D) == 2) ? 2 : kPipeStages;
     u32x4_t a[NS][RM][NCH];
     int sa[NS][RM];
     float sc[NS][RM][SCN];
@@ -492,10 +497,15 @@ __global__ __launch_bounds__(kScoreThreads) __attribute__((amdgpu_waves_per_eu(1
         compute_stage(a[u], sa[u], sc[u], xw[u], (t + u * kScoreWaves) * RM);
         return t + (u + 1) * kScoreWaves >= t_end;
       };
-      static_assert(NS == 3, "the step chain below is written for three stages");
-      while (!(step(std::integral_constant<int, 0>{}) || step(std::integral_constant<int, 1>{}) ||
-               step(std::integral_constant<int, 2>{})))
-        t += NS * kScoreWaves;
+      static_assert(NS == 2 || NS == 3, "the step chains below are written for two or three stages");
+      if constexpr (NS == 3) {
+        while (!(step(std::integral_constant<int, 0>{}) || step(std::integral_constant<int, 1>{}) ||
+                 step(std::integral_constant<int, 2>{})))
+          t += NS * kScoreWaves;
+      } else {
+        while (!(step(std::integral_constant<int, 0>{}) || step(std::integral_constant<int, 1>{})))
+          t += NS * kScoreWaves;
+      }
     }
     if (MODE == MODE_MAIN) {
       if (st_n > 0) flush();
@@ -518,7 +528,7 @@ static int launch_score(const ScoreArgs& A, int grid, hipStream_t s) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     attr = true;
   }
-  hipLaunchKernelGGL((score_kernel<CT, D, NQF, MODE>), dim3(grid), dim3(kScoreThreads), lds, s, A);
+  hipLaunchKernelGGL((score_kernel<CT, D, NQF, MODE>), dim3(grid), dim3(score_threads(CT, D)), lds, s, A);
   return check_launch();
 }
 

@@ -9,16 +9,13 @@
 
 namespace mips {
 
-constexpr int kScoreThreads = 256;  // 4 waves: one per SIMD, up to 512 registers each
-constexpr int kScoreWaves = kScoreThreads / kWave;
 constexpr int kStageCap = 512;      // staged survivors per wave
 constexpr int kStageBurst = 256;    // room kept free before each stage
-constexpr int kStageLds = kScoreWaves * kStageCap * (8 + 2);
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int kMaxSample = 8192;    // sampled 32-row blocks
 
 constexpr int kMaxSegments = 256;   // list segments per query (corpus slices of a pass)
-constexpr int kStageBytes = 16384;  // corpus bytes per wave and pipeline stage
+constexpr int kSimdStageBytes = 16384;  // corpus bytes per SIMD and pipeline stage
 constexpr int kPipeStages = 3;      // corpus stages per wave: one in use, two in flight
 constexpr int kSelCache = 6144;     // candidates the final select caches in LDS
 
@@ -26,17 +23,39 @@ constexpr int kSelCache = 6144;     // candidates the final select caches in LDS
 // (delegates of a strided block sample) and the dense pass (every score, small corpora).
 enum { MODE_MAIN = 0, MODE_SAMPLE = 1, MODE_DENSE = 2 };
 
-// Corpus blocks per pipeline stage: 16 KiB of corpus per wave and stage (at most 4
-// blocks). An int8 stage also holds 16 row scales per lane and block, so it is capped at
-// 8 KiB and 2 blocks.
-__host__ __device__ constexpr int stage_frags(int ct, int d) {
-  const int cap = ct == MIPS_INT8 ? 2 : 4;
-  const int r = (ct == MIPS_INT8 ? kStageBytes / 2 : kStageBytes) / (kFrag * d * elem_bytes(ct));
+// Corpus blocks per pipeline stage for `wps` waves per SIMD: 16 KiB of corpus per SIMD and
+// stage, split between its waves (at most 4 blocks per wave with one wave, 2 with two). An
+// int8 stage also holds 16 row scales per lane and block, so it takes half the bytes and at
+// most 2 blocks.
+__host__ __device__ constexpr int frags_for(int ct, int d, int wps) {
+  const int cap = (ct == MIPS_INT8 || wps > 1) ? 2 : 4;
+  const int bytes = kSimdStageBytes / wps / (ct == MIPS_INT8 ? 2 : 1);
+  const int r = bytes / (int)block_bytes(ct, d);
   return r < 1 ? 1 : (r > cap ? cap : r);
 }
-// LDS of a score workgroup holding 32 * nqf queries.
+// Registers a wave of the main pass needs, roughly: the stage ring, int8 row scales, two
+// fragments' accumulators, the query operand and about 60 for addresses and the epilogue.
+__host__ __device__ constexpr int score_regs(int ct, int d, int rm) {
+  const int nch = chunks_per_block(ct, d);
+  return kPipeStages * rm * nch * 4 + (ct == MIPS_INT8 ? kPipeStages * rm * 16 : 0) +
+         2 * rm * 16 + nch * 4 + 60;
+}
+// Waves per SIMD of the score kernel. With one wave, its in-order issue stalls the matrix
+// pipe whenever it waits (on an accumulator, an LDS read, a branch); a second wave fills
+// those gaps. Two waves split the 512 registers, so the second wave is used where the
+// pass fits in 256 (one 8 KiB block per stage, or two smaller ones).
+__host__ __device__ constexpr int score_wps(int ct, int d) {
+  return score_regs(ct, d, frags_for(ct, d, 2)) <= 240 ? 2 : 1;
+}
+__host__ __device__ constexpr int score_threads(int ct, int d) { return 256 * score_wps(ct, d); }
+__host__ __device__ constexpr int score_waves(int ct, int d) { return 4 * score_wps(ct, d); }
+__host__ __device__ constexpr int stage_frags(int ct, int d) {
+  return frags_for(ct, d, score_wps(ct, d));
+}
+// LDS of a score workgroup holding 32 * nqf queries: the query tile, 16 bytes of per-column
+// state per query and the survivor staging of every wave (8-byte key, 2-byte column).
 __host__ __device__ constexpr int score_lds_bytes(int ct, int d, int nqf) {
-  return kFrag * nqf * (d * elem_bytes(ct) + 16) + kStageLds;
+  return kFrag * nqf * (d * elem_bytes(ct) + 16) + score_waves(ct, d) * kStageCap * (8 + 2);
 }
 __host__ __device__ constexpr bool nqf_fits(int ct, int d, int nqf) {
   return score_lds_bytes(ct, d, nqf) <= kLdsLimit;
