@@ -381,12 +381,11 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
     };
 
     // Auxiliary epilogue. Dense pass: every score of the block goes to the query's list at
-    // its id (0 for excluded and padding rows). Sample pass: each half of the wave holds 16
-    // of a block's 32 rows, and its best eligible score is the delegate of that half-block
-    // (key 0 if none is eligible); the stage's 2 RM delegates of a query form one slot,
-    // written by the two lanes of the query's column (no cross-lane reduction). Slots are
-    // laid out del[tile / 16][query][tile % 16][2 RM], so that each query's delegates lie in
-    // runs of 16 slots.
+    // its id (0 for excluded and padding rows). Sample pass: the best eligible score of a
+    // block is its delegate (key 0 if none is eligible); each half of the wave holds 16 of the
+    // block's 32 rows, so the two lanes of a query's column combine their maxima. The stage's
+    // RM delegates of a query form one slot, laid out del[tile / 16][query][tile % 16][RM],
+    // so that each query's delegates lie in runs of 16 slots.
     auto epi_aux = [&](const f32x16_t (&acc)[RM], const float (&sc)[RM][SCN], uint32_t xwv,
                        int64_t j0, int qf) __attribute__((always_inline)) {
       const int qg = qgq(qf);
@@ -430,13 +429,14 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
             const int row = acc_row(i, lane);
             mx = ((w >> row) & 1u) ? mx : fmaxf(mx, x[i]);
           }
+          mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));  // the block's other 16 rows
           d[g] = (mx == -INFINITY) ? 0u : score_key(post(mx, sq));
           asm volatile("" : "+v"(d[g]));  // computed in uniform control flow, as above
         }
-        const int qc = qbase + qf * kFrag + (lane & 31);
-        if (qc < A.b32) {
+        const int qc = qbase + qf * kFrag + lane;
+        if (lane < kFrag && qc < A.b32) {
           const int64_t tt = j0 / RM;  // sample tile
-          uint32_t* dst = A.del + (((tt >> 4) * A.b32 + qc) * 16 + (tt & 15)) * (2 * RM) + (lane >> 5) * RM;
+          uint32_t* dst = A.del + (((tt >> 4) * A.b32 + qc) * 16 + (tt & 15)) * RM;
 #pragma unroll
           for (int g = 0; g < RM; ++g) dst[g] = d[g];
         }

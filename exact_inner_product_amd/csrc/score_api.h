@@ -85,7 +85,7 @@ struct ScoreArgs {
   int nseg;               // segments per query (one per corpus slice)
   const uint32_t* qlist;  // rescue pass: queued query ids ...
   const uint32_t* nlist;  // ... and their number (device); NULL for the full batch
-  uint32_t* del;          // sample delegates [tile/16][b32][16][2 RM]: one per half-block and query
+  uint32_t* del;          // sample delegates [tile/16][b32][16][RM]: one per block and query
   uint64_t sample_step;   // sampled block j is block (j * sample_step) >> 32
 };
 

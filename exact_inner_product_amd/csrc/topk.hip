@@ -95,9 +95,10 @@ __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict
 }
 
 // ------------------------------------------------------------ sampled threshold
-// Per query, from the G delegates (best eligible score per sampled half-block of 16 rows):
+// Per query, from the G delegates (best eligible score per sampled block of 32 rows):
 // tb, a proven lower bound of the K-th best score (at least K delegates, i.e. K distinct
-// half-blocks, reach it), and te >= tb at delegate rank r (r <= K), the estimate the main pass filters with.
+// blocks, reach it), and te >= tb at delegate rank r (r <= K), the estimate the main pass
+// filters with.
 // Both come from one histogram of the delegate scores over kThrBins equal bins of
 // [-kThrRange, kThrRange] (scores outside fall into the end bins) and a suffix scan: the
 // threshold of rank r is the lower edge of the bin holding the r-th largest delegate, less
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(kSelThreads) void sample_threshold_kernel(const uin
   const int ngroups = (ntiles + 15) / 16;
   for (int gi = t; gi < ngroups; gi += kSelThreads) {
     const u32x4_t* src = (const u32x4_t*)(del + ((int64_t)gi * b32 + q) * 16 * slot);
-    const int nvec = 16 * slot / 4;  // slot is 2, 4 or 8
+    const int nvec = 16 * slot / 4;  // slot is 1, 2 or 4
     for (int v0 = 0; v0 < nvec; v0 += 8) {
       u32x4_t v[8];
 #pragma unroll
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
   }
   const uint32_t tu = A.thr[q], tb = A.thrb[q];
   if (tu == 0u) {
-    // no sampled bound for this query (fewer than K eligible sampled half-blocks)
+    // no sampled bound for this query (fewer than K sampled blocks with an eligible row)
     fallback_scan<CT, D>(A, q, 0ull, cache, sel_buf, S, qv, &nbuf);
     return;
   }
@@ -530,7 +531,7 @@ static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt,
   p.off_del = o;
   const int64_t gmax = std::min<int64_t>(p.n32, kMaxSample);
   const int64_t tgroups = ((gmax + p.rm - 1) / p.rm + 15) / 16;
-  o = align256(o + (size_t)tgroups * 16 * p.rm * 2 * p.b32 * 4);
+  o = align256(o + (size_t)tgroups * 16 * p.rm * p.b32 * 4);
   p.off_cand = o;
   p.fixed = o;
 }
@@ -631,7 +632,7 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   A.nslices = slices_for(A.ntiles, p.nqblk);
   if ((rc = launch_score_nqf<CT, D, MODE_SAMPLE>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
   hipLaunchKernelGGL(sample_threshold_kernel, dim3(p.b), dim3(kSelThreads), 0, s, del, (int)A.ntiles,
-                     2 * p.rm, p.b32, p.b, p.k, p.rest, thr, thrb);
+                     p.rm, p.b32, p.b, p.k, p.rest, thr, thrb);
   if ((rc = check_launch())) return rc;
 
   // main pass
