@@ -59,10 +59,14 @@ class HipEvents:
 
 
 def kernel_source_hash():
+    """Hash of the main score pass's sources with comments and blank lines dropped, so that a
+    counter summary stays valid across edits that do not change the code."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        for line in open(f, encoding="utf-8"):
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -57,9 +57,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* p, int 
 // One workgroup = 4 or 8 waves (one or two per SIMD) = one corpus slice x one block of
 // 32 * NQF queries. Each wave streams stage tiles of RM 32-row blocks (16 KiB per SIMD)
 // into registers, two stages in flight, and multiplies each stage against every query
-// fragment of the block in LDS. The query-fragment loop is unrolled and software-pipelined: the MFMAs of
-// fragment qf+1 and the LDS reads of fragment qf+2's operand are issued before the
-// epilogue of fragment qf.
+// fragment of the block in LDS. The query-fragment loop is unrolled and software-pipelined:
+// the MFMAs of fragment qf+1 and the LDS reads of fragment qf+2's operand are issued
+// before the epilogue of fragment qf.
 template <int CT, int D, int NQF, int MODE>
 __global__ __launch_bounds__(score_threads(CT, D))
 __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void score_kernel(ScoreArgs A) {
@@ -95,8 +95,8 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
     }
   }
 
-  // LDS: query operand tile | global query id per column | per-wave survivor staging
-  // (composite keys, query column).
+  // LDS: query operand tile | per column: global query id, segment counter, threshold,
+  // fp8 exponent or int8 scale | per-wave survivor staging (composite keys, query column).
   int* qid_lds = (int*)(lds + (size_t)QB * D * E);
   uint32_t* seg_lds = (uint32_t*)(qid_lds + QB);  // survivors per query column (this segment)
   float* thr_lds = (float*)(seg_lds + QB);        // threshold per query column
