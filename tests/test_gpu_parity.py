@@ -474,3 +474,14 @@ def test_topk_per_item_type():
                    floor=floor_for("bf16", "bf16"))
         assert np.array_equal(v, i >= 0)
         assert np.all(types[i[i >= 0]] == t)
+
+
+@pytest.mark.parametrize("cdt,qdt,d,n,b,k", [
+    ("bf16", "bf16", 128, 120000, 9, 1024),   # K at its maximum on the sampled path
+    ("int8", "bf16", 128, 120000, 9, 1024),
+    ("bf16", "bf16", 256, 90000, 300, 64),    # one wave per SIMD, two query blocks
+    ("f32", "f32", 128, 70000, 40, 200),      # one wave per SIMD, f32 MFMA
+    ("fp8", "f32", 64, 150000, 70, 300),      # two blocks per stage with two waves
+])
+def test_sampled_path_across_geometries(cdt, qdt, d, n, b, k):
+    run_case(n, d, b, k, cdt, qdt, seed=n + d + k, excl=0.05)
