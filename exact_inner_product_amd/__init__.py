@@ -66,8 +66,8 @@ def lib() -> C.CDLL:
         L.mips_topk_workspace_size.restype = sz
         L.mips_topk_workspace_size_for.argtypes = [i32, i64, i32, i32, i32, i32, i64]
         L.mips_topk_workspace_size_for.restype = sz
-        L.mips_topk.argtypes = [p, i32, i32, p, p, i32, i64, i32, p, i32, p, p, p, sz, p]
-        L.mips_topk_ranges.argtypes = [p, i32, i32, p, p, i32, i64, i32, p, p, i32, i32, p, p, p,
+        L.mips_topk.argtypes = [p, i32, i32, p, p, i32, i64, i32, p, i64, i32, p, p, p, sz, p]
+        L.mips_topk_ranges.argtypes = [p, i32, i32, p, p, i32, i64, i32, p, i64, p, i32, i32, p, p, p,
                                        sz, p]
         L.mips_merge_topk.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p]
         L.mips_merge_interests.argtypes = [p, p, i32, i32, i32, i32, p, p, p]
@@ -189,6 +189,24 @@ def check_version(corpus: Corpus, model_version: Optional[str]) -> None:
                           f"queries from model {model_version!r}")
 
 
+def _exclude_arg(exclude: Optional[torch.Tensor], corpus: Corpus, b: int):
+    """(contiguous bitmap or None, words per query row): a 1-D bitmap [>= ceil(n/32)] is
+    shared by the batch (0 words per row); a 2-D one [b, w >= ceil(n/32)] holds one row per
+    query."""
+    if exclude is None:
+        return None, 0
+    words = (corpus.n + 31) // 32
+    if not exclude.is_cuda or exclude.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("exclude must be an int32/uint32 tensor on the GPU")
+    if exclude.dim() == 1:
+        if exclude.numel() < words:
+            raise ValueError(f"exclude holds {exclude.numel()} words, the corpus needs {words}")
+        return exclude.contiguous(), 0
+    if exclude.dim() != 2 or exclude.shape[0] != b or exclude.shape[1] < words:
+        raise ValueError(f"a per-query exclude must be [{b}, >= {words}], got {tuple(exclude.shape)}")
+    return exclude.contiguous(), int(exclude.shape[1])
+
+
 def topk(queries: torch.Tensor, corpus: Corpus, k: int, exclude: Optional[torch.Tensor] = None,
          workspace: Optional[torch.Tensor] = None,
          out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
@@ -197,8 +215,10 @@ def topk(queries: torch.Tensor, corpus: Corpus, k: int, exclude: Optional[torch.
     """Top-k by inner product: (scores float32 [b, k], ids int32 [b, k]).
 
     queries: float32 or bfloat16 [b, d] on the GPU, L2-normalised.
-    exclude: optional int32/uint32-bit bitmap [ceil(n/32)] on the GPU (bit i of the corpus
-    set => id i is never returned).
+    exclude: optional int32/uint32 bitmap on the GPU, bit i set => id i is never returned:
+    [ceil(n/32)] shared by the batch, or [b, w >= ceil(n/32)] with one row per query (a
+    per-user set, such as the history that hard-negative mining removes from each user's
+    top-k: "Two-Tower Retrieval at Industrial Scale", section "When hard is too hard").
     model_version: the user tower that produced the queries; see check_version.
     """
     check_version(corpus, model_version)
@@ -216,12 +236,10 @@ def topk(queries: torch.Tensor, corpus: Corpus, k: int, exclude: Optional[torch.
         ids = torch.empty((b, k), dtype=torch.int32, device=queries.device)
     else:
         scores, ids = out
-    if exclude is not None:
-        assert exclude.is_cuda and exclude.dtype in (torch.int32, torch.uint32)
-        assert exclude.numel() >= (corpus.n + 31) // 32
-        exclude = exclude.contiguous()
+    exclude, row_words = _exclude_arg(exclude, corpus, b)
     _check(lib().mips_topk(_ptr(queries), qc, b, _ptr(corpus.packed), _ptr(corpus.row_scale),
-                           corpus.code, corpus.n, corpus.d, _ptr(exclude), k, _ptr(scores),
+                           corpus.code, corpus.n, corpus.d, _ptr(exclude), row_words, k,
+                           _ptr(scores),
                            _ptr(ids), _ptr(workspace), workspace.numel(),
                            _stream(queries.device)), "mips_topk")
     return scores, ids
@@ -247,13 +265,11 @@ def topk_ranges(queries: torch.Tensor, corpus: Corpus, ranges, k: int,
         workspace = empty_workspace(nbytes, queries.device)
     scores = torch.empty((nr, b, k), dtype=torch.float32, device=queries.device)
     ids = torch.empty((nr, b, k), dtype=torch.int32, device=queries.device)
-    if exclude is not None:
-        assert exclude.is_cuda and exclude.dtype in (torch.int32, torch.uint32)
-        assert exclude.numel() >= (corpus.n + 31) // 32
-        exclude = exclude.contiguous()
+    exclude, row_words = _exclude_arg(exclude, corpus, b)
     _check(lib().mips_topk_ranges(_ptr(queries), qc, b, _ptr(corpus.packed),
                                   _ptr(corpus.row_scale), corpus.code, corpus.n, corpus.d,
-                                  _ptr(exclude), C.cast(rg, C.c_void_p), nr, k, _ptr(scores),
+                                  _ptr(exclude), row_words, C.cast(rg, C.c_void_p), nr, k,
+                                  _ptr(scores),
                                   _ptr(ids), _ptr(workspace), workspace.numel(),
                                   _stream(queries.device)), "mips_topk_ranges")
     return scores, ids
@@ -307,6 +323,8 @@ def topk_multi_interest(queries: torch.Tensor, corpus: Corpus, k: int,
     assert queries.dim() == 3
     b, m, d = queries.shape
     kv = k if k_per_vector is None else k_per_vector
+    if exclude is not None and exclude.dim() == 2:  # one row per user: one per vector
+        exclude = exclude.repeat_interleave(m, dim=0)
     s, i = topk(queries.reshape(b * m, d), corpus, kv, exclude, model_version=model_version)
     out_s = torch.empty((b, k), dtype=torch.float32, device=queries.device)
     out_i = torch.empty((b, k), dtype=torch.int32, device=queries.device)
@@ -324,8 +342,9 @@ def topk_types(queries: torch.Tensor, corpus: Corpus, item_types: torch.Tensor, 
     check_version(corpus, model_version)
     assert item_types.is_cuda and item_types.dtype == torch.int32 and item_types.numel() == corpus.n
     words = (corpus.n + 31) // 32
-    if exclude is not None:
-        exclude = exclude.contiguous()
+    exclude, _ = _exclude_arg(exclude, corpus, queries.shape[0])
+    if exclude is not None and exclude.dim() != 1:
+        raise ValueError("topk_types takes one exclusion bitmap for the batch")
     ws = None
     results = []
     for t in targets:

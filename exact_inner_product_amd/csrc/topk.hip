@@ -192,6 +192,7 @@ struct SelectArgs {
   const uint8_t* corpus;
   const float* row_scale;
   const uint32_t* exclude;
+  int64_t excl_rw;      // 0: one bitmap for every query; > 0: query q's row at q * excl_rw
   const uint8_t* qtile;
   const int* qexp;
   int64_t n;            // rows [lo, n) take part
@@ -248,6 +249,7 @@ __device__ void fallback_scan(const SelectArgs& A, int q, uint64_t thr, uint64_t
   }
   if (threadIdx.x == 0) *nbuf_p = 0u;
   __syncthreads();
+  const uint32_t* xq = A.exclude ? A.exclude + (int64_t)q * A.excl_rw : nullptr;
   constexpr int kRound = kSelThreads * 4;
   for (int64_t base = A.lo; base < A.n; base += kRound) {
     if (*nbuf_p + (uint32_t)kRound > (uint32_t)kSelCache) {
@@ -263,7 +265,7 @@ __device__ void fallback_scan(const SelectArgs& A, int q, uint64_t thr, uint64_t
     }
     for (int u = 0; u < 4; ++u) {
       const int64_t i = base + (int64_t)u * kSelThreads + threadIdx.x;
-      if (i >= A.n || (A.exclude && ((A.exclude[i >> 5] >> (i & 31)) & 1u))) continue;
+      if (i >= A.n || (xq && ((xq[i >> 5] >> (i & 31)) & 1u))) continue;
       float s = 0.0f;
       for (int j = 0; j < D; ++j) {
         const int64_t off = packed_offset(CT, D, i, j);
@@ -337,6 +339,14 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
   if (q >= A.b) return;
   const int t = threadIdx.x;
   const uint64_t* qlist = A.cand + (int64_t)q * A.nseg * A.capw;
+  // One bitmap per query: the score passes apply none, so the query's own row filters its
+  // candidates here (an excluded candidate reads as key 0, below every real key).
+  const bool own = A.excl_rw > 0;
+  const uint32_t* xrow = own ? A.exclude + (int64_t)q * A.excl_rw : nullptr;
+  auto excluded = [&](uint64_t key) {
+    const uint32_t id = composite_id(key);
+    return ((xrow[id >> 5] >> (id & 31)) & 1u) != 0u;
+  };
   int64_t c;
   bool cached;
   if (A.dense_count > 0) {
@@ -348,7 +358,8 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
     __syncthreads();
     uint32_t mine = 0u;
     for (int64_t i = t; i < c; i += kSelThreads) {
-      const uint64_t key = qlist[i];
+      uint64_t key = qlist[i];
+      if (own && key != 0ull && excluded(key)) key = 0ull;
       if (cached) cache[i] = key;
       mine += key != 0ull;
     }
@@ -362,7 +373,10 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
         if (c > r) sel = select_top(get, c, r, S);
         gather_sort(get, c, r, sel, sel_buf, &S.hist[0]);
       } else {
-        auto get = [&](int64_t i) { return qlist[i]; };
+        auto get = [&](int64_t i) {
+          const uint64_t key = qlist[i];
+          return own && key != 0ull && excluded(key) ? 0ull : key;
+        };
         if (c > r) sel = select_top(get, c, r, S);
         gather_sort(get, c, r, sel, sel_buf, &S.hist[0]);
       }
@@ -395,11 +409,30 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
     }
     return qlist[(int64_t)lo * A.capw + (i - segoff[lo])];
   };
+  auto atx = [&](int64_t i) {
+    const uint64_t key = at(i);
+    return own && excluded(key) ? 0ull : key;
+  };
+  // eligible: the stored candidates the query's own bitmap keeps (all without one)
+  int64_t eligible = stored;
+  if (own) {
+    if (t == 0) nbuf = 0u;
+    __syncthreads();
+    const uint64_t* seg = qlist + (int64_t)t * A.capw;
+    uint32_t keep = 0u;
+    for (uint32_t i = 0; i < mine; ++i) keep += excluded(seg[i]) ? 0u : 1u;
+    atomicAdd(&nbuf, keep);
+    __syncthreads();
+    eligible = nbuf;
+  }
   __syncthreads();
   const bool over = stored < c || A.ovf[q] != 0u;
-  const bool shortfall = !over && c < A.k && tu > tb;
+  // Fewer than k candidates: final when the threshold was the proven bound. With one
+  // bitmap per query the sample pass applied none, so its bound is not proven and a short
+  // list is always rescued; at the bound itself only the exact rescan is left.
+  const bool shortfall = !over && eligible < A.k && (tu > tb || own);
   if (over || shortfall) {
-    if (round > 0) {
+    if (round > 0 || (shortfall && tu == tb)) {
       fallback_scan<CT, D>(A, q, 0ull, cache, sel_buf, S, qv, &nbuf);
       return;
     }
@@ -408,8 +441,8 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
     uint32_t nt = tb;
     if (over) {
       nt = tu;
-      if (stored >= A.k) {
-        const uint32_t kth = (uint32_t)(select_top(at, stored, A.k, S).prefix >> 32);
+      if (eligible >= A.k) {
+        const uint32_t kth = (uint32_t)(select_top(atx, stored, A.k, S).prefix >> 32);
         nt = kth > nt ? kth : nt;
       }
     }
@@ -421,7 +454,7 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
     }
     return;
   }
-  const int r = (int)min<int64_t>(c, A.k);
+  const int r = (int)min<int64_t>(eligible, A.k);
   if (r > 0) {
     if (c <= kSelCache) {
       // each thread copies its own segment, 8 entries per round trip
@@ -432,7 +465,7 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
         for (int e = 0; e < 8; ++e) v[e] = i0 + e < mine ? seg[i0 + e] : 0ull;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (i0 + e < mine) cache[segoff[t] + i0 + e] = v[e];
+          if (i0 + e < mine) cache[segoff[t] + i0 + e] = own && excluded(v[e]) ? 0ull : v[e];
       }
       __syncthreads();
       auto get = [&](int64_t i) { return cache[i]; };
@@ -440,8 +473,9 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
       if (c > r) sel = select_top(get, c, r, S);
       gather_sort(get, c, r, sel, sel_buf, &S.hist[0]);
     } else {
-      const Sel64 sel = select_top(at, c, r, S);
-      gather_sort(at, c, r, sel, sel_buf, &S.hist[0]);
+      Sel64 sel{0ull, 0ull};
+      if (c > r) sel = select_top(atx, c, r, S);
+      gather_sort(atx, c, r, sel, sel_buf, &S.hist[0]);
     }
   }
   write_out(A, q, sel_buf, r);
@@ -450,6 +484,7 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
 // ------------------------------------------------------------------- planning
 struct Plan {
   int b, b32, k, d, qdt, cdt;
+  int64_t excl_rw;           // exclusion words per query (0: one shared bitmap)
   int64_t n, n32, lo, blk0;  // rows [lo, n); n32 blocks from blk0
   int rm, nqf, nqblk, G, rest, nseg;
   bool dense;
@@ -487,6 +522,7 @@ static int estimate_rank(int64_t n32, int G, int k) {
 static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt, int64_t capq,
                       int64_t lo = 0) {
   p.b = b;
+  p.excl_rw = 0;
   p.b32 = (b + 31) / 32 * 32;
   p.k = k;
   p.d = d;
@@ -563,7 +599,9 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   ScoreArgs A{};
   A.corpus = (const uint8_t*)corpus;
   A.row_scale = row_scale;
-  A.exclude = exclude;
+  // the score passes apply a shared bitmap as they read the corpus; one bitmap per query
+  // is applied to each query's candidates by the final select
+  A.exclude = p.excl_rw > 0 ? nullptr : exclude;
   A.qtile = qtile;
   A.qexp = qexp;
   A.n = p.n;
@@ -592,6 +630,7 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   S.corpus = (const uint8_t*)corpus;
   S.row_scale = row_scale;
   S.exclude = exclude;
+  S.excl_rw = p.excl_rw;
   S.qtile = qtile;
   S.qexp = qexp;
   S.n = p.n;
@@ -710,16 +749,18 @@ size_t mips_topk_workspace_size_for(int32_t b, int64_t n, int32_t d, int32_t k, 
 
 int mips_topk(const void* queries, int32_t query_dtype, int32_t b, const void* corpus,
               const float* row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
-              const uint32_t* exclude, int32_t k, float* out_scores, int32_t* out_ids,
-              void* workspace, size_t workspace_bytes, void* stream) {
+              const uint32_t* exclude, int64_t exclude_row_words, int32_t k, float* out_scores,
+              int32_t* out_ids, void* workspace, size_t workspace_bytes, void* stream) {
   const int64_t whole[2] = {0, n};
   return mips_topk_ranges(queries, query_dtype, b, corpus, row_scale, corpus_dtype, n, d, exclude,
-                          whole, 1, k, out_scores, out_ids, workspace, workspace_bytes, stream);
+                          exclude_row_words, whole, 1, k, out_scores, out_ids, workspace,
+                          workspace_bytes, stream);
 }
 
 int mips_topk_ranges(const void* queries, int32_t query_dtype, int32_t b, const void* corpus,
                      const float* row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
-                     const uint32_t* exclude, const int64_t* ranges, int32_t nranges, int32_t k,
+                     const uint32_t* exclude, int64_t exclude_row_words, const int64_t* ranges,
+                     int32_t nranges, int32_t k,
                      float* out_scores, int32_t* out_ids, void* workspace, size_t workspace_bytes,
                      void* stream) {
   if (!queries || !corpus || !out_scores || !out_ids || !workspace || !ranges)
@@ -727,6 +768,8 @@ int mips_topk_ranges(const void* queries, int32_t query_dtype, int32_t b, const 
   const int rc0 = mips::validate_topk(query_dtype, b, corpus_dtype, n, d, k);
   if (rc0 != MIPS_OK) return rc0;
   if (nranges < 1) return MIPS_ERR_INVALID_ARG;
+  if (exclude_row_words < 0 || (exclude_row_words > 0 && (!exclude || exclude_row_words < (n + 31) / 32)))
+    return MIPS_ERR_INVALID_ARG;
   for (int r = 0; r < nranges; ++r)
     if (ranges[2 * r] < 0 || ranges[2 * r] >= ranges[2 * r + 1] || ranges[2 * r + 1] > n)
       return MIPS_ERR_INVALID_ARG;
@@ -747,6 +790,7 @@ int mips_topk_ranges(const void* queries, int32_t query_dtype, int32_t b, const 
   uint8_t* ws = (uint8_t*)workspace;
   for (int r = 0; r < nranges; ++r) {
     mips::make_plan(p, b, ranges[2 * r + 1], d, k, query_dtype, corpus_dtype, capq, ranges[2 * r]);
+    p.excl_rw = exclude_row_words;
     float* os = out_scores + (int64_t)r * b * k;
     int32_t* oi = out_ids + (int64_t)r * b * k;
     int rc;

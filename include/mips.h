@@ -156,8 +156,16 @@ MIPS_API size_t mips_topk_workspace_size_for(int32_t b, int64_t n, int32_t d, in
  *                branch of `RecsysTwoTowerModel.forward` does; the int32 dot product of
  *                the codes is scaled by the row scale, then by the query scale).
  *   n            1 .. 2^31 - 64.  d: as mips_prepare_corpus.
- *   exclude      device or NULL: uint32 [ceil(n/32)]; bit (i & 31) of word (i >> 5) set
- *                means id i is never returned. One bitmap serves the whole batch.
+ *   exclude      device or NULL: bit (i & 31) of word (i >> 5) set means id i is never
+ *                returned. With exclude_row_words == 0, one uint32 [ceil(n/32)] bitmap
+ *                serves the whole batch; with exclude_row_words = w > 0, query q's own
+ *                bitmap starts at word q * w (uint32 [b, w], w >= ceil(n/32)): a
+ *                per-user set, such as the engagement history that hard-negative
+ *                mining removes from each user's retrieved top-k ("Two-Tower Retrieval
+ *                at Industrial Scale", section "When hard is too hard"). The sampled thresholds ignore per-query bitmaps, so
+ *                a query whose own bitmap removes many of its best rows is rescued (exact,
+ *                slower).
+ *   exclude_row_words  0 or >= ceil(n/32), as above; > 0 needs a non-NULL exclude.
  *   k            1 .. MIPS_K_MAX.
  *   out_scores   device float [b, k]; out_ids device int32 [b, k]. Row q holds query q's
  *                min(k, eligible) best (score, id) pairs, score descending then id
@@ -170,12 +178,14 @@ MIPS_API size_t mips_topk_workspace_size_for(int32_t b, int64_t n, int32_t d, in
  *                one stream.
  * Errors: INVALID_ARG (NULL where a buffer is required, b/n/k out of range, fp8 or int8
  * without row_scale, misalignment), UNSUPPORTED (d, k > MIPS_K_MAX, dtype pair), WORKSPACE
- * (workspace_bytes too small), HIP (a launch failed).
+ * (workspace_bytes too small), HIP (a launch failed); INVALID_ARG also for
+ * exclude_row_words < 0, or > 0 with a NULL exclude or below ceil(n/32).
  */
 MIPS_API int mips_topk(const void *queries, int32_t query_dtype, int32_t b, const void *corpus,
               const float *row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
-              const uint32_t *exclude, int32_t k, float *out_scores, int32_t *out_ids,
-              void *workspace, size_t workspace_bytes, void *stream);
+              const uint32_t *exclude, int64_t exclude_row_words, int32_t k,
+              float *out_scores, int32_t *out_ids, void *workspace, size_t workspace_bytes,
+              void *stream);
 
 /*
  * mips_topk_ranges -- mips_topk restricted to id ranges, one result set per range: for
@@ -196,7 +206,8 @@ MIPS_API int mips_topk(const void *queries, int32_t query_dtype, int32_t b, cons
  */
 MIPS_API int mips_topk_ranges(const void *queries, int32_t query_dtype, int32_t b, const void *corpus,
                               const float *row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
-                              const uint32_t *exclude, const int64_t *ranges, int32_t nranges,
+                              const uint32_t *exclude, int64_t exclude_row_words,
+                              const int64_t *ranges, int32_t nranges,
                               int32_t k, float *out_scores, int32_t *out_ids, void *workspace,
                               size_t workspace_bytes, void *stream);
 

@@ -69,10 +69,10 @@ def test_workspace_size(L):
 
 
 def _topk(L, q=0x1000, qdt=BF16, b=4, corpus=0x2000, scale=None, cdt=BF16, n=1000, d=128,
-          excl=None, k=10, out_s=0x3000, out_i=0x4000, ws=0x10000, wsb=1 << 30):
+          excl=None, rw=0, k=10, out_s=0x3000, out_i=0x4000, ws=0x10000, wsb=1 << 30):
     vp = lambda x: None if x is None else C.c_void_p(x)
-    return L.mips_topk(vp(q), qdt, b, vp(corpus), vp(scale), cdt, n, d, vp(excl), k, vp(out_s),
-                       vp(out_i), vp(ws), wsb, None)
+    return L.mips_topk(vp(q), qdt, b, vp(corpus), vp(scale), cdt, n, d, vp(excl), rw, k,
+                       vp(out_s), vp(out_i), vp(ws), wsb, None)
 
 
 def test_topk_argument_validation(L):
@@ -94,6 +94,11 @@ def test_topk_argument_validation(L):
     assert _topk(L, q=0x1002) == INVALID
     assert _topk(L, wsb=1024) == WORKSPACE
     assert _topk(L, n=(1 << 31)) == INVALID
+    # per-query exclusion rows: at least ceil(n/32) words each, and a bitmap to read
+    assert _topk(L, excl=0x6000, rw=-1) == INVALID
+    assert _topk(L, excl=None, rw=32) == INVALID
+    assert _topk(L, excl=0x6000, rw=31) == INVALID      # n = 1000 needs 32 words
+    assert _topk(L, excl=0x6002, rw=32) == INVALID      # misaligned
 
 
 def test_normalize_and_prepare_validation(L):
@@ -188,7 +193,7 @@ def test_topk_ranges_rejects_bad_ranges_before_launch(L):
 
     def call(rg, nr=None):
         arr = (C.c_int64 * max(1, len(rg)))(*rg) if rg else None
-        return L.mips_topk_ranges(vp(0x1000), BF16, 4, vp(0x2000), None, BF16, 1000, 128, None,
+        return L.mips_topk_ranges(vp(0x1000), BF16, 4, vp(0x2000), None, BF16, 1000, 128, None, 0,
                                   None if arr is None else C.cast(arr, vp),
                                   len(rg) // 2 if nr is None else nr, 10, vp(0x3000), vp(0x4000),
                                   vp(0x5000), 1 << 30, None)

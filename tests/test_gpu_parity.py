@@ -485,3 +485,114 @@ def test_topk_per_item_type():
 ])
 def test_sampled_path_across_geometries(cdt, qdt, d, n, b, k):
     run_case(n, d, b, k, cdt, qdt, seed=n + d + k, excl=0.05)
+
+
+# ------------------------------------------------------- one bitmap per query
+def _per_query_masks(n, b, rng, o_i=None):
+    """[b, words] bitmaps with a different shape per query: random fractions from 0 to 30%,
+    one empty row, one row that keeps only 30 ids (fewer than k: padded), and, given the
+    oracle's unmasked top ids o_i, rows that remove each query's own best ids (the main pass
+    then finds fewer than k eligible candidates above its estimate)."""
+    words = (n + 31) // 32
+    rows = np.zeros((b, words), np.uint32)
+    for qi in range(b):
+        kind = qi % 5
+        if kind == 0:
+            ids = np.empty(0, np.int64)
+        elif kind == 1:
+            keep = rng.choice(n, 30, replace=False)
+            ids = np.setdiff1d(np.arange(n), keep)
+        elif kind == 2 and o_i is not None:
+            ids = o_i[qi][o_i[qi] >= 0]
+        else:
+            ids = rng.choice(n, int(n * rng.uniform(0.02, 0.3)), replace=False)
+        rows[qi] = bitmap_from_ids(ids, n)
+    return rows
+
+
+def _check_per_query(s, i, rows, q_or, qdt, c_or, cdt, sc_or, n, k):
+    ids_all = np.arange(n)
+    for qi in range(rows.shape[0]):
+        bm = rows[qi]
+        o_s, o_i = oracle.topk(q_or[qi:qi + 1], qdt, c_or, cdt, k, row_scale=sc_or, exclude=bm)
+        excluded = set(ids_all[((bm[ids_all >> 5] >> (ids_all & 31).astype(np.uint32)) & 1) == 1].tolist())
+        check_topk(s[qi:qi + 1], i[qi:qi + 1], o_s, o_i, q_or[qi:qi + 1], qdt, c_or, cdt, sc_or,
+                   excluded, n, TOL[cdt], floor=floor_for(cdt, qdt))
+
+
+@pytest.mark.parametrize("cdt,qdt,d,n,b,k", [
+    ("bf16", "bf16", 128, 60_000, 10, 100),    # every block sampled: the bound is exact rank k
+    ("fp8", "bf16", 256, 400_000, 10, 200),   # a strided sample: estimate above the bound
+    ("int8", "bf16", 64, 3_000, 6, 50),       # dense pass
+    ("f32", "f32", 64, 20_000, 7, 500),       # dense pass, k above some rows' eligible count
+    ("bf16", "f32", 64, 1_000_000, 5, 1000),  # k at its maximum
+])
+def test_per_query_exclusion_matches_oracle(cdt, qdt, d, n, b, k):
+    """One bitmap per query (a per-user history): each row of the result is the oracle's
+    top-k of that query with its own bitmap, including rows whose bitmap removes the query's
+    own best items and rows left with fewer than k eligible ids."""
+    dev = _dev()
+    w = _workload(n, d, b, k, cdt, qdt, 71 + d)
+    x, qraw = w.corpus(), w.queries()
+    corpus, q = _gpu_inputs(w, x, qraw, dev)
+    c_or, sc_or = oracle.prepare(x, cdt)
+    q_or, _ = oracle.prepare(qraw, qdt)
+    _, top = oracle.topk(q_or, qdt, c_or, cdt, min(k, 300), row_scale=sc_or)
+    rows = _per_query_masks(n, b, np.random.default_rng(71), top)
+    print(f"case per-query n={n} d={d} b={b} k={k} {cdt}/{qdt}", flush=True)
+    s, i = mips.topk(q, corpus, k, torch.from_numpy(rows.view(np.int32)).to(dev))
+    torch.cuda.synchronize()
+    _check_per_query(s.cpu().numpy(), i.cpu().numpy(), rows, q_or, qdt, c_or, cdt, sc_or, n, k)
+
+
+def test_per_query_rows_equal_to_shared_bitmap_match_it():
+    """A per-query bitmap whose rows all equal the shared bitmap gives the shared result,
+    bitwise (the same scores reach the same selection either way); a row stride wider than
+    the corpus needs is honoured."""
+    dev = _dev()
+    n, d, b, k = 1_000_000, 128, 16, 100
+    w = _workload(n, d, b, k, "bf16", "bf16", 72, excl=0.05)
+    corpus, q = _gpu_inputs(w, w.corpus(), w.queries(), dev)
+    bm = w.exclude_bitmap()
+    s0, i0 = _scores_ids(q, corpus, k, _excl_tensor(bm, dev))
+    wide = np.full((b, bm.size + 5), 0xFFFFFFFF, np.uint32)  # padding words past the corpus
+    wide[:, :bm.size] = bm
+    s1, i1 = _scores_ids(q, corpus, k, torch.from_numpy(wide.view(np.int32)).to(dev))
+    assert np.array_equal(i0, i1) and np.array_equal(s0.view(np.uint32), s1.view(np.uint32))
+
+
+def test_per_query_exclusion_with_ranges_and_interests():
+    """Per-query bitmaps combine with id ranges (each range's top-k of the query's
+    eligible rows inside it) and with multi-interest users (one row per user, shared by
+    the user's vectors)."""
+    dev = _dev()
+    n, d, b, k, m = 40_000, 64, 6, 60, 2
+    w = _workload(n, d, b * m, k, "bf16", "bf16", 73)
+    x, qraw = w.corpus(), w.queries()
+    corpus, q = _gpu_inputs(w, x, qraw, dev)
+    c_or, sc_or = oracle.prepare(x, "bf16")
+    q_or, _ = oracle.prepare(qraw, "bf16")
+    rng = np.random.default_rng(73)
+    rows = _per_query_masks(n, b * m, rng)
+    ranges = [(0, n), (100, 5000), (n // 2, n)]
+    s, i = mips.topk_ranges(q, corpus, ranges, k, torch.from_numpy(rows.view(np.int32)).to(dev))
+    torch.cuda.synchronize()
+    s, i = s.cpu().numpy(), i.cpu().numpy()
+    for r, (lo, hi) in enumerate(ranges):
+        print(f"per-query range {r}: [{lo}, {hi})", flush=True)
+        rr = np.stack([_range_bitmap(n, lo, hi, rows[qi]) for qi in range(b * m)])
+        _check_per_query(s[r], i[r], rr, q_or, "bf16", c_or, "bf16", None, n, k)
+    # multi-interest: user u's row applies to each of its m vectors
+    urows = rows[::m]
+    su, iu = mips.topk_multi_interest(q.reshape(b, m, d), corpus, k,
+                                      torch.from_numpy(urows.view(np.int32)).to(dev))
+    torch.cuda.synchronize()
+    su, iu = su.cpu().numpy(), iu.cpu().numpy()
+    for u in range(b):
+        o_s, o_i = oracle.maxsim_topk(q_or[u * m:(u + 1) * m].reshape(1, m, d), "bf16", c_or,
+                                      "bf16", k, exclude=urows[u])
+        gi = iu[u][iu[u] >= 0]
+        assert gi.size == (o_i[0] >= 0).sum()
+        ex = ((urows[u][gi >> 5] >> (gi & 31).astype(np.uint32)) & 1) == 1
+        assert not ex.any(), "an id the user's bitmap excludes was returned"
+        assert np.abs(su[u][: gi.size] - o_s[0][: gi.size].astype(np.float32)).max() <= TOL["bf16"]
