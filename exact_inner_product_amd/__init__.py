@@ -25,9 +25,11 @@ K_MAX = 1024
 EXPORTS = (
     "mips_corpus_bytes", "mips_scale_count", "mips_l2_normalize", "mips_prepare_corpus",
     "mips_topk_workspace_size", "mips_topk_workspace_size_for", "mips_topk", "mips_topk_ranges",
+    "mips_topk_masks_workspace_size", "mips_topk_masks",
     "mips_merge_topk", "mips_merge_interests", "mips_type_bitmap", "mips_set_timing_events", "mips_status_string", "mips_last_hip_error",
 )
 MERGE_MAX_LISTS = 64
+MAX_MASKS = 4  # result sets of one mips_topk_masks pass
 
 
 class MipsError(RuntimeError):
@@ -69,6 +71,10 @@ def lib() -> C.CDLL:
         L.mips_topk.argtypes = [p, i32, i32, p, p, i32, i64, i32, p, i64, i32, p, p, p, sz, p]
         L.mips_topk_ranges.argtypes = [p, i32, i32, p, p, i32, i64, i32, p, i64, p, i32, i32, p, p, p,
                                        sz, p]
+        L.mips_topk_masks_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32, i64]
+        L.mips_topk_masks_workspace_size.restype = sz
+        L.mips_topk_masks.argtypes = [p, i32, i32, p, p, i32, i64, i32, p, i32, i64, i32, p, p, p,
+                                      sz, p]
         L.mips_merge_topk.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p]
         L.mips_merge_interests.argtypes = [p, p, i32, i32, i32, i32, p, p, p]
         L.mips_type_bitmap.argtypes = [p, i64, i32, p, p, p]
@@ -77,6 +83,7 @@ def lib() -> C.CDLL:
         L.mips_status_string.restype = C.c_char_p
         L.mips_last_hip_error.argtypes = []
         for f in (L.mips_l2_normalize, L.mips_prepare_corpus, L.mips_topk, L.mips_topk_ranges,
+                  L.mips_topk_masks,
                   L.mips_merge_topk, L.mips_merge_interests, L.mips_type_bitmap,
                   L.mips_set_timing_events, L.mips_last_hip_error):
             f.restype = C.c_int
@@ -174,6 +181,15 @@ def workspace_size(b: int, n: int, d: int, k: int, query_dtype: str, corpus_dtyp
     if candidates_per_query is None:
         return int(lib().mips_topk_workspace_size(b, n, d, k, qc, cc))
     return int(lib().mips_topk_workspace_size_for(b, n, d, k, qc, cc, candidates_per_query))
+
+
+def masks_workspace_size(b: int, n: int, d: int, k: int, query_dtype: str, corpus_dtype: str,
+                         nmasks: int, candidates_per_list: Optional[int] = None) -> int:
+    """Workspace bytes of mips_topk_masks: the default candidate capacity per (mask, query)
+    list, or at least `candidates_per_list`."""
+    qc, cc = DTYPE_CODES[query_dtype], DTYPE_CODES[corpus_dtype]
+    return int(lib().mips_topk_masks_workspace_size(b, n, d, k, qc, cc, nmasks,
+                                                    candidates_per_list or 0))
 
 
 def empty_workspace(nbytes: int, device="cuda") -> torch.Tensor:
@@ -333,33 +349,62 @@ def topk_multi_interest(queries: torch.Tensor, corpus: Corpus, k: int,
     return out_s, out_i
 
 
+def topk_masks(queries: torch.Tensor, corpus: Corpus, masks: torch.Tensor, k: int,
+               workspace: Optional[torch.Tensor] = None, model_version: Optional[str] = None
+               ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Several result sets from one pass over the corpus: masks int32/uint32 [t, w] on the
+    GPU (1 <= t <= MAX_MASKS, w >= ceil(n/32)), bit i of row r set => id i is not in result
+    set r. Returns (scores float32 [t, b, k], ids int32 [t, b, k])."""
+    check_version(corpus, model_version)
+    assert queries.is_cuda and queries.dim() == 2 and queries.shape[1] == corpus.d
+    words = (corpus.n + 31) // 32
+    if not masks.is_cuda or masks.dtype not in (torch.int32, torch.uint32) or masks.dim() != 2:
+        raise ValueError("masks must be a 2-D int32/uint32 tensor on the GPU")
+    nm = masks.shape[0]
+    if not 1 <= nm <= MAX_MASKS or masks.shape[1] < words:
+        raise ValueError(f"masks must be [1..{MAX_MASKS}, >= {words}], got {tuple(masks.shape)}")
+    queries, masks = queries.contiguous(), masks.contiguous()
+    b = queries.shape[0]
+    qc = _qcode(queries)
+    if workspace is None:
+        nbytes = lib().mips_topk_masks_workspace_size(b, corpus.n, corpus.d, k, qc, corpus.code, nm, 0)
+        if nbytes == 0:
+            raise MipsError(2, "mips_topk_masks_workspace_size")
+        workspace = empty_workspace(nbytes, queries.device)
+    scores = torch.empty((nm, b, k), dtype=torch.float32, device=queries.device)
+    ids = torch.empty((nm, b, k), dtype=torch.int32, device=queries.device)
+    _check(lib().mips_topk_masks(_ptr(queries), qc, b, _ptr(corpus.packed), _ptr(corpus.row_scale),
+                                 corpus.code, corpus.n, corpus.d, _ptr(masks), nm, masks.shape[1],
+                                 k, _ptr(scores), _ptr(ids), _ptr(workspace), workspace.numel(),
+                                 _stream(queries.device)), "mips_topk_masks")
+    return scores, ids
+
+
 def topk_types(queries: torch.Tensor, corpus: Corpus, item_types: torch.Tensor, targets, k: int,
                exclude: Optional[torch.Tensor] = None, return_validity: bool = False,
                model_version: Optional[str] = None):
     """One top-k per target item type: a tuple with, per target, (ids [b, k], scores [b, k])
     or (ids, scores, validity) with return_validity. Items of other types are never returned,
-    so validity is ids >= 0 (padding marks a type with fewer than k eligible items)."""
+    so validity is ids >= 0 (padding marks a type with fewer than k eligible items). Up to
+    MAX_MASKS types share one pass over the corpus (mips_topk_masks)."""
     check_version(corpus, model_version)
     assert item_types.is_cuda and item_types.dtype == torch.int32 and item_types.numel() == corpus.n
     words = (corpus.n + 31) // 32
     exclude, _ = _exclude_arg(exclude, corpus, queries.shape[0])
     if exclude is not None and exclude.dim() != 1:
         raise ValueError("topk_types takes one exclusion bitmap for the batch")
-    ws = None
+    targets = [int(t) for t in targets]
     results = []
-    for t in targets:
-        bm = torch.empty(words, dtype=torch.int32, device=item_types.device)
-        _check(lib().mips_type_bitmap(_ptr(item_types.contiguous()), corpus.n, int(t),
-                                      _ptr(exclude), _ptr(bm), _stream(item_types.device)),
-               "mips_type_bitmap")
-        if ws is None:
-            nbytes = lib().mips_topk_workspace_size(queries.shape[0], corpus.n, corpus.d, k,
-                                                    _qcode(queries), corpus.code)
-            if nbytes == 0:
-                raise MipsError(2, "mips_topk_workspace_size")
-            ws = empty_workspace(nbytes, queries.device)
-        s, i = topk(queries, corpus, k, bm, workspace=ws, model_version=model_version)
-        results.append((i, s, i >= 0) if return_validity else (i, s))
+    for g0 in range(0, len(targets), MAX_MASKS):
+        group = targets[g0:g0 + MAX_MASKS]
+        bms = torch.empty((len(group), words), dtype=torch.int32, device=item_types.device)
+        for r, t in enumerate(group):
+            _check(lib().mips_type_bitmap(_ptr(item_types.contiguous()), corpus.n, t,
+                                          _ptr(exclude), _ptr(bms[r]), _stream(item_types.device)),
+                   "mips_type_bitmap")
+        s, i = topk_masks(queries, corpus, bms, k, model_version=model_version)
+        for r in range(len(group)):
+            results.append((i[r], s[r], i[r] >= 0) if return_validity else (i[r], s[r]))
     return tuple(results)
 
 

@@ -55,12 +55,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* p, int 
 }
 
 // One workgroup = 4 or 8 waves (one or two per SIMD) = one corpus slice x one block of
-// 32 * NQF queries. Each wave streams stage tiles of RM 32-row blocks (16 KiB per SIMD)
+// 32 * NQF queries. With NT > 0 (a multi-mask pass) every score is tested against up to NT
+// masks, each with its own threshold and candidate list per query. Each wave streams stage tiles of RM 32-row blocks (16 KiB per SIMD)
 // into registers, two stages in flight, and multiplies each stage against every query
 // fragment of the block in LDS. The query-fragment loop is unrolled and software-pipelined:
 // the MFMAs of fragment qf+1 and the LDS reads of fragment qf+2's operand are issued
 // before the epilogue of fragment qf.
-template <int CT, int D, int NQF, int MODE>
+template <int CT, int D, int NQF, int MODE, int NT>
 __global__ __launch_bounds__(score_threads(CT, D))
 __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void score_kernel(ScoreArgs A) {
   constexpr int kScoreThreads = score_threads(CT, D);
@@ -74,6 +75,7 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
   constexpr int SCN = CT == MIPS_INT8 ? 16 : 1;
   constexpr int64_t BLK = block_bytes(CT, D);
   constexpr int QB = kFrag * NQF;
+  constexpr int NTS = NT > 0 ? NT : 1;  // survivor counters per query column
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int lane = threadIdx.x & 63;
@@ -95,14 +97,16 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
     }
   }
 
-  // LDS: query operand tile | per column: global query id, segment counter, threshold,
-  // fp8 exponent or int8 scale | per-wave survivor staging (composite keys, query column).
+  // LDS: query operand tile | per column: global query id, segment counter(s), threshold,
+  // fp8 exponent or int8 scale | multi-mask: threshold per column and mask | per-wave
+  // survivor staging (composite keys, query column; column * NT + mask with masks).
   int* qid_lds = (int*)(lds + (size_t)QB * D * E);
-  uint32_t* seg_lds = (uint32_t*)(qid_lds + QB);  // survivors per query column (this segment)
-  float* thr_lds = (float*)(seg_lds + QB);        // threshold per query column
+  uint32_t* seg_lds = (uint32_t*)(qid_lds + QB);  // survivors per query column (and mask)
+  float* thr_lds = (float*)(seg_lds + QB * NTS);  // threshold per query column (lowest mask's)
   int* sexp_lds = (int*)(thr_lds + QB);           // fp8 exponent / int8 scale per column
-  uint64_t* st_key = (uint64_t*)(sexp_lds + QB) + wave * kStageCap;
-  uint16_t* st_q = (uint16_t*)((uint64_t*)(sexp_lds + QB) + kScoreWaves * kStageCap) + wave * kStageCap;
+  float* thrt_lds = (float*)(sexp_lds + QB);      // [QB][NT] thresholds of a multi-mask pass
+  uint64_t* st_key = (uint64_t*)(sexp_lds + QB + QB * NT) + wave * kStageCap;
+  uint16_t* st_q = (uint16_t*)((uint64_t*)(sexp_lds + QB + QB * NT) + kScoreWaves * kStageCap) + wave * kStageCap;
 
   const int64_t t_begin = (int64_t)slice * A.ntiles / A.nslices;
   const int64_t t_end = (int64_t)(slice + 1) * A.ntiles / A.nslices;
@@ -139,11 +143,15 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
         qid_lds[i] = qbase + i < A.b ? qbase + i : -1;
         seg_lds[i] = 0u;
       }
+      if constexpr (NT > 0)
+        for (int i = QB + threadIdx.x; i < QB * NT; i += kScoreThreads) seg_lds[i] = 0u;
     } else {
       for (int i = threadIdx.x; i < QB; i += kScoreThreads) {
         qid_lds[i] = qbase + i < nq_total ? (int)A.qlist[qbase + i] : -1;
         seg_lds[i] = 0u;
       }
+      if constexpr (NT > 0)
+        for (int i = QB + threadIdx.x; i < QB * NT; i += kScoreThreads) seg_lds[i] = 0u;
       __syncthreads();
       // gather the queued queries' operand rows: 16-byte slot s of chunk c of column
       // fragment qf comes from slot (q & 31) + 32 (s >> 5) of the same chunk of q's block
@@ -156,7 +164,8 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
           v[u] = u32x4_t{0u, 0u, 0u, 0u};
           if (i0 + u < PER && i < NV) {
             const int s = i & 63, c = (i >> 6) % NCH, qf = (i >> 6) / NCH;
-            const int q = qid_lds[qf * kFrag + (s & 31)];
+            const int qv = qid_lds[qf * kFrag + (s & 31)];
+            const int q = (NT > 0 && qv >= 0) ? qv % A.b : qv;  // a masked pass queues (mask, query)
             if (q >= 0)
               v[u] = *(const u32x4_t*)(A.qtile + (int64_t)(q >> 5) * BLK + c * kChunkBytes +
                                        ((q & 31) + 32 * (s >> 5)) * 16);
@@ -176,13 +185,27 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
     for (int i = threadIdx.x; i < QB; i += kScoreThreads) {
       const int qg = qid_lds[i];
       float T = INFINITY;
-      if (MODE == MODE_MAIN && qg >= 0) {
+      if constexpr (NT > 0) {
+        // one threshold per mask (a rescued column scores its own mask only); the column's
+        // own threshold, the lowest of them, gates the fast path
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          float Tt = INFINITY;
+          if (MODE == MODE_MAIN && qg >= 0 && t < A.nmask && (!rescue || qg / A.b == t)) {
+            const uint32_t k = A.thr[rescue ? qg : t * A.b + qg];
+            if (k != 0u) Tt = key_threshold(k);
+          }
+          thrt_lds[i * NT + t] = Tt;
+          T = fminf(T, Tt);
+        }
+      } else if (MODE == MODE_MAIN && qg >= 0) {
         const uint32_t k = A.thr[qg];
         if (k != 0u) T = key_threshold(k);
       }
       thr_lds[i] = T;
       int e = CT == MIPS_INT8 ? __float_as_int(1.0f) : 127;
-      if ((CT == MIPS_FP8_E4M3 || CT == MIPS_INT8) && qg >= 0) e = A.qexp[qg];
+      if ((CT == MIPS_FP8_E4M3 || CT == MIPS_INT8) && qg >= 0)
+        e = A.qexp[(NT > 0 && rescue) ? qg % A.b : qg];
       sexp_lds[i] = e;
     }
     __syncthreads();
@@ -196,6 +219,11 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
       return CT == MIPS_INT8 ? __int_as_float(sexp_lds[qf * kFrag + (lane & 31)]) : 1.0f;
     };
     auto qgq = [&](int qf) __attribute__((always_inline)) { return qid_lds[qf * kFrag + (lane & 31)]; };
+    // list (query or virtual query) of query column c and mask t
+    auto listid = [&](int c, int t) __attribute__((always_inline)) {
+      const int qg = qid_lds[c];
+      return (NT > 0 && !rescue) ? t * A.b + qg : qg;
+    };
 
     int st_n = 0;  // staged survivors of this wave (wave-uniform; may exceed the capacity)
 
@@ -216,8 +244,10 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
           const uint64_t ck = st_key[e];
           const int qc = st_q[e];
           const uint32_t pos = atomicAdd(&seg_lds[qc], 1u);
-          if ((int64_t)pos < A.capw)
-            A.cand[((int64_t)qid_lds[qc] * A.nseg + slice) * A.capw + pos] = ck;
+          if ((int64_t)pos < A.capw) {
+            const int64_t list = NT > 0 ? listid(qc / NTS, qc % NTS) : qid_lds[qc];
+            A.cand[(list * A.nseg + slice) * A.capw + pos] = ck;
+          }
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -255,14 +285,28 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
           }
         }
       }
-      const int r = lane < RM ? lane : RM - 1;
+      // lane r (multi-mask: lane NT r + t, mask t) holds the word of block r
+      const int rl = NT > 0 ? lane / NTS : lane;
+      const int r = rl < RM ? rl : RM - 1;
       const bool live = j0 + r < A.nfrag;
       const int64_t j = live ? j0 + r : A.nfrag - 1;
       const int64_t fr = A.blk0 + ((MODE == MODE_SAMPLE) ? (int64_t)(((uint64_t)j * A.sample_step) >> 32) : j);
       // branch-free: without a bitmap, any readable word masked to zero (a conditional
-      // load would make the compiler's wait counts conservative at the join)
-      const uint32_t* wp = A.exclude ? A.exclude + fr : (const uint32_t*)A.corpus;
-      uint32_t w = *wp & (A.exclude ? ~0u : 0u);
+      // load would make the compiler's wait counts conservative at the join); a mask
+      // past the pass's count excludes every row
+      const uint32_t* wp;
+      uint32_t keep, force = 0u;
+      if constexpr (NT > 0) {
+        const int mt = lane % NTS;
+        const bool use = mt < A.nmask;
+        wp = use ? A.masks + (int64_t)mt * A.mask_words + fr : (const uint32_t*)A.corpus;
+        keep = use ? ~0u : 0u;
+        force = use ? 0u : ~0u;
+      } else {
+        wp = A.exclude ? A.exclude + fr : (const uint32_t*)A.corpus;
+        keep = A.exclude ? ~0u : 0u;
+      }
+      uint32_t w = (*wp & keep) | force;
       const int64_t rows = A.n - fr * kFrag;
       if (rows < kFrag) w |= ~0u << rows;
       const int64_t below = A.lo - fr * kFrag;  // rows before the start of the id range
@@ -320,6 +364,41 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
     // Main epilogue of one query fragment: one max per block (16 scores per lane) and one
     // ballot, branch-free so it interleaves with the next fragment's MFMAs. A block that
     // clears the threshold is resolved on the scalar unit (below).
+    // Slow path of one block: per lane, a 16-bit mask of its values that pass: bit i <=>
+    // y[i] >= T and its row (8 (i >> 2) + 4 (lane >> 5) + (i & 3)) is not set in the
+    // block's word w (excluded or padding). The wave then walks the passing (lane, value)
+    // pairs on the scalar unit, usually one, and stages each survivor for mask t.
+    auto pass_walk = [&](const float (&y)[16], uint32_t w, float T, uint32_t idb, int qf,
+                         int t) __attribute__((always_inline)) {
+      uint32_t pm = 0u;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pm |= (y[i] >= T ? 1u : 0u) << i;
+      const uint32_t wl = w >> (4 * (lane >> 5));
+      pm &= ~((wl & 0xFu) | ((wl >> 4) & 0xF0u) | ((wl >> 8) & 0xF00u) | ((wl >> 12) & 0xF000u));
+      uint64_t H = __ballot(pm != 0u);
+      while (H != 0ull) {
+        const int L = __builtin_ctzll(H);
+        H &= H - 1ull;
+        uint32_t pl = (uint32_t)__builtin_amdgcn_readlane((int)pm, L);
+        const int qcol = qf * kFrag + (L & 31);
+        while (pl != 0u) {
+          const int i = __builtin_ctz(pl);
+          pl &= pl - 1u;
+          const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(y[i]), L));
+          const uint32_t id = idb + (uint32_t)(8 * (i >> 2) + 4 * (L >> 5) + (i & 3));
+          if (st_n < kStageCap) {
+            if (lane == 0) {
+              st_key[st_n] = composite(score_key(v), id);
+              st_q[st_n] = (uint16_t)(NT > 0 ? qcol * NTS + t : qcol);
+            }
+          } else if (lane == 0) {
+            atomicOr(&A.ovf[listid(qcol, t)], 1u);  // no room: the query is rescued
+          }
+          ++st_n;
+        }
+      }
+    };
+
     auto epi_main = [&](const f32x16_t (&acc)[RM], const float (&sc)[RM][SCN], uint32_t xwv,
                         int64_t j0, int qf) __attribute__((always_inline)) {
       const float T = Tq(qf);
@@ -340,40 +419,22 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
 #pragma unroll
         for (int g = 0; g < RM; ++g) {
           if (__ballot(m[g] >= T) == 0ull) continue;
-          const uint32_t w = __builtin_amdgcn_readlane(xwv, g);
           const uint32_t idb = (uint32_t)((A.blk0 + j0 + g) * kFrag);
           float y[16];
           vals(acc[g], sc[g], y);
 #pragma unroll
           for (int i = 0; i < 16; ++i) y[i] = post(y[i], sq);
-          // per lane, a 16-bit mask of its values that pass: bit i <=> value i >= T and
-          // its row (8 (i >> 2) + 4 (lane >> 5) + (i & 3)) is neither excluded nor padding
-          uint32_t pm = 0u;
+          if constexpr (NT == 0) {
+            pass_walk(y, (uint32_t)__builtin_amdgcn_readlane((int)xwv, g), T, idb, qf, 0);
+          } else {
+            // the block max reached the lowest of the column's thresholds; resolve only
+            // the masks whose own threshold some lane's max reaches
 #pragma unroll
-          for (int i = 0; i < 16; ++i) pm |= (y[i] >= T ? 1u : 0u) << i;
-          const uint32_t wl = w >> (4 * (lane >> 5));
-          pm &= ~((wl & 0xFu) | ((wl >> 4) & 0xF0u) | ((wl >> 8) & 0xF00u) | ((wl >> 12) & 0xF000u));
-          // walk the passing (lane, value) pairs on the scalar unit: usually one
-          uint64_t H = __ballot(pm != 0u);
-          while (H != 0ull) {
-            const int L = __builtin_ctzll(H);
-            H &= H - 1ull;
-            uint32_t pl = (uint32_t)__builtin_amdgcn_readlane((int)pm, L);
-            const int qcol = qf * kFrag + (L & 31);
-            while (pl != 0u) {
-              const int i = __builtin_ctz(pl);
-              pl &= pl - 1u;
-              const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(y[i]), L));
-              const uint32_t id = idb + (uint32_t)(8 * (i >> 2) + 4 * (L >> 5) + (i & 3));
-              if (st_n < kStageCap) {
-                if (lane == 0) {
-                  st_key[st_n] = composite(score_key(v), id);
-                  st_q[st_n] = (uint16_t)qcol;
-                }
-              } else if (lane == 0) {
-                atomicOr(&A.ovf[qid_lds[qcol]], 1u);  // no room: the query is rescued
-              }
-              ++st_n;
+            for (int t = 0; t < NT; ++t) {
+              if (t >= A.nmask) break;
+              const float Tt = thrt_lds[(qf * kFrag + (lane & 31)) * NT + t];
+              if (__ballot(m[g] >= Tt) == 0ull) continue;
+              pass_walk(y, (uint32_t)__builtin_amdgcn_readlane((int)xwv, g * NT + t), Tt, idb, qf, t);
             }
           }
         }
@@ -394,7 +455,10 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
 #pragma unroll
         for (int g = 0; g < RM; ++g) {
           const int64_t j = j0 + g;
-          const uint32_t w = __builtin_amdgcn_readlane(xwv, g);
+          uint32_t wt[NTS];  // the block's word (per mask)
+#pragma unroll
+          for (int t = 0; t < NTS; ++t)
+            wt[t] = (uint32_t)__builtin_amdgcn_readlane((int)xwv, NT > 0 ? g * NT + t : g);
           // The stores below are per lane (padding query columns are skipped). Their only
           // inputs are the accumulators, so without this pin the compiler may sink the
           // MFMAs, and the VALU work that feeds their per-lane scale operand, into the
@@ -405,40 +469,55 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
           if (j < A.nfrag && qg >= 0) {
             float x[16];
             vals(v, sc[g], x);
-            uint64_t* dst = A.cand + (int64_t)qg * A.nseg * A.capw + j * kFrag;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int row = acc_row(i, lane);
-              dst[row] = ((w >> row) & 1u)
-                             ? 0ull
-                             : composite(score_key(post(x[i], sq)),
-                                         (uint32_t)((A.blk0 + j) * kFrag + row));
+            for (int t = 0; t < NTS; ++t) {
+              if (NT > 0 && t >= A.nmask) break;
+              uint64_t* dst = A.cand + (int64_t)(NT > 0 ? t * A.b + qg : qg) * A.nseg * A.capw + j * kFrag;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int row = acc_row(i, lane);
+                dst[row] = ((wt[t] >> row) & 1u)
+                               ? 0ull
+                               : composite(score_key(post(x[i], sq)),
+                                           (uint32_t)((A.blk0 + j) * kFrag + row));
+              }
             }
           }
         }
       } else {
-        uint32_t d[RM];
-#pragma unroll
-        for (int g = 0; g < RM; ++g) {
-          const uint32_t w = __builtin_amdgcn_readlane(xwv, g);
-          float x[16];
-          vals(acc[g], sc[g], x);
-          float mx = -INFINITY;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int row = acc_row(i, lane);
-            mx = ((w >> row) & 1u) ? mx : fmaxf(mx, x[i]);
-          }
-          mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));  // the block's other 16 rows
-          d[g] = (mx == -INFINITY) ? 0u : score_key(post(mx, sq));
-          asm volatile("" : "+v"(d[g]));  // computed in uniform control flow, as above
-        }
         const int qc = qbase + qf * kFrag + lane;
-        if (lane < kFrag && qc < A.b32) {
-          const int64_t tt = j0 / RM;  // sample tile
-          uint32_t* dst = A.del + (((tt >> 4) * A.b32 + qc) * 16 + (tt & 15)) * RM;
+        const int64_t tt = j0 / RM;  // sample tile
 #pragma unroll
-          for (int g = 0; g < RM; ++g) dst[g] = d[g];
+        for (int t = 0; t < NTS; ++t) {
+          if (NT > 0 && t >= A.nmask) break;
+          uint32_t d[RM];
+#pragma unroll
+          for (int g = 0; g < RM; ++g) {
+            const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)xwv, NT > 0 ? g * NT + t : g);
+            float x[16];
+            vals(acc[g], sc[g], x);
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int row = acc_row(i, lane);
+              mx = ((w >> row) & 1u) ? mx : fmaxf(mx, x[i]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));  // the block's other 16 rows
+            d[g] = (mx == -INFINITY) ? 0u : score_key(post(mx, sq));
+            asm volatile("" : "+v"(d[g]));  // computed in uniform control flow, as above
+          }
+          if constexpr (NT > 0) {
+            // mask t's delegates are those of virtual query t * b + q
+            if (lane < kFrag && qc < A.b) {
+              uint32_t* dst = A.del + (((tt >> 4) * A.bv32 + t * A.b + qc) * 16 + (tt & 15)) * RM;
+#pragma unroll
+              for (int g = 0; g < RM; ++g) dst[g] = d[g];
+            }
+          } else if (lane < kFrag && qc < A.b32) {
+            uint32_t* dst = A.del + (((tt >> 4) * A.b32 + qc) * 16 + (tt & 15)) * RM;
+#pragma unroll
+            for (int g = 0; g < RM; ++g) dst[g] = d[g];
+          }
         }
       }
     };
@@ -511,38 +590,42 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
       if (st_n > 0) flush();
       // this workgroup's segment counts of the block's queries
       __syncthreads();
-      for (int i = threadIdx.x; i < QB; i += kScoreThreads) {
-        const int q = qid_lds[i];
-        if (q >= 0) A.segcnt[(int64_t)q * A.nseg + slice] = seg_lds[i];
+      for (int i = threadIdx.x; i < QB * NTS; i += kScoreThreads) {
+        const int c = i / NTS, t = i % NTS;
+        const int q = qid_lds[c];
+        if (q >= 0 && (NT == 0 || (t < A.nmask && (!rescue || q / A.b == t))))
+          A.segcnt[(int64_t)listid(c, t) * A.nseg + slice] = seg_lds[i];
       }
     }
   }
 }
 
-template <int CT, int D, int NQF, int MODE>
+template <int CT, int D, int NQF, int MODE, int NT>
 static int launch_score(const ScoreArgs& A, int grid, hipStream_t s) {
-  constexpr int lds = score_lds_bytes(CT, D, NQF);
+  constexpr int lds = score_lds_bytes(CT, D, NQF, NT);
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)score_kernel<CT, D, NQF, MODE>,
+    (void)hipFuncSetAttribute((const void*)score_kernel<CT, D, NQF, MODE, NT>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     attr = true;
   }
-  hipLaunchKernelGGL((score_kernel<CT, D, NQF, MODE>), dim3(grid), dim3(score_threads(CT, D)), lds, s, A);
+  hipLaunchKernelGGL((score_kernel<CT, D, NQF, MODE, NT>), dim3(grid), dim3(score_threads(CT, D)), lds, s, A);
   return check_launch();
 }
 
-template <int CT, int D, int MODE>
+template <int CT, int D, int MODE, int NT>
 int launch_score_nqf(int nqf, const ScoreArgs& A, int grid, hipStream_t s) {
   switch (nqf) {
-    case 1: return launch_score<CT, D, 1, MODE>(A, grid, s);
-    case 2: return launch_score<CT, D, 2, MODE>(A, grid, s);
-    case 4: return launch_score<CT, D, 4, MODE>(A, grid, s);
+    case 1: return launch_score<CT, D, 1, MODE, NT>(A, grid, s);
+    case 2: return launch_score<CT, D, 2, MODE, NT>(A, grid, s);
+    case 4:
+      if constexpr (nqf_fits(CT, D, 4, NT)) return launch_score<CT, D, 4, MODE, NT>(A, grid, s);
+      break;
     case 8:
-      if constexpr (nqf_fits(CT, D, 8)) return launch_score<CT, D, 8, MODE>(A, grid, s);
+      if constexpr (NT == 0 && nqf_fits(CT, D, 8)) return launch_score<CT, D, 8, MODE, NT>(A, grid, s);
       break;
     case 16:
-      if constexpr (nqf_fits(CT, D, 16)) return launch_score<CT, D, 16, MODE>(A, grid, s);
+      if constexpr (NT == 0 && nqf_fits(CT, D, 16)) return launch_score<CT, D, 16, MODE, NT>(A, grid, s);
       break;
   }
   return MIPS_ERR_UNSUPPORTED;

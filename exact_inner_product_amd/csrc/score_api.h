@@ -18,6 +18,8 @@ constexpr int kMaxSegments = 256;   // list segments per query (corpus slices of
 constexpr int kSimdStageBytes = 16384;  // corpus bytes per SIMD and pipeline stage
 constexpr int kPipeStages = 3;      // corpus stages per wave: one in use, two in flight
 constexpr int kSelCache = 6144;     // candidates the final select caches in LDS
+constexpr int kMaxMasks = 4;        // result sets (exclusion masks) of one multi-mask pass
+constexpr int kMaskNqfMax = 4;      // query fragments per workgroup of a multi-mask pass
 
 // Passes of the score kernel: the main filter pass (also the rescue pass), the sample pass
 // (delegates of a strided block sample) and the dense pass (every score, small corpora).
@@ -53,12 +55,13 @@ __host__ __device__ constexpr int stage_frags(int ct, int d) {
   return frags_for(ct, d, score_wps(ct, d));
 }
 // LDS of a score workgroup holding 32 * nqf queries: the query tile, 16 bytes of per-column
-// state per query and the survivor staging of every wave (8-byte key, 2-byte column).
-__host__ __device__ constexpr int score_lds_bytes(int ct, int d, int nqf) {
-  return kFrag * nqf * (d * elem_bytes(ct) + 16) + score_waves(ct, d) * kStageCap * (8 + 2);
+// state per query and the survivor staging of every wave (8-byte key, 2-byte column). A
+// multi-mask pass (nt masks) adds a threshold and a survivor counter per column and mask.
+__host__ __device__ constexpr int score_lds_bytes(int ct, int d, int nqf, int nt = 0) {
+  return kFrag * nqf * (d * elem_bytes(ct) + 16 + 8 * nt) + score_waves(ct, d) * kStageCap * (8 + 2);
 }
-__host__ __device__ constexpr bool nqf_fits(int ct, int d, int nqf) {
-  return score_lds_bytes(ct, d, nqf) <= kLdsLimit;
+__host__ __device__ constexpr bool nqf_fits(int ct, int d, int nqf, int nt = 0) {
+  return score_lds_bytes(ct, d, nqf, nt) <= kLdsLimit;
 }
 
 struct ScoreArgs {
@@ -87,11 +90,19 @@ struct ScoreArgs {
   const uint32_t* nlist;  // ... and their number (device); NULL for the full batch
   uint32_t* del;          // sample delegates [tile/16][b32][16][RM]: one per block and query
   uint64_t sample_step;   // sampled block j is block (j * sample_step) >> 32
+  // Multi-mask pass: nmask result sets, mask t excluding the rows whose bit is set in
+  // masks[t * mask_words ..]; result set t of query q is the virtual query t * b + q, which
+  // indexes thr, segcnt, ovf, cand and the rescue list (`exclude` is not used).
+  const uint32_t* masks;
+  int64_t mask_words;
+  int nmask;
+  int bv32;               // virtual queries rounded up to 32: the delegate stride
 };
 
-// Launches score_kernel<CT, D, nqf, MODE> (nqf in {1, 2, 4, 8, 16}); defined in
-// score_inst.hip, built once per corpus dtype and width.
-template <int CT, int D, int MODE>
+// Launches score_kernel<CT, D, nqf, MODE, NT> (nqf in {1, 2, 4, 8, 16}; NT = 0 for one
+// result set, kMaxMasks for a multi-mask pass); defined in score_inst.hip, built once per
+// corpus dtype and width.
+template <int CT, int D, int MODE, int NT = 0>
 int launch_score_nqf(int nqf, const ScoreArgs& A, int grid, hipStream_t s);
 
 }  // namespace mips

@@ -11,4 +11,8 @@ namespace mips {
 template int launch_score_nqf<MIPS_CT, MIPS_D, MODE_MAIN>(int, const ScoreArgs&, int, hipStream_t);
 template int launch_score_nqf<MIPS_CT, MIPS_D, MODE_SAMPLE>(int, const ScoreArgs&, int, hipStream_t);
 template int launch_score_nqf<MIPS_CT, MIPS_D, MODE_DENSE>(int, const ScoreArgs&, int, hipStream_t);
+// multi-mask passes
+template int launch_score_nqf<MIPS_CT, MIPS_D, MODE_MAIN, kMaxMasks>(int, const ScoreArgs&, int, hipStream_t);
+template int launch_score_nqf<MIPS_CT, MIPS_D, MODE_SAMPLE, kMaxMasks>(int, const ScoreArgs&, int, hipStream_t);
+template int launch_score_nqf<MIPS_CT, MIPS_D, MODE_DENSE, kMaxMasks>(int, const ScoreArgs&, int, hipStream_t);
 }  // namespace mips

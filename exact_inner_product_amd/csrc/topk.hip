@@ -49,7 +49,7 @@ template <int CT, int QT, int D>
 __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict__ queries, int b,
                                                           uint8_t* __restrict__ qtile,
                                                           int* __restrict__ qexp,
-                                                          uint32_t* __restrict__ ovf,
+                                                          uint32_t* __restrict__ ovf, int nflags,
                                                           uint32_t* __restrict__ nfail) {
   constexpr int NCH = chunks_per_block(CT, D);
   const int lane = threadIdx.x;
@@ -90,7 +90,8 @@ __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict
       v[t >> 2] |= (uint32_t)f32_to_e4m3(val(slot_dim(CT, c, lane, t)) * sinv) << (8 * (t & 3));
   }
   *(u32x4_t*)(qtile + (int64_t)qb * block_bytes(CT, D) + (int64_t)c * kChunkBytes + lane * 16) = v;
-  if (c == 0 && lane < 32 && live) ovf[q] = 0u;
+  // the overflow flag of every list (query, or virtual query of a multi-mask pass)
+  for (int i = blockIdx.x * 64 + lane; i < nflags; i += gridDim.x * 64) ovf[i] = 0u;
   if (blockIdx.x == 0 && lane == 0) *nfail = 0u;
 }
 
@@ -193,6 +194,9 @@ struct SelectArgs {
   const float* row_scale;
   const uint32_t* exclude;
   int64_t excl_rw;      // 0: one bitmap for every query; > 0: query q's row at q * excl_rw
+  const uint32_t* masks;  // multi-mask pass: list q is mask q / breal of query q % breal
+  int64_t mask_words;
+  int breal;              // 0: one result set, list q is query q
   const uint8_t* qtile;
   const int* qexp;
   int64_t n;            // rows [lo, n) take part
@@ -234,8 +238,12 @@ __device__ void write_out(const SelectArgs& A, int q, const uint64_t* s, int cnt
 template <int CT, int D>
 __device__ void fallback_scan(const SelectArgs& A, int q, uint64_t thr, uint64_t* buf,
                               uint64_t* sel_buf, SelScratch& S, float* qv, uint32_t* nbuf_p) {
+  // list q: query qr, rows excluded by the bitmap row xq (or the mask of a multi-mask pass)
+  const int qr = A.breal > 0 ? q % A.breal : q;
+  const uint32_t* xq = A.breal > 0 ? A.masks + (int64_t)(q / A.breal) * A.mask_words
+                                   : (A.exclude ? A.exclude + (int64_t)q * A.excl_rw : nullptr);
   for (int j = threadIdx.x; j < D; j += kSelThreads) {
-    const int64_t off = (int64_t)(q >> 5) * block_bytes(CT, D) + packed_offset(CT, D, q & 31, j);
+    const int64_t off = (int64_t)(qr >> 5) * block_bytes(CT, D) + packed_offset(CT, D, qr & 31, j);
     float v;
     if (CT == MIPS_F32)
       v = *(const float*)(A.qtile + off);
@@ -244,12 +252,11 @@ __device__ void fallback_scan(const SelectArgs& A, int q, uint64_t thr, uint64_t
     else if (CT == MIPS_INT8)
       v = (float)(int8_t)A.qtile[off];  // the query scale is applied to the sum
     else
-      v = e4m3_to_f32(A.qtile[off]) * exp2_int(A.qexp[q] - 127);
+      v = e4m3_to_f32(A.qtile[off]) * exp2_int(A.qexp[qr] - 127);
     qv[j] = v;
   }
   if (threadIdx.x == 0) *nbuf_p = 0u;
   __syncthreads();
-  const uint32_t* xq = A.exclude ? A.exclude + (int64_t)q * A.excl_rw : nullptr;
   constexpr int kRound = kSelThreads * 4;
   for (int64_t base = A.lo; base < A.n; base += kRound) {
     if (*nbuf_p + (uint32_t)kRound > (uint32_t)kSelCache) {
@@ -283,7 +290,7 @@ __device__ void fallback_scan(const SelectArgs& A, int q, uint64_t thr, uint64_t
       if (CT == MIPS_FP8_E4M3) s *= A.row_scale[i];
       // int8: the sum of code products is an integer below 2^24, exact in fp32 as in the
       // MFMA path; then the row scale and the query scale, in the score pass's order
-      if (CT == MIPS_INT8) s = (s * A.row_scale[i]) * __int_as_float(A.qexp[q]);
+      if (CT == MIPS_INT8) s = (s * A.row_scale[i]) * __int_as_float(A.qexp[qr]);
       const uint64_t key = composite(score_key(s), (uint32_t)i);
       if (key >= thr) buf[atomicAdd(nbuf_p, 1u)] = key;
     }
@@ -484,6 +491,8 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
 // ------------------------------------------------------------------- planning
 struct Plan {
   int b, b32, k, d, qdt, cdt;
+  int nt;                    // masks of a multi-mask pass (0: one result set)
+  int bv, bv32;              // lists: b per mask (virtual queries), and rounded up to 32
   int64_t excl_rw;           // exclusion words per query (0: one shared bitmap)
   int64_t n, n32, lo, blk0;  // rows [lo, n); n32 blocks from blk0
   int rm, nqf, nqblk, G, rest, nseg;
@@ -520,8 +529,11 @@ static int estimate_rank(int64_t n32, int G, int k) {
 // capq: candidate capacity per query (< 0: the default).
 // The pass covers rows [lo, n): the blocks from lo / 32 to the one holding row n - 1.
 static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt, int64_t capq,
-                      int64_t lo = 0) {
+                      int64_t lo = 0, int nt = 0) {
   p.b = b;
+  p.nt = nt;
+  p.bv = b * std::max(nt, 1);
+  p.bv32 = (p.bv + 31) / 32 * 32;
   p.excl_rw = 0;
   p.b32 = (b + 31) / 32 * 32;
   p.k = k;
@@ -533,8 +545,8 @@ static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt,
   p.blk0 = lo / 32;
   p.n32 = (n + 31) / 32 - p.blk0;
   p.rm = stage_frags(cdt, d);
-  int nqf_max = 16;
-  while (nqf_max > 1 && !nqf_fits(cdt, d, nqf_max)) nqf_max >>= 1;
+  int nqf_max = nt > 0 ? kMaskNqfMax : 16;
+  while (nqf_max > 1 && !nqf_fits(cdt, d, nqf_max, nt > 0 ? kMaxMasks : 0)) nqf_max >>= 1;
   const int need = p.b32 / 32;
   int nqblk = (need + nqf_max - 1) / nqf_max;
   const int per = (need + nqblk - 1) / nqblk;
@@ -552,30 +564,31 @@ static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt,
   o = align256(o + (size_t)p.b32 * d * E);
   p.off_qexp = o;
   o = align256(o + (size_t)p.b32 * 4);
+  // per list (query, or virtual query of a multi-mask pass)
   p.off_thr = o;
-  o = align256(o + (size_t)b * 4);
+  o = align256(o + (size_t)p.bv * 4);
   p.off_thrb = o;
-  o = align256(o + (size_t)b * 4);
+  o = align256(o + (size_t)p.bv * 4);
   p.off_ovf = o;
-  o = align256(o + (size_t)b * 4);
+  o = align256(o + (size_t)p.bv * 4);
   p.off_nfail = o;
   o = align256(o + 4);
   p.off_flist = o;
-  o = align256(o + (size_t)b * 4);
+  o = align256(o + (size_t)p.bv * 4);
   p.off_segcnt = o;
-  o = align256(o + (size_t)b * p.nseg * 4);
+  o = align256(o + (size_t)p.bv * p.nseg * 4);
   p.off_del = o;
   const int64_t gmax = std::min<int64_t>(p.n32, kMaxSample);
   const int64_t tgroups = ((gmax + p.rm - 1) / p.rm + 15) / 16;
-  o = align256(o + (size_t)tgroups * 16 * p.rm * p.b32 * 4);
+  o = align256(o + (size_t)tgroups * 16 * p.rm * (nt > 0 ? p.bv32 : p.b32) * 4);
   p.off_cand = o;
   p.fixed = o;
 }
 
-template <int CT, int D>
+template <int CT, int D, int NT>
 static int run_topk(const Plan& p, const void* queries, const void* corpus, const float* row_scale,
-                    const uint32_t* exclude, float* out_scores, int32_t* out_ids, uint8_t* ws,
-                    hipStream_t s) {
+                    const uint32_t* exclude, const uint32_t* masks, int64_t mask_words,
+                    float* out_scores, int32_t* out_ids, uint8_t* ws, hipStream_t s) {
   uint8_t* qtile = ws + p.off_qtile;
   int* qexp = (int*)(ws + p.off_qexp);
   uint32_t* thr = (uint32_t*)(ws + p.off_thr);
@@ -589,10 +602,10 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
 
   if (p.qdt == MIPS_F32)
     hipLaunchKernelGGL((prep_queries_kernel<CT, MIPS_F32, D>), dim3(p.b32 / 32 * chunks_per_block(CT, D)), dim3(64), 0, s,
-                       queries, p.b, qtile, qexp, ovf, nfail);
+                       queries, p.b, qtile, qexp, ovf, p.bv, nfail);
   else
     hipLaunchKernelGGL((prep_queries_kernel<CT, MIPS_BF16, D>), dim3(p.b32 / 32 * chunks_per_block(CT, D)), dim3(64), 0, s,
-                       queries, p.b, qtile, qexp, ovf, nfail);
+                       queries, p.b, qtile, qexp, ovf, p.bv, nfail);
   int rc = check_launch();
   if (rc) return rc;
 
@@ -618,6 +631,10 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   A.capw = p.capw;
   A.nseg = p.nseg;
   A.del = del;
+  A.masks = masks;
+  A.mask_words = mask_words;
+  A.nmask = p.nt;
+  A.bv32 = p.bv32;
 
   const int cus = device_cu_count();
   auto slices_for = [&](int64_t ntiles, int nqblk) {
@@ -635,8 +652,11 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   S.qexp = qexp;
   S.n = p.n;
   S.lo = p.lo;
-  S.b = p.b;
+  S.b = p.bv;
   S.k = p.k;
+  S.masks = masks;
+  S.mask_words = mask_words;
+  S.breal = NT > 0 ? p.b : 0;
   S.capw = p.capw;
   S.nseg = p.nseg;
   S.thr = thr;
@@ -657,10 +677,10 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
     A.ntiles = (p.n32 + p.rm - 1) / p.rm;
     A.nslices = slices_for(A.ntiles, p.nqblk);
     if (ev0) (void)hipEventRecord(ev0, s);
-    if ((rc = launch_score_nqf<CT, D, MODE_DENSE>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
+    if ((rc = launch_score_nqf<CT, D, MODE_DENSE, NT>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
     if (ev1) (void)hipEventRecord(ev1, s);
     S.dense_count = p.n32 * kFrag;
-    hipLaunchKernelGGL((final_select_kernel<CT, D>), dim3(p.b), dim3(kSelThreads), 0, s, S, 0);
+    hipLaunchKernelGGL((final_select_kernel<CT, D>), dim3(p.bv), dim3(kSelThreads), 0, s, S, 0);
     return check_launch();
   }
 
@@ -669,9 +689,9 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   A.sample_step = ((uint64_t)p.n32 << 32) / (uint64_t)p.G;
   A.ntiles = (p.G + p.rm - 1) / p.rm;
   A.nslices = slices_for(A.ntiles, p.nqblk);
-  if ((rc = launch_score_nqf<CT, D, MODE_SAMPLE>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
-  hipLaunchKernelGGL(sample_threshold_kernel, dim3(p.b), dim3(kSelThreads), 0, s, del, (int)A.ntiles,
-                     p.rm, p.b32, p.b, p.k, p.rest, thr, thrb);
+  if ((rc = launch_score_nqf<CT, D, MODE_SAMPLE, NT>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
+  hipLaunchKernelGGL(sample_threshold_kernel, dim3(p.bv), dim3(kSelThreads), 0, s, del, (int)A.ntiles,
+                     p.rm, NT > 0 ? p.bv32 : p.b32, p.bv, p.k, p.rest, thr, thrb);
   if ((rc = check_launch())) return rc;
 
   // main pass
@@ -679,11 +699,11 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   A.ntiles = (p.n32 + p.rm - 1) / p.rm;
   A.nslices = slices_for(A.ntiles, p.nqblk);
   if (ev0) (void)hipEventRecord(ev0, s);
-  if ((rc = launch_score_nqf<CT, D, MODE_MAIN>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
+  if ((rc = launch_score_nqf<CT, D, MODE_MAIN, NT>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
   if (ev1) (void)hipEventRecord(ev1, s);
   S.dense_count = 0;
   S.nseg_used = A.nslices;
-  hipLaunchKernelGGL((final_select_kernel<CT, D>), dim3(p.b), dim3(kSelThreads), 0, s, S, 0);
+  hipLaunchKernelGGL((final_select_kernel<CT, D>), dim3(p.bv), dim3(kSelThreads), 0, s, S, 0);
   if ((rc = check_launch())) return rc;
 
   // rescue pass over the queued queries (one workgroup per slice loops over them)
@@ -692,17 +712,22 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   R.nlist = nfail;
   R.nqblk = 1;
   R.nslices = slices_for(A.ntiles, 1);
-  if ((rc = launch_score_nqf<CT, D, MODE_MAIN>(p.nqf, R, R.nslices, s))) return rc;
+  if ((rc = launch_score_nqf<CT, D, MODE_MAIN, NT>(p.nqf, R, R.nslices, s))) return rc;
   S.nseg_used = R.nslices;
-  hipLaunchKernelGGL((final_select_kernel<CT, D>), dim3(p.b), dim3(kSelThreads), 0, s, S, 1);
+  hipLaunchKernelGGL((final_select_kernel<CT, D>), dim3(p.bv), dim3(kSelThreads), 0, s, S, 1);
   return check_launch();
 }
 
 template <int CT>
 static int dispatch_d(const Plan& p, const void* queries, const void* corpus,
-                      const float* row_scale, const uint32_t* exclude, float* out_scores,
-                      int32_t* out_ids, uint8_t* ws, hipStream_t s) {
-#define MIPS_RUN(DD) return run_topk<CT, DD>(p, queries, corpus, row_scale, exclude, out_scores, out_ids, ws, s)
+                      const float* row_scale, const uint32_t* exclude, const uint32_t* masks,
+                      int64_t mask_words, float* out_scores, int32_t* out_ids, uint8_t* ws,
+                      hipStream_t s) {
+#define MIPS_RUN(DD)                                                                           \
+  return p.nt > 0 ? run_topk<CT, DD, kMaxMasks>(p, queries, corpus, row_scale, exclude, masks, \
+                                                mask_words, out_scores, out_ids, ws, s)        \
+                  : run_topk<CT, DD, 0>(p, queries, corpus, row_scale, exclude, masks,         \
+                                        mask_words, out_scores, out_ids, ws, s)
   switch (p.d) {
     case 16: if constexpr (CT != MIPS_FP8_E4M3 && CT != MIPS_INT8) { MIPS_RUN(16); } break;
     case 32: if constexpr (CT != MIPS_FP8_E4M3) { MIPS_RUN(32); } break;
@@ -725,26 +750,100 @@ static int validate_topk(int32_t qdt, int32_t b, int32_t cdt, int64_t n, int32_t
   return MIPS_OK;
 }
 
+static_assert(kMaxMasks == MIPS_MAX_MASKS, "the header's mask limit is the kernel's");
+
+// Every top-k entry point: validation, then one pass per id range (nmasks > 0: one
+// multi-mask pass over the whole corpus, lists per (mask, query)).
+static int topk_entry(const void* queries, int32_t query_dtype, int32_t b, const void* corpus,
+                      const float* row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
+                      const uint32_t* exclude, int64_t exclude_row_words, const uint32_t* masks,
+                      int32_t nmasks, int64_t mask_words, const int64_t* ranges, int32_t nranges,
+                      int32_t k, float* out_scores, int32_t* out_ids, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!queries || !corpus || !out_scores || !out_ids || !workspace || !ranges)
+    return MIPS_ERR_INVALID_ARG;
+  const int rc0 = validate_topk(query_dtype, b, corpus_dtype, n, d, k);
+  if (rc0 != MIPS_OK) return rc0;
+  if (nranges < 1) return MIPS_ERR_INVALID_ARG;
+  for (int r = 0; r < nranges; ++r)
+    if (ranges[2 * r] < 0 || ranges[2 * r] >= ranges[2 * r + 1] || ranges[2 * r + 1] > n)
+      return MIPS_ERR_INVALID_ARG;
+  if (exclude_row_words < 0 || (exclude_row_words > 0 && (!exclude || exclude_row_words < (n + 31) / 32)))
+    return MIPS_ERR_INVALID_ARG;
+  if (nmasks > 0 && (!masks || mask_words < (n + 31) / 32 || exclude || !aligned(masks, 4) ||
+                     (int64_t)b * nmasks > 0x3FFFFFFF))
+    return MIPS_ERR_INVALID_ARG;
+  if ((corpus_dtype == MIPS_FP8_E4M3 || corpus_dtype == MIPS_INT8) && !row_scale)
+    return MIPS_ERR_INVALID_ARG;
+  if (!aligned(queries, 4) || !aligned(corpus, 16) || !aligned(workspace, 256) ||
+      !aligned(out_scores, 4) || !aligned(out_ids, 4) ||
+      (exclude && !aligned(exclude, 4)) || (row_scale && !aligned(row_scale, 4)))
+    return MIPS_ERR_INVALID_ARG;
+  // the whole corpus's plan bounds every range's fixed part and capacity
+  Plan p;
+  make_plan(p, b, n, d, k, query_dtype, corpus_dtype, -1, 0, nmasks);
+  if (workspace_bytes < p.fixed) return MIPS_ERR_WORKSPACE;
+  // candidate capacity per list: whole segments of what the workspace holds
+  const int64_t capq = (int64_t)((workspace_bytes - p.fixed) / ((size_t)p.bv * 8u));
+  if (capq / p.nseg < 1) return MIPS_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  for (int r = 0; r < nranges; ++r) {
+    make_plan(p, b, ranges[2 * r + 1], d, k, query_dtype, corpus_dtype, capq, ranges[2 * r], nmasks);
+    p.excl_rw = exclude_row_words;
+    float* os = out_scores + (int64_t)r * p.bv * k;
+    int32_t* oi = out_ids + (int64_t)r * p.bv * k;
+    int rc;
+    switch (corpus_dtype) {
+      case MIPS_F32:
+        rc = dispatch_d<MIPS_F32>(p, queries, corpus, row_scale, exclude, masks, mask_words, os, oi, ws, s);
+        break;
+      case MIPS_BF16:
+        rc = dispatch_d<MIPS_BF16>(p, queries, corpus, row_scale, exclude, masks, mask_words, os, oi, ws, s);
+        break;
+      case MIPS_INT8:
+        rc = dispatch_d<MIPS_INT8>(p, queries, corpus, row_scale, exclude, masks, mask_words, os, oi, ws, s);
+        break;
+      default:
+        rc = dispatch_d<MIPS_FP8_E4M3>(p, queries, corpus, row_scale, exclude, masks, mask_words, os, oi, ws, s);
+        break;
+    }
+    if (rc != MIPS_OK) return rc;
+  }
+  return MIPS_OK;
+}
+
+static size_t workspace_bytes_for(int32_t b, int64_t n, int32_t d, int32_t k, int32_t qdt,
+                                  int32_t cdt, int32_t nmasks, int64_t candidates) {
+  if (validate_topk(qdt, b, cdt, n, d, k) != MIPS_OK) return 0;
+  if (nmasks < 0 || nmasks > kMaxMasks) return 0;
+  Plan p;
+  make_plan(p, b, n, d, k, qdt, cdt, -1, 0, nmasks);
+  const int64_t capw = candidates < 0 ? p.capw : (candidates + p.nseg - 1) / p.nseg;
+  return p.fixed + (size_t)p.bv * (size_t)p.nseg * (size_t)capw * 8u;
+}
+
 }  // namespace mips
 
 extern "C" {
 
 size_t mips_topk_workspace_size(int32_t b, int64_t n, int32_t d, int32_t k, int32_t query_dtype,
                                 int32_t corpus_dtype) {
-  if (mips::validate_topk(query_dtype, b, corpus_dtype, n, d, k) != MIPS_OK) return 0;
-  mips::Plan p;
-  mips::make_plan(p, b, n, d, k, query_dtype, corpus_dtype, -1);
-  return p.fixed + (size_t)b * (size_t)p.nseg * (size_t)p.capw * 8u;
+  return mips::workspace_bytes_for(b, n, d, k, query_dtype, corpus_dtype, 0, -1);
 }
 
 size_t mips_topk_workspace_size_for(int32_t b, int64_t n, int32_t d, int32_t k, int32_t query_dtype,
                                     int32_t corpus_dtype, int64_t candidates_per_query) {
-  if (mips::validate_topk(query_dtype, b, corpus_dtype, n, d, k) != MIPS_OK) return 0;
   if (candidates_per_query < 1) return 0;
-  mips::Plan p;
-  mips::make_plan(p, b, n, d, k, query_dtype, corpus_dtype, -1);
-  const int64_t capw = (candidates_per_query + p.nseg - 1) / p.nseg;
-  return p.fixed + (size_t)b * (size_t)p.nseg * (size_t)capw * 8u;
+  return mips::workspace_bytes_for(b, n, d, k, query_dtype, corpus_dtype, 0, candidates_per_query);
+}
+
+size_t mips_topk_masks_workspace_size(int32_t b, int64_t n, int32_t d, int32_t k, int32_t query_dtype,
+                                      int32_t corpus_dtype, int32_t nmasks,
+                                      int64_t candidates_per_list) {
+  if (nmasks < 1) return 0;
+  return mips::workspace_bytes_for(b, n, d, k, query_dtype, corpus_dtype, nmasks,
+                                   candidates_per_list < 1 ? -1 : candidates_per_list);
 }
 
 int mips_topk(const void* queries, int32_t query_dtype, int32_t b, const void* corpus,
@@ -752,65 +851,31 @@ int mips_topk(const void* queries, int32_t query_dtype, int32_t b, const void* c
               const uint32_t* exclude, int64_t exclude_row_words, int32_t k, float* out_scores,
               int32_t* out_ids, void* workspace, size_t workspace_bytes, void* stream) {
   const int64_t whole[2] = {0, n};
-  return mips_topk_ranges(queries, query_dtype, b, corpus, row_scale, corpus_dtype, n, d, exclude,
-                          exclude_row_words, whole, 1, k, out_scores, out_ids, workspace,
-                          workspace_bytes, stream);
+  return mips::topk_entry(queries, query_dtype, b, corpus, row_scale, corpus_dtype, n, d, exclude,
+                          exclude_row_words, nullptr, 0, 0, whole, 1, k, out_scores, out_ids,
+                          workspace, workspace_bytes, stream);
 }
 
 int mips_topk_ranges(const void* queries, int32_t query_dtype, int32_t b, const void* corpus,
                      const float* row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
                      const uint32_t* exclude, int64_t exclude_row_words, const int64_t* ranges,
-                     int32_t nranges, int32_t k,
-                     float* out_scores, int32_t* out_ids, void* workspace, size_t workspace_bytes,
-                     void* stream) {
-  if (!queries || !corpus || !out_scores || !out_ids || !workspace || !ranges)
-    return MIPS_ERR_INVALID_ARG;
-  const int rc0 = mips::validate_topk(query_dtype, b, corpus_dtype, n, d, k);
-  if (rc0 != MIPS_OK) return rc0;
-  if (nranges < 1) return MIPS_ERR_INVALID_ARG;
-  if (exclude_row_words < 0 || (exclude_row_words > 0 && (!exclude || exclude_row_words < (n + 31) / 32)))
-    return MIPS_ERR_INVALID_ARG;
-  for (int r = 0; r < nranges; ++r)
-    if (ranges[2 * r] < 0 || ranges[2 * r] >= ranges[2 * r + 1] || ranges[2 * r + 1] > n)
-      return MIPS_ERR_INVALID_ARG;
-  if ((corpus_dtype == MIPS_FP8_E4M3 || corpus_dtype == MIPS_INT8) && !row_scale)
-    return MIPS_ERR_INVALID_ARG;
-  if (!mips::aligned(queries, 4) || !mips::aligned(corpus, 16) || !mips::aligned(workspace, 256) ||
-      !mips::aligned(out_scores, 4) || !mips::aligned(out_ids, 4) ||
-      (exclude && !mips::aligned(exclude, 4)) || (row_scale && !mips::aligned(row_scale, 4)))
-    return MIPS_ERR_INVALID_ARG;
-  // the whole corpus's plan bounds every range's fixed part and capacity
-  mips::Plan p;
-  mips::make_plan(p, b, n, d, k, query_dtype, corpus_dtype, -1);
-  if (workspace_bytes < p.fixed) return MIPS_ERR_WORKSPACE;
-  // candidate capacity per query: whole segments of what the workspace holds
-  const int64_t capq = (int64_t)((workspace_bytes - p.fixed) / ((size_t)b * 8u));
-  if (capq / p.nseg < 1) return MIPS_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  uint8_t* ws = (uint8_t*)workspace;
-  for (int r = 0; r < nranges; ++r) {
-    mips::make_plan(p, b, ranges[2 * r + 1], d, k, query_dtype, corpus_dtype, capq, ranges[2 * r]);
-    p.excl_rw = exclude_row_words;
-    float* os = out_scores + (int64_t)r * b * k;
-    int32_t* oi = out_ids + (int64_t)r * b * k;
-    int rc;
-    switch (corpus_dtype) {
-      case MIPS_F32:
-        rc = mips::dispatch_d<MIPS_F32>(p, queries, corpus, row_scale, exclude, os, oi, ws, s);
-        break;
-      case MIPS_BF16:
-        rc = mips::dispatch_d<MIPS_BF16>(p, queries, corpus, row_scale, exclude, os, oi, ws, s);
-        break;
-      case MIPS_INT8:
-        rc = mips::dispatch_d<MIPS_INT8>(p, queries, corpus, row_scale, exclude, os, oi, ws, s);
-        break;
-      default:
-        rc = mips::dispatch_d<MIPS_FP8_E4M3>(p, queries, corpus, row_scale, exclude, os, oi, ws, s);
-        break;
-    }
-    if (rc != MIPS_OK) return rc;
-  }
-  return MIPS_OK;
+                     int32_t nranges, int32_t k, float* out_scores, int32_t* out_ids,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return mips::topk_entry(queries, query_dtype, b, corpus, row_scale, corpus_dtype, n, d, exclude,
+                          exclude_row_words, nullptr, 0, 0, ranges, nranges, k, out_scores,
+                          out_ids, workspace, workspace_bytes, stream);
+}
+
+int mips_topk_masks(const void* queries, int32_t query_dtype, int32_t b, const void* corpus,
+                    const float* row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
+                    const uint32_t* masks, int32_t nmasks, int64_t mask_words, int32_t k,
+                    float* out_scores, int32_t* out_ids, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (nmasks < 1 || nmasks > mips::kMaxMasks) return nmasks < 1 ? MIPS_ERR_INVALID_ARG : MIPS_ERR_UNSUPPORTED;
+  const int64_t whole[2] = {0, n};
+  return mips::topk_entry(queries, query_dtype, b, corpus, row_scale, corpus_dtype, n, d, nullptr,
+                          0, masks, nmasks, mask_words, whole, 1, k, out_scores, out_ids,
+                          workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

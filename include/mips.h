@@ -212,11 +212,41 @@ MIPS_API int mips_topk_ranges(const void *queries, int32_t query_dtype, int32_t 
                               size_t workspace_bytes, void *stream);
 
 /*
+ * mips_topk_masks -- several result sets from one pass over the corpus: for each of the
+ * nmasks exclusion masks, every query's exact top-k of the rows that mask does not
+ * exclude. This is the per-type loop of `RecsysTwoTowerModel.forward`
+ * (recsys_two_tower_model.py), which scores the batch once and takes one masked top-k per
+ * target type; here each score is computed once and tested against the threshold of each
+ * mask that admits its row. Masks may overlap.
+ *   masks        device uint32 [nmasks][mask_words]: bit (i & 31) of word (i >> 5) of row t
+ *                set means id i is not in result set t (mips_type_bitmap builds one per
+ *                item type, with a shared exclusion folded in).
+ *   nmasks       1 .. MIPS_MAX_MASKS.  mask_words >= ceil(n/32).
+ *   out_scores   device float [nmasks, b, k]; out_ids device int32 [nmasks, b, k]: result
+ *                set t of query q at [t][q], as mips_topk's row q.
+ *   workspace    mips_topk_masks_workspace_size bytes: the fixed part and candidate lists
+ *                per mask and query, of candidates_per_list entries each (< 1: the default
+ *                capacity, as mips_topk_workspace_size; 0 returned for invalid sizes).
+ *   The other arguments, the ordering and the padding are as mips_topk's.
+ * Errors: as mips_topk; INVALID_ARG for a NULL or misaligned masks, nmasks < 1 or
+ * mask_words < ceil(n/32); UNSUPPORTED for nmasks > MIPS_MAX_MASKS.
+ */
+#define MIPS_MAX_MASKS 4
+MIPS_API size_t mips_topk_masks_workspace_size(int32_t b, int64_t n, int32_t d, int32_t k,
+                                               int32_t query_dtype, int32_t corpus_dtype,
+                                               int32_t nmasks, int64_t candidates_per_list);
+MIPS_API int mips_topk_masks(const void *queries, int32_t query_dtype, int32_t b, const void *corpus,
+                             const float *row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
+                             const uint32_t *masks, int32_t nmasks, int64_t mask_words, int32_t k,
+                             float *out_scores, int32_t *out_ids, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
  * mips_type_bitmap -- the exclusion bitmap of a search restricted to one item type: id i
  * is excluded when item_types[i] != target or exclude marks it (the per-type mask of
  * `RecsysTwoTowerModel.forward`, recsys_two_tower_model.py, one result set per target
- * type). Feed the result to mips_topk; excluded ids are never returned, so every id a
- * type-restricted search returns has that type.
+ * type). Feed the result to mips_topk, or one row per type to mips_topk_masks; excluded
+ * ids are never returned, so every id a type-restricted search returns has that type.
  *   item_types   device int32 [n]; n >= 1.
  *   exclude      device uint32 [ceil(n/32)] or NULL: ids excluded in any case.
  *   out_bitmap   device uint32 [ceil(n/32)]; bits of ids >= n are set. May alias exclude.

@@ -228,3 +228,29 @@ def test_type_bitmap_rejects_bad_arguments_before_launch(L):
     assert L.mips_type_bitmap(None, 10, 1, None, vp(0x1000), None) == INVALID
     assert L.mips_type_bitmap(vp(0x1000), 0, 1, None, vp(0x2000), None) == INVALID
     assert L.mips_type_bitmap(vp(0x1002), 10, 1, None, vp(0x2000), None) == INVALID
+
+
+def test_topk_masks_validation_and_workspace(L):
+    """mips_topk_masks: argument checks before any launch, and a workspace that grows with
+    the number of result sets and the candidate capacity."""
+    vp = C.c_void_p
+    one = L.mips_topk_masks_workspace_size(256, 10_000_000, 128, 500, BF16, BF16, 1, 0)
+    four = L.mips_topk_masks_workspace_size(256, 10_000_000, 128, 500, BF16, BF16, 4, 0)
+    assert 0 < one < four
+    assert L.mips_topk_masks_workspace_size(256, 10_000_000, 128, 500, BF16, BF16, 5, 0) == 0
+    assert L.mips_topk_masks_workspace_size(256, 10_000_000, 128, 500, BF16, BF16, 0, 0) == 0
+    small = L.mips_topk_masks_workspace_size(256, 10_000_000, 128, 500, BF16, BF16, 2, 256)
+    assert 0 < small < L.mips_topk_masks_workspace_size(256, 10_000_000, 128, 500, BF16, BF16, 2, 0)
+
+    def call(masks=0x6000, nm=2, words=32, q=0x1000, ws=0x10000, wsb=1 << 30, k=10, n=1000):
+        return L.mips_topk_masks(vp(q), BF16, 4, vp(0x2000), None, BF16, n, 128,
+                                 None if masks is None else vp(masks), nm, words, k, vp(0x3000),
+                                 vp(0x4000), vp(ws), wsb, None)
+    assert call(nm=0) == INVALID
+    assert call(nm=5) == UNSUPPORTED
+    assert call(masks=None) == INVALID
+    assert call(words=31) == INVALID         # n = 1000 needs 32 words per mask
+    assert call(masks=0x6002) == INVALID     # misaligned
+    assert call(q=None) == INVALID
+    assert call(k=1025) == UNSUPPORTED
+    assert call(wsb=1024) == WORKSPACE

@@ -596,3 +596,107 @@ def test_per_query_exclusion_with_ranges_and_interests():
         ex = ((urows[u][gi >> 5] >> (gi & 31).astype(np.uint32)) & 1) == 1
         assert not ex.any(), "an id the user's bitmap excludes was returned"
         assert np.abs(su[u][: gi.size] - o_s[0][: gi.size].astype(np.float32)).max() <= TOL["bf16"]
+
+
+# ----------------------------------------------------------- multi-mask pass
+def _typed_masks(n, rng, base=None):
+    """Four exclusion masks over n ids: three disjoint item types (about 60%, 39% and 1% of
+    the rows, so the last is rare) and an overlapping mask that keeps a random half; each
+    with the optional shared bitmap folded in."""
+    types = rng.choice(3, n, p=[0.6, 0.39, 0.01]).astype(np.int32)
+    rows = [bitmap_from_ids(np.nonzero(types != t)[0], n) for t in range(3)]
+    rows.append(bitmap_from_ids(rng.choice(n, n // 2, replace=False), n))
+    rows = np.stack(rows)
+    if base is not None:
+        rows |= base
+    return rows
+
+
+def _check_mask_rows(s, i, rows, q_or, qdt, c_or, cdt, sc_or, n, k):
+    ids_all = np.arange(n)
+    for t in range(rows.shape[0]):
+        print(f"mask {t}", flush=True)
+        bm = rows[t]
+        o_s, o_i = oracle.topk(q_or, qdt, c_or, cdt, k, row_scale=sc_or, exclude=bm)
+        excluded = set(ids_all[((bm[ids_all >> 5] >> (ids_all & 31).astype(np.uint32)) & 1) == 1].tolist())
+        check_topk(s[t], i[t], o_s, o_i, q_or, qdt, c_or, cdt, sc_or, excluded, n, TOL[cdt],
+                   floor=floor_for(cdt, qdt))
+
+
+@pytest.mark.parametrize("cdt,qdt,d,n,b,k", [
+    ("bf16", "bf16", 128, 300_000, 20, 100),   # a strided sample of blocks
+    ("int8", "bf16", 64, 60_000, 9, 50),       # every block sampled
+    ("fp8", "bf16", 256, 3_000, 6, 40),        # dense pass
+    ("f32", "f32", 32, 20_000, 7, 300),        # dense pass, more queries than one fragment
+    ("bf16", "f32", 64, 1_000_000, 5, 1000),   # k at its maximum
+    ("bf16", "bf16", 128, 100_000, 200, 64),   # two query blocks of 128
+])
+def test_topk_masks_match_oracle(cdt, qdt, d, n, b, k):
+    """Several result sets from one pass: each mask's result is the oracle's top-k with that
+    mask, and equals mips_topk run with the mask as its exclusion bitmap, bitwise."""
+    dev = _dev()
+    w = _workload(n, d, b, k, cdt, qdt, 91 + d, excl=0.05)
+    x, qraw = w.corpus(), w.queries()
+    corpus, q = _gpu_inputs(w, x, qraw, dev)
+    rows = _typed_masks(n, np.random.default_rng(91), w.exclude_bitmap())
+    print(f"case masks n={n} d={d} b={b} k={k} {cdt}/{qdt}", flush=True)
+    s, i = mips.topk_masks(q, corpus, torch.from_numpy(rows.view(np.int32)).to(dev), k)
+    torch.cuda.synchronize()
+    s, i = s.cpu().numpy(), i.cpu().numpy()
+    for t in range(rows.shape[0]):
+        s1, i1 = _scores_ids(q, corpus, k, _excl_tensor(rows[t], dev))
+        assert np.array_equal(i1, i[t]) and np.array_equal(s1.view(np.uint32), s[t].view(np.uint32)), t
+    c_or, sc_or = oracle.prepare(x, cdt)
+    q_or, _ = oracle.prepare(qraw, qdt)
+    _check_mask_rows(s, i, rows, q_or, qdt, c_or, cdt, sc_or, n, k)
+
+
+def test_topk_masks_edge_sets_and_rescue():
+    """Masks that exclude every row, leave fewer than k rows, or exclude nothing; one to
+    three masks per pass; and a workspace of one candidate per list segment, so that every
+    list overflows and is rescued: all equal the oracle."""
+    dev = _dev()
+    n, d, b, k = 200_000, 128, 8, 50
+    w = _workload(n, d, b, k, "bf16", "bf16", 92)
+    x, qraw = w.corpus(), w.queries()
+    corpus, q = _gpu_inputs(w, x, qraw, dev)
+    rng = np.random.default_rng(92)
+    words = (n + 31) // 32
+    keep = rng.choice(n, 20, replace=False)
+    rows = np.stack([np.full(words, 0xFFFFFFFF, np.uint32),
+                     bitmap_from_ids(np.setdiff1d(np.arange(n), keep), n),
+                     np.zeros(words, np.uint32)])
+    c_or, sc_or = oracle.prepare(x, "bf16")
+    q_or, _ = oracle.prepare(qraw, "bf16")
+    for nm in (1, 2, 3):
+        s, i = mips.topk_masks(q, corpus, torch.from_numpy(rows[:nm].view(np.int32)).to(dev), k)
+        torch.cuda.synchronize()
+        print(f"masks {nm}", flush=True)
+        _check_mask_rows(s.cpu().numpy(), i.cpu().numpy(), rows[:nm], q_or, "bf16", c_or, "bf16",
+                         None, n, k)
+    ws = mips.empty_workspace(mips.masks_workspace_size(b, n, d, k, "bf16", "bf16", 3, 1), dev)
+    s, i = mips.topk_masks(q, corpus, torch.from_numpy(rows.view(np.int32)).to(dev), k, workspace=ws)
+    torch.cuda.synchronize()
+    print("masks with one candidate per segment", flush=True)
+    _check_mask_rows(s.cpu().numpy(), i.cpu().numpy(), rows, q_or, "bf16", c_or, "bf16", None, n, k)
+
+
+def test_topk_types_more_than_one_pass():
+    """Six target types take two multi-mask passes (four, then two); each result set still
+    holds only its type and equals the oracle."""
+    dev = _dev()
+    n, d, b, k = 50_000, 64, 5, 30
+    w = _workload(n, d, b, k, "bf16", "bf16", 93)
+    x, qraw = w.corpus(), w.queries()
+    corpus, q = _gpu_inputs(w, x, qraw, dev)
+    types = np.random.default_rng(93).integers(0, 6, n).astype(np.int32)
+    targets = [5, 0, 3, 1, 4, 2]
+    res = mips.topk_types(q, corpus, torch.from_numpy(types).to(dev), targets, k)
+    c_or, _ = oracle.prepare(x, "bf16")
+    q_or, _ = oracle.prepare(qraw, "bf16")
+    for t, (i, s) in zip(targets, res):
+        i, s = i.cpu().numpy(), s.cpu().numpy()
+        other = np.nonzero(types != t)[0]
+        o_s, o_i = oracle.topk(q_or, "bf16", c_or, "bf16", k, exclude=bitmap_from_ids(other, n))
+        check_topk(s, i, o_s, o_i, q_or, "bf16", c_or, "bf16", None, set(other.tolist()), n,
+                   TOL["bf16"], floor=floor_for("bf16", "bf16"))
