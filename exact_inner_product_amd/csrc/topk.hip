@@ -208,7 +208,7 @@ struct SelectArgs {
   int nseg_used;        // segments written by the pass being selected from
   int64_t dense_count;  // > 0: lists hold one slot per row (0 = empty), this many
   uint32_t* thr;
-  const uint32_t* thrb;
+  uint32_t* thrb;
   const uint32_t* segcnt;
   uint32_t* ovf;
   const uint64_t* cand;
@@ -326,6 +326,9 @@ __device__ inline uint2 block_exclusive_sum(uint32_t v, uint32_t* wsum) {
   return make_uint2(before + c - v, total);
 }
 
+// Threshold key of -infinity: a pass with it keeps every eligible row.
+constexpr uint32_t kEveryRowKey = 0x007FFFFFu;
+
 // One workgroup per query. Round 0 covers the batch; round 1 the queries queued by round 0.
 // A query's candidates lie in segments (one per workgroup of the pass that found them);
 // thread s handles segment s.
@@ -393,8 +396,20 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
   }
   const uint32_t tu = A.thr[q], tb = A.thrb[q];
   if (tu == 0u) {
-    // no sampled bound for this query (fewer than K sampled blocks with an eligible row)
-    fallback_scan<CT, D>(A, q, 0ull, cache, sel_buf, S, qv, &nbuf);
+    // No sampled bound (fewer than K sampled blocks hold an eligible row, so the query has
+    // few eligible rows): the rescue pass gathers every eligible row on the MFMA path, and
+    // its list is complete unless it overflows.
+    if (round > 0) {
+      fallback_scan<CT, D>(A, q, 0ull, cache, sel_buf, S, qv, &nbuf);
+      return;
+    }
+    if (t == 0) {
+      const uint32_t slot = atomicAdd(A.nfail, 1u);
+      A.flist[slot] = (uint32_t)q;
+      A.thr[q] = kEveryRowKey;
+      A.thrb[q] = kEveryRowKey;
+      A.ovf[q] = 0u;
+    }
     return;
   }
   // segment s: found (counted by the pass) and stored (what fits the segment)
@@ -437,15 +452,15 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
   // Fewer than k candidates: final when the threshold was the proven bound. With one
   // bitmap per query the sample pass applied none, so its bound is not proven and a short
   // list is always rescued; at the bound itself only the exact rescan is left.
-  const bool shortfall = !over && eligible < A.k && (tu > tb || own);
+  const bool shortfall = !over && tu != kEveryRowKey && eligible < A.k && (tu > tb || own);
   if (over || shortfall) {
     if (round > 0 || (shortfall && tu == tb)) {
       fallback_scan<CT, D>(A, q, 0ull, cache, sel_buf, S, qv, &nbuf);
       return;
     }
-    // Rescue threshold: the proven bound after a shortfall; after an overflow, the k-th
-    // best stored candidate (k real items reach it).
-    uint32_t nt = tb;
+    // Rescue threshold: the proven bound after a shortfall (every row if the sample proved
+    // none); after an overflow, the k-th best stored candidate (k real items reach it).
+    uint32_t nt = tb == 0u ? kEveryRowKey : tb;
     if (over) {
       nt = tu;
       if (eligible >= A.k) {

@@ -244,8 +244,8 @@ def test_estimate_shortfall_is_rescued():
 
 
 def test_no_sampled_bound_takes_exact_scan():
-    """Fewer than K eligible sampled half-blocks: there is no sampled bound, and the final
-    select rescans the corpus exactly (excluded items never returned, the rest padded)."""
+    """Fewer than K eligible sampled blocks: there is no sampled bound, so the rescue pass
+    gathers every eligible row (excluded items never returned, the rest padded)."""
     n, d, b, k = 400_000, 64, 3, 100
     keep = np.random.default_rng(32).choice(n, 60, replace=False)
     bm = np.full((n + 31) // 32, 0xFFFFFFFF, np.uint32)
