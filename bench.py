@@ -101,6 +101,24 @@ def copy_calibration(torch, dev, gib):
     log(f"copy calibration: 3 copies of {n * 4} bytes")
 
 
+def copy_probe_gbs(torch, dev, gib=1.0, reps=5):
+    """Measured HBM bandwidth of a plain device-to-device copy of `gib` GiB (bytes read +
+    bytes written per second), a practical ceiling reported beside the published peak."""
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2.0 * n * 4 / (ms / 1e3) / 1e9
+
+
 def build_gpu_inputs(w, dev, torch, mips):
     """Raw corpus chunks -> device -> mips_prepare_corpus; queries -> mips_l2_normalize."""
     corpus = mips.empty_corpus(w.n, w.d, w.corpus_dtype, dev)
@@ -226,6 +244,11 @@ def main():
     roof["kernel_avg_us"] = main_avg * 1e6
     roof["algorithmic_bytes"] = alg_bytes
     roof["mfma_frac"] = achieved_tflops / PEAK_TFLOPS[w.corpus_dtype]
+    # measured after the timed region: the HBM rate of a plain 1 GiB device copy
+    copy_gbs = copy_probe_gbs(torch, dev)
+    roof["copy_gbs"] = copy_gbs
+    roof["hbm_frac_of_copy"] = achieved_gbs / copy_gbs
+    log(f"device copy probe: {copy_gbs:.0f} GB/s; main pass at {achieved_gbs / copy_gbs:.3f} of it")
 
     result = {
         "metric": "query-item scores/s (exhaustive inner-product top-K)",
