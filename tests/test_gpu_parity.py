@@ -630,6 +630,9 @@ def _check_mask_rows(s, i, rows, q_or, qdt, c_or, cdt, sc_or, n, k):
     ("f32", "f32", 32, 20_000, 7, 300),        # dense pass, more queries than one fragment
     ("bf16", "f32", 64, 1_000_000, 5, 1000),   # k at its maximum
     ("bf16", "bf16", 128, 100_000, 200, 64),   # two query blocks of 128
+    ("fp8", "bf16", 128, 200_000, 6, 50),      # fp8 scale operands on the sampled path
+    ("f32", "f32", 64, 150_000, 5, 30),        # f32 MFMA, sampled
+    ("bf16", "bf16", 256, 100_000, 40, 20),    # one wave per SIMD
 ])
 def test_topk_masks_match_oracle(cdt, qdt, d, n, b, k):
     """Several result sets from one pass: each mask's result is the oracle's top-k with that
