@@ -55,12 +55,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* p, int 
 }
 
 // One workgroup = 4 or 8 waves (one or two per SIMD) = one corpus slice x one block of
-// 32 * NQF queries. With NT > 0 (a multi-mask pass) every score is tested against up to NT
-// masks, each with its own threshold and candidate list per query. Each wave streams stage tiles of RM 32-row blocks (16 KiB per SIMD)
+// 32 * NQF queries. Each wave streams stage tiles of RM 32-row blocks (16 KiB per SIMD)
 // into registers, two stages in flight, and multiplies each stage against every query
 // fragment of the block in LDS. The query-fragment loop is unrolled and software-pipelined:
 // the MFMAs of fragment qf+1 and the LDS reads of fragment qf+2's operand are issued
-// before the epilogue of fragment qf.
+// before the epilogue of fragment qf. With NT > 0 (a multi-mask pass) every score is
+// tested against up to NT masks, each with its own threshold and list per query.
 template <int CT, int D, int NQF, int MODE, int NT>
 __global__ __launch_bounds__(score_threads(CT, D))
 __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void score_kernel(ScoreArgs A) {
