@@ -106,3 +106,45 @@ def test_int8_n10m():
 
 def test_bf16_n100m():
     run_workload("bf16_n100m_d64_b1024", [0, 1023])
+
+
+@pytest.mark.timeout(1200)
+def test_bf16_n10m_four_masks():
+    """The headline corpus and batch with four result sets from one multi-mask pass: three
+    disjoint item types (about 60%, 39% and 1% of the rows) and a random half, each with the
+    workload's exclusion folded in. Every set equals mips_topk with that mask bitwise, and
+    sampled queries equal the oracle's top-k under the mask."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from workloads import bitmap_from_ids
+    dev = torch.device("cuda:0")
+    w = WORKLOADS["bf16_n10m_d128_b256_excl5"]
+    print("four masks: building inputs", flush=True)
+    corpus, q, bm, codes, scale, q_or = build_both(w, dev)
+    rng = np.random.default_rng(20261203)
+    types = rng.choice(3, w.n, p=[0.6, 0.39, 0.01]).astype(np.int8)
+    rows = [bitmap_from_ids(np.nonzero(types != t)[0], w.n) | bm for t in range(3)]
+    rows.append(bitmap_from_ids(rng.choice(w.n, w.n // 2, replace=False), w.n) | bm)
+    rows = np.stack(rows)
+    masks = torch.from_numpy(rows.view(np.int32)).to(dev)
+    print("four masks: mips_topk_masks", flush=True)
+    s, i = mips.topk_masks(q, corpus, masks, w.k)
+    torch.cuda.synchronize()
+    s, i = s.cpu().numpy(), i.cpu().numpy()
+    sel = np.array([0, 77, 255], np.int64)
+    ids_all = np.arange(w.n)
+    for t in range(rows.shape[0]):
+        s1, i1 = mips.topk(q, corpus, w.k, masks[t])
+        torch.cuda.synchronize()
+        assert np.array_equal(i1.cpu().numpy(), i[t])
+        assert np.array_equal(s1.cpu().numpy().view(np.uint32), s[t].view(np.uint32))
+        bad = ((rows[t][np.maximum(i[t], 0) >> 5] >> (np.maximum(i[t], 0) & 31).astype(np.uint32)) & 1) == 1
+        assert not (bad & (i[t] >= 0)).any(), f"mask {t}: an excluded id was returned"
+        print(f"four masks: oracle, mask {t}", flush=True)
+        o_s, o_i = oracle.topk(q_or[sel], w.query_dtype, codes, w.corpus_dtype, w.k,
+                               exclude=rows[t], threads=threads())
+        excluded = set(ids_all[((rows[t][ids_all >> 5] >> (ids_all & 31).astype(np.uint32)) & 1) == 1].tolist())
+        stats = check_topk(s[t][sel], i[t][sel], o_s, o_i, q_or[sel], w.query_dtype, codes,
+                           w.corpus_dtype, scale, excluded, w.n, TOL[w.corpus_dtype],
+                           floor=floor_for(w.corpus_dtype, w.query_dtype))
+        print(f"four masks: mask {t}: {stats}", flush=True)
