@@ -134,23 +134,30 @@ __global__ __launch_bounds__(kSelThreads) void sample_threshold_kernel(const uin
   if (t < 2) found[t] = 0;
   __syncthreads();
   // the query's delegates: runs of 16 slots of `slot` delegates each (one slot per sample
-  // tile); each thread reads whole runs, contiguous bytes
+  // tile), 4 * slot 16-byte vectors per run; consecutive threads read consecutive vectors,
+  // eight loads in flight per thread before any histogram update
   const int ngroups = (ntiles + 15) / 16;
-  for (int gi = t; gi < ngroups; gi += kSelThreads) {
-    const u32x4_t* src = (const u32x4_t*)(del + ((int64_t)gi * b32 + q) * 16 * slot);
-    const int nvec = 16 * slot / 4;  // slot is 1, 2 or 4
-    for (int v0 = 0; v0 < nvec; v0 += 8) {
-      u32x4_t v[8];
+  const int nvec = 4 * slot;  // slot is 1, 2 or 4
+  const int total = ngroups * nvec;
+  for (int j0 = 0; j0 < total; j0 += kSelThreads * 8) {
+    u32x4_t v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = v0 + u < nvec ? src[v0 + u] : u32x4_t{0u, 0u, 0u, 0u};
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u * kSelThreads + t;
+      v[u] = u32x4_t{0u, 0u, 0u, 0u};
+      if (j < total)
+        v[u] = *((const u32x4_t*)(del + ((int64_t)(j / nvec) * b32 + q) * 16 * slot) + j % nvec);
+    }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u * kSelThreads + t;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // slots of tiles past the end of the pass are never written
-          const int tile = gi * 16 + ((v0 + u) * 4 + e) / slot;
-          if (tile < ntiles && v[u][e] != 0u) atomicAdd(&hist[thr_bin(key_score(v[u][e]))], 1u);
-        }
+      for (int e = 0; e < 4; ++e) {
+        // slots of tiles past the end of the pass are never written
+        const int tile = (j / nvec) * 16 + ((j % nvec) * 4 + e) / slot;
+        if (j < total && tile < ntiles && v[u][e] != 0u)
+          atomicAdd(&hist[thr_bin(key_score(v[u][e]))], 1u);
+      }
     }
   }
   __syncthreads();
