@@ -68,7 +68,8 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
   constexpr int kScoreWaves = score_waves(CT, D);
   constexpr int E = elem_bytes(CT);
   constexpr int NCH = chunks_per_block(CT, D);
-  constexpr int RM = stage_frags(CT, D);
+  constexpr int RM = MODE == MODE_MAIN ? main_frags(CT, D) : stage_frags(CT, D);
+  constexpr bool SINGLE = MODE == MODE_MAIN && main_doubles(CT, D);  // one accumulator set
   constexpr int KSTEPS = (CT == MIPS_F32) ? D / 2
                         : (CT == MIPS_BF16 ? D / 16 : (CT == MIPS_INT8 ? D / 32 : D / 64));
   // int8: per stage block, the scales of the 16 rows a lane's accumulators cover
@@ -528,6 +529,20 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
     auto compute_stage = [&](const u32x4_t (&a)[RM][NCH], const int (&sa)[RM],
                              const float (&sc)[RM][SCN], uint32_t xwv,
                              int64_t j0) __attribute__((always_inline)) {
+      if constexpr (SINGLE) {
+        // one accumulator set: fragment qf's MFMAs, then its epilogue (the other wave on
+        // the SIMD keeps the matrix pipe busy meanwhile); the operand of fragment qf+1
+        // streams in from LDS behind the MFMAs
+        f32x16_t acc1[RM];
+        u32x4_t bq1[NCH];
+        load_b(bq1, 0);
+        static_for<NQF>([&](auto qfc) __attribute__((always_inline)) {
+          constexpr int qf = decltype(qfc)::value;
+          mfmas(acc1, a, sa, bq1, sbq(qf), qf + 1 < NQF ? qf + 1 : -1);
+          epi_main(acc1, sc, xwv, j0, qf);
+        });
+        return;
+      }
       f32x16_t acc[2][RM];
       u32x4_t bq[NCH];
       load_b(bq, 0);
@@ -554,7 +569,7 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
     // microseconds of loaded latency), hence NS - 1 = 2 stages of 16 KiB per SIMD. The
     // sample and dense passes hold one stage less with two waves per SIMD: their epilogues
     // need the registers, and they run few stages per wave.
-    constexpr int NS = (MODE != MODE_MAIN && score_wps(CT, D) == 2) ? 2 : kPipeStages;
+    constexpr int NS = (SINGLE || (MODE != MODE_MAIN && score_wps(CT, D) == 2)) ? 2 : kPipeStages;
     u32x4_t a[NS][RM][NCH];
     int sa[NS][RM];
     float sc[NS][RM][SCN];

@@ -54,6 +54,20 @@ __host__ __device__ constexpr int score_waves(int ct, int d) { return 4 * score_
 __host__ __device__ constexpr int stage_frags(int ct, int d) {
   return frags_for(ct, d, score_wps(ct, d));
 }
+// Main pass with two blocks per stage. Where two waves share a SIMD with one block per
+// stage, each query operand read from LDS feeds only one block's MFMAs, and LDS read
+// bandwidth becomes a co-bound of the pass. The main pass then takes two blocks per stage
+// in a two-stage ring (the same stage bytes in flight per SIMD) with one accumulator set
+// per wave, which fits the 256 registers; the sample and dense passes keep one block.
+__host__ __device__ constexpr bool main_doubles(int ct, int d) {
+  // (the fp8 MFMA's operand packing needs more registers than this estimate allows for)
+  return (ct == MIPS_BF16 || ct == MIPS_INT8) && score_wps(ct, d) == 2 && stage_frags(ct, d) == 1 &&
+         2 * 2 * chunks_per_block(ct, d) * 4 + (ct == MIPS_INT8 ? 2 * 2 * 16 : 0) + 2 * 16 +
+                 chunks_per_block(ct, d) * 4 + 60 <= 256;
+}
+__host__ __device__ constexpr int main_frags(int ct, int d) {
+  return main_doubles(ct, d) ? 2 : stage_frags(ct, d);
+}
 // LDS of a score workgroup holding 32 * nqf queries: the query tile, 16 bytes of per-column
 // state per query and the survivor staging of every wave (8-byte key, 2-byte column). A
 // multi-mask pass (nt masks) adds a threshold and a survivor counter per column and mask.

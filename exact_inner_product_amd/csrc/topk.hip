@@ -517,7 +517,7 @@ struct Plan {
   int bv, bv32;              // lists: b per mask (virtual queries), and rounded up to 32
   int64_t excl_rw;           // exclusion words per query (0: one shared bitmap)
   int64_t n, n32, lo, blk0;  // rows [lo, n); n32 blocks from blk0
-  int rm, nqf, nqblk, G, rest, nseg;
+  int rm, rm_main, nqf, nqblk, G, rest, nseg;  // blocks per stage: sample/dense, main
   bool dense;
   int64_t capw;  // candidate entries per list segment
   size_t off_qtile, off_qexp, off_thr, off_thrb, off_ovf, off_nfail, off_flist, off_segcnt,
@@ -567,6 +567,7 @@ static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt,
   p.blk0 = lo / 32;
   p.n32 = (n + 31) / 32 - p.blk0;
   p.rm = stage_frags(cdt, d);
+  p.rm_main = main_frags(cdt, d);
   int nqf_max = nt > 0 ? kMaskNqfMax : 16;
   while (nqf_max > 1 && !nqf_fits(cdt, d, nqf_max, nt > 0 ? kMaxMasks : 0)) nqf_max >>= 1;
   const int need = p.b32 / 32;
@@ -718,7 +719,7 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
 
   // main pass
   A.nfrag = p.n32;
-  A.ntiles = (p.n32 + p.rm - 1) / p.rm;
+  A.ntiles = (p.n32 + p.rm_main - 1) / p.rm_main;
   A.nslices = slices_for(A.ntiles, p.nqblk);
   if (ev0) (void)hipEventRecord(ev0, s);
   if ((rc = launch_score_nqf<CT, D, MODE_MAIN, NT>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
