@@ -579,7 +579,11 @@ static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt,
   p.nseg = list_segments();
   p.capw = capq < 0 ? default_capw(p.n32, k, p.nseg) : capq / p.nseg;
   p.dense = p.n32 < 2 * (int64_t)k + 64 && p.n32 * kFrag <= p.nseg * p.capw;
-  p.G = p.dense ? 0 : (int)std::min<int64_t>(p.n32, kMaxSample);
+  // sampled blocks: at most kMaxSample and a 16th of the corpus (the sample pass re-reads
+  // them), but at least 4 K so that the K-th delegate usually exists
+  p.G = p.dense ? 0
+                : (int)std::min<int64_t>(std::min<int64_t>(p.n32, kMaxSample),
+                                         std::max<int64_t>(p.n32 / 16, 4 * (int64_t)k));
   p.rest = p.dense ? 0 : estimate_rank(p.n32, p.G, k);
   const int E = elem_bytes(cdt);
   size_t o = 0;

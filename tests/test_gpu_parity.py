@@ -214,10 +214,11 @@ def test_small_workspace_forces_exact_rescan():
     run_case(n, d, b, k, "bf16", "bf16", seed=12, workspace_bytes=wsb)
 
 
-def _sampled_blocks(n, g_max=8192):
-    """Blocks the sample pass reads: an even integer stride over the 32-row blocks."""
+def _sampled_blocks(n, k, g_max=8192):
+    """Blocks the sample pass reads: an even integer stride over the 32-row blocks, G of them
+    (at most 8192 and a 16th of the blocks, at least 4 k)."""
     n32 = (n + 31) // 32
-    g = min(n32, g_max)
+    g = min(n32, g_max, max(n32 // 16, 4 * k))
     step = (n32 << 32) // g
     return np.array([(j * step) >> 32 for j in range(g)], np.int64)
 
@@ -231,7 +232,7 @@ def test_estimate_shortfall_is_rescued():
     rng = np.random.default_rng(31)
     x = rng.standard_normal((n, d)).astype(np.float32)
     x[:, 0] *= 0.05  # base items are nearly orthogonal to e_0
-    blocks = _sampled_blocks(n)
+    blocks = _sampled_blocks(n, k)
     planted = blocks[:: len(blocks) // 40][:40] * 32
     x[planted] = 0.0
     x[planted, 0] = 1.0
@@ -521,7 +522,7 @@ def _check_per_query(s, i, rows, q_or, qdt, c_or, cdt, sc_or, n, k):
 
 
 @pytest.mark.parametrize("cdt,qdt,d,n,b,k", [
-    ("bf16", "bf16", 128, 60_000, 10, 100),    # every block sampled: the bound is exact rank k
+    ("bf16", "bf16", 128, 12_000, 10, 100),    # every block sampled: the bound is exact rank k
     ("fp8", "bf16", 256, 400_000, 10, 200),   # a strided sample: estimate above the bound
     ("int8", "bf16", 64, 3_000, 6, 50),       # dense pass
     ("f32", "f32", 64, 20_000, 7, 500),       # dense pass, k above some rows' eligible count
@@ -625,7 +626,8 @@ def _check_mask_rows(s, i, rows, q_or, qdt, c_or, cdt, sc_or, n, k):
 
 @pytest.mark.parametrize("cdt,qdt,d,n,b,k", [
     ("bf16", "bf16", 128, 300_000, 20, 100),   # a strided sample of blocks
-    ("int8", "bf16", 64, 60_000, 9, 50),       # every block sampled
+    ("int8", "bf16", 64, 6_000, 9, 50),        # every block sampled
+    ("int8", "bf16", 64, 60_000, 9, 50),       # a strided sample
     ("fp8", "bf16", 256, 3_000, 6, 40),        # dense pass
     ("f32", "f32", 32, 20_000, 7, 300),        # dense pass, more queries than one fragment
     ("bf16", "f32", 64, 1_000_000, 5, 1000),   # k at its maximum
