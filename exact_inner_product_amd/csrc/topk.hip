@@ -333,6 +333,10 @@ __device__ inline uint2 block_exclusive_sum(uint32_t v, uint32_t* wsum) {
   return make_uint2(before + c - v, total);
 }
 
+// Lists of at most this many candidates (and at most 4 k) are sorted whole instead of
+// radix-selected first; for a k much smaller than the list, selecting first is cheaper.
+constexpr int kSortAll = 512;
+
 // Threshold key of -infinity: a pass with it keeps every eligible row.
 constexpr uint32_t kEveryRowKey = 0x007FFFFFu;
 
@@ -383,6 +387,12 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
     atomicAdd(&nbuf, mine);
     __syncthreads();
     const int r = (int)min<int64_t>((int64_t)nbuf, A.k);
+    if (cached && c <= kSortAll && c <= 4 * (int64_t)A.k) {
+      // few slots: one sort of all of them (empty slots, key 0, sink to the end)
+      bitonic_sort_desc(cache, (int)c);
+      write_out(A, q, cache, r);
+      return;
+    }
     if (r > 0) {
       Sel64 sel{0ull, 0ull};
       if (cached) {
@@ -497,6 +507,12 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
           if (i0 + e < mine) cache[segoff[t] + i0 + e] = own && excluded(v[e]) ? 0ull : v[e];
       }
       __syncthreads();
+      if (c <= kSortAll && c <= 4 * (int64_t)A.k) {
+        // a short list: one sort of every candidate (excluded ones, key 0, sink to the end)
+        bitonic_sort_desc(cache, (int)c);
+        write_out(A, q, cache, r);
+        return;
+      }
       auto get = [&](int64_t i) { return cache[i]; };
       Sel64 sel{0ull, 0ull};
       if (c > r) sel = select_top(get, c, r, S);
