@@ -161,6 +161,54 @@ def cpu_baseline(w, budget_queries):
                       f"{dt:.1f}s"}
 
 
+def bench_masks(args, w, corpus, q, excl, torch, mips, dev):
+    """One multi-mask pass against T separate calls, each with one mask as its bitmap; the
+    same synthetic masks, inputs resident, the same step count for both."""
+    import numpy as np
+    from workloads import typed_masks
+    t = args.masks
+    if not 1 <= t <= 4:
+        log("--masks takes 1 to 4")
+        sys.exit(2)
+    base = None if excl is None else excl.cpu().numpy().view(np.uint32)
+    rows = typed_masks(w.n, base)[:t]
+    masks = torch.from_numpy(rows.view(np.int32)).to(dev)
+    wsm = mips.empty_workspace(mips.masks_workspace_size(w.b, w.n, w.d, w.k, w.query_dtype,
+                                                         w.corpus_dtype, t), dev)
+    ws1 = mips.empty_workspace(mips.workspace_size(w.b, w.n, w.d, w.k, w.query_dtype,
+                                                   w.corpus_dtype), dev)
+
+    def one_pass():
+        mips.topk_masks(q, corpus, masks, w.k, workspace=wsm)
+
+    def separate():
+        for r in range(t):
+            mips.topk(q, corpus, w.k, masks[r], workspace=ws1)
+
+    def timed(f):
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            f()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps * 1e3
+
+    ms_pass = timed(one_pass)
+    ms_sep = timed(separate)
+    log(f"{t} masks: one pass {ms_pass:.3f} ms, {t} separate calls {ms_sep:.3f} ms")
+    print(json.dumps({
+        "metric": "query-item scores/s (exhaustive inner-product top-K, multi-mask pass)",
+        "value": w.b * w.n / (ms_pass / 1e3), "unit": "scores/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_pass,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.corpus_dtype, "data": "synthetic",
+        "config": {"workload": w.name, "masks": t, "n": w.n, "d": w.d, "b": w.b, "k": w.k},
+        "separate_calls_ms": ms_sep, "speedup_vs_separate": ms_sep / ms_pass,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +220,9 @@ def main():
                     help="queries in the CPU-baseline sample (default: host threads)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="first run a plain device copy of GIB GiB (counter calibration)")
+    ap.add_argument("--masks", type=int, default=0, metavar="T",
+                    help="time a T-mask pass (mips_topk_masks, 1 <= T <= 4, the item-type "
+                         "masks of workloads.typed_masks) beside T separate mips_topk calls")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
@@ -190,6 +241,9 @@ def main():
     t0 = time.perf_counter()
     corpus, q, excl, prep_gbs = build_gpu_inputs(w, dev, torch, mips)
     log(f"inputs resident in HBM after {time.perf_counter() - t0:.1f}s; prepare {prep_gbs:.0f} GB/s")
+
+    if args.masks:
+        return bench_masks(args, w, corpus, q, excl, torch, mips, dev)
 
     wsb = mips.workspace_size(w.b, w.n, w.d, w.k, w.query_dtype, w.corpus_dtype)
     ws = mips.empty_workspace(wsb, dev)

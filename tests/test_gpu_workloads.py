@@ -116,16 +116,12 @@ def test_bf16_n10m_four_masks():
     sampled queries equal the oracle's top-k under the mask."""
     if not torch.cuda.is_available():
         pytest.skip("needs a GPU")
-    from workloads import bitmap_from_ids
+    from workloads import typed_masks
     dev = torch.device("cuda:0")
     w = WORKLOADS["bf16_n10m_d128_b256_excl5"]
     print("four masks: building inputs", flush=True)
     corpus, q, bm, codes, scale, q_or = build_both(w, dev)
-    rng = np.random.default_rng(20261203)
-    types = rng.choice(3, w.n, p=[0.6, 0.39, 0.01]).astype(np.int8)
-    rows = [bitmap_from_ids(np.nonzero(types != t)[0], w.n) | bm for t in range(3)]
-    rows.append(bitmap_from_ids(rng.choice(w.n, w.n // 2, replace=False), w.n) | bm)
-    rows = np.stack(rows)
+    rows = typed_masks(w.n, bm)
     masks = torch.from_numpy(rows.view(np.int32)).to(dev)
     print("four masks: mips_topk_masks", flush=True)
     s, i = mips.topk_masks(q, corpus, masks, w.k)

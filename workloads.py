@@ -195,6 +195,21 @@ class Workload:
         return bitmap_from_ids(ids, self.n)
 
 
+def typed_masks(n: int, base: Optional[np.ndarray] = None, seed: int = 20261203) -> np.ndarray:
+    """Four exclusion masks over n ids for a multi-mask search, uint32 [4, ceil(n/32)]: three
+    disjoint item types drawn per id with probabilities 0.6, 0.39 and 0.01 (the last a rare
+    type), each mask excluding the ids of the other types, and a random half of the ids;
+    the optional shared bitmap `base` is folded into every mask."""
+    rng = np.random.default_rng(seed)
+    types = rng.choice(3, n, p=[0.6, 0.39, 0.01]).astype(np.int8)
+    rows = [bitmap_from_ids(np.nonzero(types != t)[0], n) for t in range(3)]
+    rows.append(bitmap_from_ids(rng.choice(n, n // 2, replace=False), n))
+    rows = np.stack(rows)
+    if base is not None:
+        rows |= base
+    return rows
+
+
 def bitmap_from_ids(ids: np.ndarray, n: int) -> np.ndarray:
     """uint32[ceil(n/32)]; bit (i & 31) of word (i >> 5) set <=> id i excluded."""
     words = np.zeros((n + 31) // 32, np.uint32)
