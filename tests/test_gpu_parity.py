@@ -705,3 +705,21 @@ def test_topk_types_more_than_one_pass():
         o_s, o_i = oracle.topk(q_or, "bf16", c_or, "bf16", k, exclude=bitmap_from_ids(other, n))
         check_topk(s, i, o_s, o_i, q_or, "bf16", c_or, "bf16", None, set(other.tolist()), n,
                    TOL["bf16"], floor=floor_for("bf16", "bf16"))
+
+
+@pytest.mark.parametrize("b", [1, 33])
+def test_topk_masks_identical_masks_and_ragged_batches(b):
+    """Identical masks give identical result sets, each equal to mips_topk with that mask,
+    for one query and for a batch that is not a multiple of 32."""
+    dev = _dev()
+    n, d, k = 70_000, 128, 7
+    w = _workload(n, d, b, k, "bf16", "bf16", 94 + b, excl=0.05)
+    corpus, q = _gpu_inputs(w, w.corpus(), w.queries(), dev)
+    bm = w.exclude_bitmap()
+    rows = np.stack([bm, bm, bm])
+    s, i = mips.topk_masks(q, corpus, torch.from_numpy(rows.view(np.int32)).to(dev), k)
+    torch.cuda.synchronize()
+    s, i = s.cpu().numpy(), i.cpu().numpy()
+    s1, i1 = _scores_ids(q, corpus, k, _excl_tensor(bm, dev))
+    for t in range(3):
+        assert np.array_equal(i[t], i1) and np.array_equal(s[t].view(np.uint32), s1.view(np.uint32)), t
