@@ -9,6 +9,12 @@
  * whole index, masks it with one shared type mask and takes a sorted top-min(k, N)).
  * The score matrix is never written to memory.
  *
+ * Entry points: mips_l2_normalize and mips_prepare_corpus (normalisation, index build);
+ * mips_topk (one result set per query), mips_topk_ranges (one per id range) and
+ * mips_topk_masks (one per exclusion mask, from one pass over the index), with their
+ * workspace sizes; mips_merge_topk and mips_merge_interests (merges of sorted result
+ * lists); mips_type_bitmap (per-type exclusion bitmaps); status strings and a timing hook.
+ *
  * Conventions shared by every entry point:
  *  - All buffers are caller-owned. Pointers marked "device" are HIP device memory;
  *    the library never allocates, frees or synchronises. Work is enqueued on
