@@ -122,7 +122,62 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
     constexpr int NV = QB * D * E / 16;
     constexpr int kFillBatch = 4;
     constexpr int PER = (NV + kScoreThreads - 1) / kScoreThreads;
-    if (!rescue) {
+    if (fused_prep_ok(CT, D, NQF) && MODE == MODE_SAMPLE && !rescue && A.qraw != nullptr) {
+      // the operand tile from the raw queries (the layout of the packed corpus, 32 queries
+      // per block); rounding as the query prep kernel's
+      const int rows = min(QB, A.b32 - qbase);
+      const int n16 = rows * D * E / 16;
+      u32x4_t* dst = (u32x4_t*)lds;
+      u32x4_t* gdst = (u32x4_t*)(const_cast<uint8_t*>(A.qtile) + (int64_t)qbase * D * E);
+      // slot s of chunk c: bf16 dims 16c + 8h + (0..7), contiguous; f32 dims 8c + h + 2t
+      constexpr int kRawBatch = 8;
+      for (int i0 = 0; i0 < PER; i0 += kRawBatch) {
+        u32x4_t v[kRawBatch];
+#pragma unroll
+        for (int u = 0; u < kRawBatch; ++u) {
+          const int i = (i0 + u) * kScoreThreads + threadIdx.x;
+          const int c = (i >> 6) % NCH, s = i & 63, h = s >> 5;
+          const int q = qbase + (i >> 6) / NCH * kFrag + (s & 31);
+          v[u] = u32x4_t{0u, 0u, 0u, 0u};
+          if (i0 + u < PER && i < NV && q < A.b) {
+            if constexpr (CT == MIPS_BF16) {
+              if (A.qraw_f32) {
+                const float* p = (const float*)A.qraw + (int64_t)q * D + 16 * c + 8 * h;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                  v[u][t] = (uint32_t)f32_to_bf16(p[2 * t]) | ((uint32_t)f32_to_bf16(p[2 * t + 1]) << 16);
+              } else {
+                const uint32_t* p = (const uint32_t*)((const uint16_t*)A.qraw + (int64_t)q * D + 16 * c + 8 * h);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[u][t] = p[t];
+              }
+            } else {
+              const float* p = (const float*)A.qraw + (int64_t)q * D + 8 * c + h;
+#pragma unroll
+              for (int t = 0; t < 4; ++t) v[u][t] = __float_as_uint(p[2 * t]);
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kRawBatch; ++u) {
+          const int i = (i0 + u) * kScoreThreads + threadIdx.x;
+          if (i0 + u < PER && i < NV) {
+            dst[i] = v[u];
+            if (slice == 0 && i < n16) gdst[i] = v[u];
+          }
+        }
+      }
+      if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < A.nflags; i += kScoreThreads) A.ovf[i] = 0u;
+        if (threadIdx.x == 0) *A.nfail = 0u;
+      }
+      for (int i = threadIdx.x; i < QB; i += kScoreThreads) {
+        qid_lds[i] = qbase + i < A.b ? qbase + i : -1;
+        seg_lds[i] = 0u;
+      }
+      if constexpr (NT > 0)
+        for (int i = QB + threadIdx.x; i < QB * NT; i += kScoreThreads) seg_lds[i] = 0u;
+    } else if (!rescue) {
       const int rows = min(QB, A.b32 - qbase);
       const u32x4_t* src = (const u32x4_t*)(A.qtile + (int64_t)qbase * D * E);
       u32x4_t* dst = (u32x4_t*)lds;

@@ -68,6 +68,12 @@ __host__ __device__ constexpr bool main_doubles(int ct, int d) {
 __host__ __device__ constexpr int main_frags(int ct, int d) {
   return main_doubles(ct, d) ? 2 : stage_frags(ct, d);
 }
+// The sample pass builds the query operand tile itself (no separate prep kernel) for a bf16
+// or f32 index, where that takes no per-query scale, with two waves per SIMD and at most
+// 8 query fragments (beyond that the fill's registers would spill in the sample pass).
+__host__ __device__ constexpr bool fused_prep_ok(int ct, int d, int nqf) {
+  return (ct == MIPS_BF16 || ct == MIPS_F32) && score_wps(ct, d) == 2 && nqf <= 8;
+}
 // LDS of a score workgroup holding 32 * nqf queries: the query tile, 16 bytes of per-column
 // state per query and the survivor staging of every wave (8-byte key, 2-byte column). A
 // multi-mask pass (nt masks) adds a threshold and a survivor counter per column and mask.
@@ -111,6 +117,14 @@ struct ScoreArgs {
   int64_t mask_words;
   int nmask;
   int bv32;               // virtual queries rounded up to 32: the delegate stride
+  // Sample pass over a bf16 or f32 index: the raw queries ([b, D], f32 if qraw_f32, else
+  // bf16) from which each workgroup builds its operand tile; the slice-0 workgroup of each
+  // query block also writes the tile to qtile for the later passes, and workgroup 0 clears
+  // the per-list flags ovf[0, nflags) and *nfail. NULL: the tile is read from qtile.
+  const void* qraw;
+  int qraw_f32;
+  int nflags;
+  uint32_t* nfail;
 };
 
 // Launches score_kernel<CT, D, nqf, MODE, NT> (nqf in {1, 2, 4, 8, 16}; NT = 0 for one

@@ -643,14 +643,19 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   uint32_t* del = (uint32_t*)(ws + p.off_del);
   uint64_t* cand = (uint64_t*)(ws + p.off_cand);
 
-  if (p.qdt == MIPS_F32)
-    hipLaunchKernelGGL((prep_queries_kernel<CT, MIPS_F32, D>), dim3(p.b32 / 32 * chunks_per_block(CT, D)), dim3(64), 0, s,
-                       queries, p.b, qtile, qexp, ovf, p.bv, nfail);
-  else
-    hipLaunchKernelGGL((prep_queries_kernel<CT, MIPS_BF16, D>), dim3(p.b32 / 32 * chunks_per_block(CT, D)), dim3(64), 0, s,
-                       queries, p.b, qtile, qexp, ovf, p.bv, nfail);
-  int rc = check_launch();
-  if (rc) return rc;
+  // A sampled pass over a bf16 or f32 index builds the operand tile in its sample pass (no
+  // query scale to compute there); otherwise the prep kernel builds it.
+  const bool fused_prep = !p.dense && fused_prep_ok(CT, D, p.nqf);
+  int rc = MIPS_OK;
+  if (!fused_prep) {
+    if (p.qdt == MIPS_F32)
+      hipLaunchKernelGGL((prep_queries_kernel<CT, MIPS_F32, D>), dim3(p.b32 / 32 * chunks_per_block(CT, D)), dim3(64), 0, s,
+                         queries, p.b, qtile, qexp, ovf, p.bv, nfail);
+    else
+      hipLaunchKernelGGL((prep_queries_kernel<CT, MIPS_BF16, D>), dim3(p.b32 / 32 * chunks_per_block(CT, D)), dim3(64), 0, s,
+                         queries, p.b, qtile, qexp, ovf, p.bv, nfail);
+    if ((rc = check_launch())) return rc;
+  }
 
   ScoreArgs A{};
   A.corpus = (const uint8_t*)corpus;
@@ -732,7 +737,14 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   A.sample_step = ((uint64_t)p.n32 << 32) / (uint64_t)p.G;
   A.ntiles = (p.G + p.rm - 1) / p.rm;
   A.nslices = slices_for(A.ntiles, p.nqblk);
+  if (fused_prep) {
+    A.qraw = queries;
+    A.qraw_f32 = p.qdt == MIPS_F32;
+    A.nflags = p.bv;
+    A.nfail = nfail;
+  }
   if ((rc = launch_score_nqf<CT, D, MODE_SAMPLE, NT>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
+  A.qraw = nullptr;
   hipLaunchKernelGGL(sample_threshold_kernel, dim3(p.bv), dim3(kSelThreads), 0, s, del, (int)A.ntiles,
                      p.rm, NT > 0 ? p.bv32 : p.b32, p.bv, p.k, p.rest, thr, thrb);
   if ((rc = check_launch())) return rc;
