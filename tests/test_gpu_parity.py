@@ -723,3 +723,15 @@ def test_topk_masks_identical_masks_and_ragged_batches(b):
     s1, i1 = _scores_ids(q, corpus, k, _excl_tensor(bm, dev))
     for t in range(3):
         assert np.array_equal(i[t], i1) and np.array_equal(s[t].view(np.uint32), s1.view(np.uint32)), t
+
+
+def test_no_estimate_overflow_falls_back_to_exact_rescan():
+    """A bitmap that keeps only a contiguous run of 8,000 ids: too few sampled blocks hold
+    an eligible row for any estimate or bound, so the list is rescued with a threshold every
+    row passes; with room for about 2,048 candidates that rescue overflows, and the exact
+    rescan gives the result."""
+    n, d, b, k = 400_000, 64, 3, 100
+    keep = np.arange(100_000, 108_000)
+    bm = bitmap_from_ids(np.setdiff1d(np.arange(n), keep), n)
+    ws = mips.workspace_size(b, n, d, k, "bf16", "bf16", candidates_per_query=2048)
+    run_case(n, d, b, k, "bf16", "bf16", seed=95, bitmap=bm, workspace_bytes=ws)
