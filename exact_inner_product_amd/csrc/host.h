@@ -23,6 +23,10 @@ inline int check_launch() {
 
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// A launch counts its work-items per grid dimension in 32 bits. Row-wise kernels of 256
+// threads are split into launches of at most this many workgroups (2^30 work-items).
+constexpr int64_t kMaxGridBlocks = int64_t(1) << 22;
+
 inline bool corpus_d_supported(int dtype, int d) {
   if (dtype == MIPS_FP8_E4M3) return d == 64 || d == 128 || d == 256;
   if (dtype == MIPS_F32) return d == 16 || d == 32 || d == 64 || d == 128;

@@ -183,7 +183,8 @@ int mips_merge_interests(const float* in_scores, const int32_t* in_ids, int32_t 
                          void* stream) {
   if (!in_scores || !in_ids || !out_scores || !out_ids) return MIPS_ERR_INVALID_ARG;
   if (b < 1 || m < 1 || k_in < 1 || k_out < 1) return MIPS_ERR_INVALID_ARG;
-  if (k_out > MIPS_K_MAX || (int64_t)m * k_in > mips::kInterestEntries) return MIPS_ERR_UNSUPPORTED;
+  if (k_out > MIPS_K_MAX || b > MIPS_B_MAX || (int64_t)m * k_in > mips::kInterestEntries)
+    return MIPS_ERR_UNSUPPORTED;
   if (!mips::aligned(in_scores, 4) || !mips::aligned(in_ids, 4) || !mips::aligned(out_scores, 4) ||
       !mips::aligned(out_ids, 4))
     return MIPS_ERR_INVALID_ARG;
@@ -199,7 +200,7 @@ int mips_merge_topk(const float* in_scores, const int32_t* in_ids, const int64_t
   if (!in_scores || !in_ids || !offsets || !out_scores || !out_ids) return MIPS_ERR_INVALID_ARG;
   if (p < 1 || p > mips::kMergeMaxLists || b < 1 || k_in < 1 || k_out < 1)
     return MIPS_ERR_INVALID_ARG;
-  if (k_out > MIPS_K_MAX) return MIPS_ERR_UNSUPPORTED;
+  if (k_out > MIPS_K_MAX || b > MIPS_B_MAX) return MIPS_ERR_UNSUPPORTED;
   if ((int64_t)p * k_in > 0x7FFFFFFF) return MIPS_ERR_INVALID_ARG;
   if (!mips::aligned(in_scores, 4) || !mips::aligned(in_ids, 4) || !mips::aligned(out_scores, 4) ||
       !mips::aligned(out_ids, 4))

@@ -134,9 +134,14 @@ template <int DT, int D>
 static int launch_prepare(const float* src, int64_t rows, int64_t row_offset, void* dst,
                           float* row_scale, hipStream_t s) {
   const int64_t nblk = (rows + kFrag - 1) / kFrag;
-  hipLaunchKernelGGL((prepare_kernel<DT, D>), dim3((unsigned)nblk), dim3(256), 0, s, src, rows,
-                     row_offset / kFrag, (uint8_t*)dst, row_scale);
-  return check_launch();
+  for (int64_t b0 = 0; b0 < nblk; b0 += kMaxGridBlocks) {
+    const int64_t nb = nblk - b0 < kMaxGridBlocks ? nblk - b0 : kMaxGridBlocks;
+    hipLaunchKernelGGL((prepare_kernel<DT, D>), dim3((unsigned)nb), dim3(256), 0, s,
+                       src + b0 * kFrag * D, rows - b0 * kFrag, row_offset / kFrag + b0,
+                       (uint8_t*)dst, row_scale);
+    if (const int rc = check_launch()) return rc;
+  }
+  return MIPS_OK;
 }
 
 template <int DT>
@@ -169,17 +174,21 @@ int mips_l2_normalize(const float* src, int64_t rows, int32_t d, int32_t out_dty
   if (out_dtype != MIPS_F32 && out_dtype != MIPS_BF16) return MIPS_ERR_UNSUPPORTED;
   if (!mips::aligned(src, 4) || !mips::aligned(dst, out_dtype == MIPS_F32 ? 4 : 2))
     return MIPS_ERR_INVALID_ARG;
-  if (rows == 0) return MIPS_OK;
-  const int64_t grid = (rows + 3) / 4;
-  if (grid > 0x7FFFFFFF) return MIPS_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  if (out_dtype == MIPS_F32)
-    hipLaunchKernelGGL(mips::l2_normalize_kernel<MIPS_F32>, dim3((unsigned)grid), dim3(256), 0, s,
-                       src, rows, d, dst);
-  else
-    hipLaunchKernelGGL(mips::l2_normalize_kernel<MIPS_BF16>, dim3((unsigned)grid), dim3(256), 0,
-                       s, src, rows, d, dst);
-  return mips::check_launch();
+  // four rows per workgroup, in launches of at most kMaxGridBlocks workgroups
+  const int64_t per = mips::kMaxGridBlocks * 4;
+  for (int64_t r0 = 0; r0 < rows; r0 += per) {
+    const int64_t nr = rows - r0 < per ? rows - r0 : per;
+    const dim3 grid((unsigned)((nr + 3) / 4));
+    if (out_dtype == MIPS_F32)
+      hipLaunchKernelGGL(mips::l2_normalize_kernel<MIPS_F32>, grid, dim3(256), 0, s, src + r0 * d,
+                         nr, d, (void*)((float*)dst + r0 * d));
+    else
+      hipLaunchKernelGGL(mips::l2_normalize_kernel<MIPS_BF16>, grid, dim3(256), 0, s,
+                         src + r0 * d, nr, d, (void*)((uint16_t*)dst + r0 * d));
+    if (const int rc = mips::check_launch()) return rc;
+  }
+  return MIPS_OK;
 }
 
 int mips_prepare_corpus(const float* src, int64_t rows, int64_t row_offset, int32_t d,

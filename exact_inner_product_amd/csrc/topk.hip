@@ -800,7 +800,7 @@ static int validate_topk(int32_t qdt, int32_t b, int32_t cdt, int64_t n, int32_t
     return MIPS_ERR_UNSUPPORTED;
   if (cdt == MIPS_F32 && qdt != MIPS_F32) return MIPS_ERR_UNSUPPORTED;
   if (b < 1 || n < 1 || n > (int64_t)0x7FFFFFFF - 64 || k < 1) return MIPS_ERR_INVALID_ARG;
-  if (k > MIPS_K_MAX) return MIPS_ERR_UNSUPPORTED;
+  if (k > MIPS_K_MAX || b > MIPS_B_MAX) return MIPS_ERR_UNSUPPORTED;
   if (!corpus_d_supported(cdt, d)) return MIPS_ERR_UNSUPPORTED;
   return MIPS_OK;
 }
@@ -825,9 +825,9 @@ static int topk_entry(const void* queries, int32_t query_dtype, int32_t b, const
       return MIPS_ERR_INVALID_ARG;
   if (exclude_row_words < 0 || (exclude_row_words > 0 && (!exclude || exclude_row_words < (n + 31) / 32)))
     return MIPS_ERR_INVALID_ARG;
-  if (nmasks > 0 && (!masks || mask_words < (n + 31) / 32 || exclude || !aligned(masks, 4) ||
-                     (int64_t)b * nmasks > 0x3FFFFFFF))
+  if (nmasks > 0 && (!masks || mask_words < (n + 31) / 32 || exclude || !aligned(masks, 4)))
     return MIPS_ERR_INVALID_ARG;
+  if ((int64_t)b * std::max(nmasks, 1) > MIPS_B_MAX) return MIPS_ERR_UNSUPPORTED;
   if ((corpus_dtype == MIPS_FP8_E4M3 || corpus_dtype == MIPS_INT8) && !row_scale)
     return MIPS_ERR_INVALID_ARG;
   if (!aligned(queries, 4) || !aligned(corpus, 16) || !aligned(workspace, 256) ||
@@ -871,7 +871,7 @@ static int topk_entry(const void* queries, int32_t query_dtype, int32_t b, const
 static size_t workspace_bytes_for(int32_t b, int64_t n, int32_t d, int32_t k, int32_t qdt,
                                   int32_t cdt, int32_t nmasks, int64_t candidates) {
   if (validate_topk(qdt, b, cdt, n, d, k) != MIPS_OK) return 0;
-  if (nmasks < 0 || nmasks > kMaxMasks) return 0;
+  if (nmasks < 0 || nmasks > kMaxMasks || (int64_t)b * std::max(nmasks, 1) > MIPS_B_MAX) return 0;
   Plan p;
   make_plan(p, b, n, d, k, qdt, cdt, -1, 0, nmasks);
   const int64_t capw = candidates < 0 ? p.capw : (candidates + p.nseg - 1) / p.nseg;

@@ -57,6 +57,10 @@ extern "C" {
 /* Largest supported K. */
 #define MIPS_K_MAX 1024
 
+/* Largest supported number of result lists per call: b for mips_topk, mips_topk_ranges and
+ * the merges, b * nmasks for mips_topk_masks (each list is one workgroup of a launch). */
+#define MIPS_B_MAX 16777216
+
 /*
  * Packed corpus layout ("fragment-tiled"). Rows are grouped in blocks of 32
  * (N is padded up to a multiple of 32 with zero rows). Block g covers rows
@@ -149,7 +153,7 @@ MIPS_API size_t mips_topk_workspace_size_for(int32_t b, int64_t n, int32_t d, in
  * score descending, then id ascending.
  *   queries      device, [b, d] row-major, query_dtype MIPS_F32 or MIPS_BF16, assumed
  *                L2-normalised (use mips_l2_normalize); 4-byte aligned.
- *   b            >= 1.
+ *   b            1 .. MIPS_B_MAX.
  *   corpus       device, packed by mips_prepare_corpus (n rows, width d, corpus_dtype);
  *                16-byte aligned.
  *   row_scale    device, per-row scales for MIPS_FP8_E4M3 and MIPS_INT8 (NULL
@@ -183,8 +187,8 @@ MIPS_API size_t mips_topk_workspace_size_for(int32_t b, int64_t n, int32_t d, in
  *                undefined between calls. Calls that share a workspace must be ordered on
  *                one stream.
  * Errors: INVALID_ARG (NULL where a buffer is required, b/n/k out of range, fp8 or int8
- * without row_scale, misalignment), UNSUPPORTED (d, k > MIPS_K_MAX, dtype pair), WORKSPACE
- * (workspace_bytes too small), HIP (a launch failed); INVALID_ARG also for
+ * without row_scale, misalignment), UNSUPPORTED (d, k > MIPS_K_MAX, b > MIPS_B_MAX, dtype
+ * pair), WORKSPACE (workspace_bytes too small), HIP (a launch failed); INVALID_ARG also for
  * exclude_row_words < 0, or > 0 with a NULL exclude or below ceil(n/32).
  */
 MIPS_API int mips_topk(const void *queries, int32_t query_dtype, int32_t b, const void *corpus,
@@ -235,7 +239,8 @@ MIPS_API int mips_topk_ranges(const void *queries, int32_t query_dtype, int32_t 
  *                capacity, as mips_topk_workspace_size; 0 returned for invalid sizes).
  *   The other arguments, the ordering and the padding are as mips_topk's.
  * Errors: as mips_topk; INVALID_ARG for a NULL or misaligned masks, nmasks < 1 or
- * mask_words < ceil(n/32); UNSUPPORTED for nmasks > MIPS_MAX_MASKS.
+ * mask_words < ceil(n/32); UNSUPPORTED for nmasks > MIPS_MAX_MASKS or b * nmasks >
+ * MIPS_B_MAX.
  */
 #define MIPS_MAX_MASKS 4
 MIPS_API size_t mips_topk_masks_workspace_size(int32_t b, int64_t n, int32_t d, int32_t k,
@@ -272,14 +277,14 @@ MIPS_API int mips_type_bitmap(const int32_t *item_types, int64_t n, int32_t targ
  *   offsets      host int64 [p], each in [0, 2^31): list l's ids are shifted by
  *                offsets[l]. Shifted ids must be distinct across lists (disjoint
  *                indexes) and below 2^31.
- *   p            1 .. 64 lists; b >= 1 queries; k_in >= 1; k_out 1 .. MIPS_K_MAX.
+ *   p            1 .. 64 lists; b 1 .. MIPS_B_MAX queries; k_in >= 1; k_out 1 .. MIPS_K_MAX.
  *   out_scores   device float [b, k_out]; out_ids device int32 [b, k_out]: per query the
  *                k_out best real entries of all lists, score descending then id
  *                ascending, then (-INFINITY, -1). Exact for its inputs: when each list is
  *                its index's exact top-k_out, the result is the exact top-k_out of the
  *                union of the indexes.
  * Errors: INVALID_ARG (NULL, p/b/k out of range, an offset out of range, misaligned
- * pointers), UNSUPPORTED (k_out > MIPS_K_MAX), HIP (the launch failed).
+ * pointers), UNSUPPORTED (k_out > MIPS_K_MAX or b > MIPS_B_MAX), HIP (the launch failed).
  */
 MIPS_API int mips_merge_topk(const float *in_scores, const int32_t *in_ids, const int64_t *offsets,
                              int32_t p, int32_t b, int32_t k_in, int32_t k_out, float *out_scores,
@@ -296,11 +301,11 @@ MIPS_API int mips_merge_topk(const float *in_scores, const int32_t *in_ids, cons
  * maximum over the user's vectors.
  *   in_scores    device float [b, m, k_in] (user-major: rows u*m .. u*m+m-1 of a mips_topk
  *                output); in_ids device int32 [b, m, k_in], id < 0 is padding.
- *   b >= 1 users, m >= 1 vectors per user, k_in >= 1 with m * k_in <= 2048,
+ *   b 1 .. MIPS_B_MAX users, m >= 1 vectors per user, k_in >= 1 with m * k_in <= 2048,
  *   k_out 1 .. MIPS_K_MAX.
  *   out_scores   device float [b, k_out]; out_ids device int32 [b, k_out].
- * Errors: INVALID_ARG (NULL, b/m/k < 1, misaligned pointers), UNSUPPORTED (m * k_in > 2048
- * or k_out > MIPS_K_MAX), HIP (the launch failed).
+ * Errors: INVALID_ARG (NULL, b/m/k < 1, misaligned pointers), UNSUPPORTED (m * k_in > 2048,
+ * k_out > MIPS_K_MAX or b > MIPS_B_MAX), HIP (the launch failed).
  */
 MIPS_API int mips_merge_interests(const float *in_scores, const int32_t *in_ids, int32_t b, int32_t m,
                                   int32_t k_in, int32_t k_out, float *out_scores, int32_t *out_ids,

@@ -254,3 +254,46 @@ def test_topk_masks_validation_and_workspace(L):
     assert call(q=None) == INVALID
     assert call(k=1025) == UNSUPPORTED
     assert call(wsb=1024) == WORKSPACE
+
+
+def test_header_limits_match_the_binding():
+    text = open(HEADER).read()
+    limits = dict(re.findall(r"#define (MIPS_\w*MAX\w*) (\d+)", text))
+    assert int(limits["MIPS_K_MAX"]) == mips.K_MAX
+    assert int(limits["MIPS_B_MAX"]) == mips.B_MAX
+    assert int(limits["MIPS_MAX_MASKS"]) == mips.MAX_MASKS
+
+
+def test_batch_limit_rejected_before_launch(L):
+    """More result lists than MIPS_B_MAX (one workgroup each) are refused on the host."""
+    vp = C.c_void_p
+    big = mips.B_MAX + 1
+    assert _topk(L, b=big) == UNSUPPORTED
+    assert L.mips_topk_workspace_size(big, 1000, 128, 10, BF16, BF16) == 0
+    assert L.mips_topk_workspace_size_for(big, 1000, 128, 10, BF16, BF16, 100) == 0
+    # four masks: b * 4 lists
+    quarter = mips.B_MAX // 4 + 1
+    assert L.mips_topk_masks_workspace_size(quarter, 1000, 128, 10, BF16, BF16, 4, 0) == 0
+    assert L.mips_topk_masks(vp(0x1000), BF16, quarter, vp(0x2000), None, BF16, 1000, 128,
+                             vp(0x6000), 4, 32, 10, vp(0x3000), vp(0x4000), vp(0x10000), 1 << 30,
+                             None) == UNSUPPORTED
+    offs = (C.c_int64 * 2)(0, 100)
+    assert L.mips_merge_topk(vp(0x1000), vp(0x2000), C.cast(offs, vp), 2, big, 10, 10, vp(0x3000),
+                             vp(0x4000), None) == UNSUPPORTED
+    assert L.mips_merge_interests(vp(0x1000), vp(0x2000), big, 2, 10, 10, vp(0x3000), vp(0x4000),
+                                  None) == UNSUPPORTED
+
+
+def test_lattice_rows_agree_between_numpy_and_torch():
+    """The deterministic pattern that large GPU inputs are built from: numpy and torch give the
+    same float32 bits, including rows past 2^27."""
+    import numpy as np
+    from workloads import lattice_rows
+    for r0, r1, d in ((0, 40, 16), ((1 << 27) - 7, (1 << 27) + 33, 16), (1000, 1003, 128)):
+        a = lattice_rows(r0, r1, d)
+        b = lattice_rows(r0, r1, d, "cpu").numpy()
+        assert a.dtype == np.float32 and a.shape == (r1 - r0, d)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    first = lattice_rows(0, 1, 4)[0]
+    want = [((12345 + j * 40503) >> 7) % 4093 - 2046 for j in range(4)]
+    assert first.tolist() == [w / 256.0 for w in want]

@@ -144,3 +144,59 @@ def test_bf16_n10m_four_masks():
                            w.corpus_dtype, scale, excluded, w.n, TOL[w.corpus_dtype],
                            floor=floor_for(w.corpus_dtype, w.query_dtype))
         print(f"four masks: mask {t}: {stats}", flush=True)
+
+
+def _bf16_close(got, want):
+    """bf16 codes that differ by at most one step (fp32 normalisation on the GPU, fp64 in the
+    oracle, each rounded to nearest even)."""
+    gv, ov = oracle.decode(got, "bf16"), oracle.decode(want, "bf16")
+    return np.all(np.abs(gv - ov) <= np.abs(ov) * 2.0 ** -7 + 1e-30)
+
+
+@pytest.mark.timeout(600)
+def test_row_kernels_past_the_launch_work_item_limit():
+    """A launch counts its work-items in 32 bits, so row-wise kernels of more than 2^22
+    workgroups go out as several launches: l2_normalize at 2^24 + 5 rows (4 rows per
+    workgroup) and the index build at 2^27 + 40 rows (one 32-row block per workgroup, D=16
+    bf16: 8.6 GB in, 4.3 GB out). Rows on both sides of each split, the first rows and the
+    last (partial) block match the oracle. The input is a deterministic integer pattern
+    built on the GPU; the oracle rebuilds the sampled rows on the host."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from tests.mips_check import untile
+    from workloads import lattice_rows
+    dev = torch.device("cuda:0")
+    d = 16
+
+    rows = 4 * (1 << 22) + 5
+    print(f"launch split: l2_normalize rows={rows} d={d}", flush=True)
+    x = lattice_rows(0, rows, d, dev)
+    y = mips.l2_normalize(x, "f32")
+    torch.cuda.synchronize()
+    del x
+    cut = 4 * (1 << 22)
+    for r0, r1 in ((0, 3), (cut - 3, cut + 3), (rows - 2, rows)):
+        want = oracle.normalize(lattice_rows(r0, r1, d))
+        got = y[r0:r1].cpu().numpy().astype(np.float64)
+        assert np.allclose(got, want, rtol=4e-7, atol=1e-30), (r0, r1)
+    del y
+
+    rows = 32 * (1 << 22) + 40
+    nblk = (rows + 31) // 32
+    print(f"launch split: prepare_corpus bf16 rows={rows} d={d} blocks={nblk}", flush=True)
+    x = torch.empty(rows, d, dtype=torch.float32, device=dev)
+    step = 1 << 24
+    for r0 in range(0, rows, step):
+        x[r0:r0 + step] = lattice_rows(r0, min(rows, r0 + step), d, dev)
+    corpus = mips.prepare_corpus(x, "bf16")
+    torch.cuda.synchronize()
+    del x
+    bb = 32 * d * 2
+    for g in (0, (1 << 22) - 1, 1 << 22, nblk - 1):
+        live = min(32, rows - 32 * g)
+        got = untile(corpus.packed[g * bb:(g + 1) * bb].cpu().numpy(), 32, d, "bf16")
+        want, _ = oracle.prepare(lattice_rows(32 * g, 32 * g + live, d), "bf16")
+        assert _bf16_close(got[:live], want), f"block {g}"
+        assert np.all(got[live:] == 0), f"block {g}: padding rows"
+    del corpus
+    torch.cuda.empty_cache()

@@ -210,6 +210,24 @@ def typed_masks(n: int, base: Optional[np.ndarray] = None, seed: int = 20261203)
     return rows
 
 
+def lattice_rows(r0: int, r1: int, d: int, device=None):
+    """Raw rows r0..r1-1 of a deterministic pattern, float32 [r1 - r0, d]: element (r, j) is
+    ((r * 2654435761 + j * 40503 + 12345) >> 7) % 4093 - 2046, divided by 256. Every value
+    is exact in float32, so a GPU-side build (`device` given: a torch tensor made there)
+    and a numpy build (`device` None) agree bit for bit. For inputs too large to draw on the
+    host: rows far apart can be regenerated one by one."""
+    if device is None:
+        r = np.arange(r0, r1, dtype=np.int64)[:, None]
+        j = np.arange(d, dtype=np.int64)[None, :]
+        v = ((r * 2654435761 + j * 40503 + 12345) >> 7) % 4093 - 2046
+        return (v.astype(np.float32) / np.float32(256.0)).astype(np.float32)
+    import torch
+    r = torch.arange(r0, r1, dtype=torch.int64, device=device)[:, None]
+    j = torch.arange(d, dtype=torch.int64, device=device)[None, :]
+    v = torch.bitwise_right_shift(r * 2654435761 + j * 40503 + 12345, 7) % 4093 - 2046
+    return v.to(torch.float32) / 256.0
+
+
 def bitmap_from_ids(ids: np.ndarray, n: int) -> np.ndarray:
     """uint32[ceil(n/32)]; bit (i & 31) of word (i >> 5) set <=> id i excluded."""
     words = np.zeros((n + 31) // 32, np.uint32)
