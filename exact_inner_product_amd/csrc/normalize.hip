@@ -16,11 +16,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
 
 // One wave per row. Lane j sums dims j, j+64, ...; the butterfly fixes the order.
 template <int OUT>
@@ -44,89 +39,108 @@ __global__ __launch_bounds__(256) void l2_normalize_kernel(const float* __restri
   }
 }
 
-// One workgroup (4 waves) per packed 32-row block. Phase 1: each wave normalises 8
-// rows' norms (and, for E4M3, the row's power-of-two scale; for int8, max|y| / 127). Phase 2: the block's
-// 1 KiB chunks are written, one 16-byte slot per lane, so stores are fully coalesced.
-template <int DT, int D>
+// One workgroup (4 waves) per packed 32-row block, one pass over its input. Lane l of a
+// wave owns slot l of the wave's chunks: row l & 31 and the P = 16 / E dimensions of that
+// slot, which it loads once (bf16, fp8 and int8 slots hold P consecutive dimensions; an f32
+// slot holds every other dimension of 8 consecutive ones, so the lane loads the 8 and keeps
+// its 4). The row's sum of squares and max |x| are reduced over the lane pair (l, l ^ 32)
+// and the 4 waves in LDS; each lane then converts its values from registers and writes its
+// 16-byte slot, so loads and stores are 1 KiB per wave instruction. VEC: src is 16-byte
+// aligned and slots are read with 16-byte loads.
+template <int DT, int D, bool VEC>
 __global__ __launch_bounds__(256) void prepare_kernel(const float* __restrict__ src, int64_t rows,
                                                       int64_t block0, uint8_t* __restrict__ dst,
                                                       float* __restrict__ row_scale) {
   constexpr int NCH = chunks_per_block(DT, D);
-  __shared__ float s_norm[kFrag];
-  __shared__ float s_scale_inv[kFrag];
+  constexpr int CPW = (NCH + 3) / 4;  // chunks per wave: wave w has chunks w*CPW ..
+  constexpr int P = DT == MIPS_F32 ? 4 : (DT == MIPS_BF16 ? 8 : 16);
+  constexpr int L = DT == MIPS_F32 ? 8 : P;  // floats loaded per slot
+  __shared__ float s_ss[4][kFrag];
+  __shared__ float s_mx[4][kFrag];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t blk = blockIdx.x;             // block within this call
-  const int64_t row_base = blk * kFrag;       // local row of the block's first row
+  const int r = lane & 31;
+  const int h = lane >> 5;
+  const int64_t blk = blockIdx.x;  // block within this call
+  const int64_t lr = blk * kFrag + r;
+  const bool live = lr < rows;
+  const float* x = src + lr * D;  // read only for live rows
 
-  for (int r = wave; r < kFrag; r += 4) {
-    const int64_t lr = row_base + r;
-    float nrm = 1.0f, amax = 0.0f;
-    if (lr < rows) {
-      const float* x = src + lr * D;
-      float ss = 0.0f;
-      for (int j = lane; j < D; j += kWave) ss = fmaf(x[j], x[j], ss);
-      ss = wave_sum(ss);
-      nrm = sqrtf(fmaxf(ss, kNormEps));
-      if (DT == MIPS_FP8_E4M3 || DT == MIPS_INT8) {
-        float m = 0.0f;
-        for (int j = lane; j < D; j += kWave) m = fmaxf(m, fabsf(x[j] / nrm));
-        amax = wave_max(m);
+  float v[CPW][P];
+  float ss = 0.0f, mx = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int c = wave * CPW + i;
+    const bool on = live && c < NCH;
+    const int base = DT == MIPS_F32 ? 8 * c : slot_dim(DT, c, lane, 0);
+    float f[L];
+#pragma unroll
+    for (int u = 0; u < L; u += 4) {
+      if (VEC) {
+        const float4 a = on ? *(const float4*)(x + base + u) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        f[u] = a.x;
+        f[u + 1] = a.y;
+        f[u + 2] = a.z;
+        f[u + 3] = a.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[u + e] = on ? x[base + u + e] : 0.0f;
       }
     }
-    if (lane == 0) {
-      s_norm[r] = nrm;
-      if (DT == MIPS_FP8_E4M3) {
-        int t = e4m3_scale_exp(amax);
-        t = t < -126 ? -126 : t;
-        s_scale_inv[r] = exp2_int(-t);
-        row_scale[(block0 + blk) * kFrag + r] = exp2_int(t);
-      } else if (DT == MIPS_INT8) {
-        const float sc = i8_scale(amax);
-        s_scale_inv[r] = sc;  // int8 divides by the scale itself
-        row_scale[(block0 + blk) * kFrag + r] = sc;
-      }
+#pragma unroll
+    for (int t = 0; t < P; ++t) {
+      v[i][t] = DT == MIPS_F32 ? (h ? f[2 * t + 1] : f[2 * t]) : f[t];
+      ss = fmaf(v[i][t], v[i][t], ss);
+      mx = fmaxf(mx, fabsf(v[i][t]));
     }
   }
+  ss += __shfl_xor(ss, 32, kWave);
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  if (lane < kFrag) {
+    s_ss[wave][r] = ss;
+    s_mx[wave][r] = mx;
+  }
   __syncthreads();
+  float nrm = 1.0f, amax = 0.0f;
+  if (live) {
+    nrm = sqrtf(fmaxf((s_ss[0][r] + s_ss[1][r]) + (s_ss[2][r] + s_ss[3][r]), kNormEps));
+    // division is monotone, so max |x| / nrm is the max of |x_j| / nrm
+    amax = fmaxf(fmaxf(s_mx[0][r], s_mx[1][r]), fmaxf(s_mx[2][r], s_mx[3][r])) / nrm;
+  }
+  float sdiv = 1.0f;  // int8: the codes are y / scale; fp8: y * 2^-t
+  if (DT == MIPS_FP8_E4M3) {
+    int t = e4m3_scale_exp(amax);
+    t = t < -126 ? -126 : t;
+    sdiv = exp2_int(-t);
+    if (wave == 0 && lane < kFrag) row_scale[(block0 + blk) * kFrag + r] = exp2_int(t);
+  } else if (DT == MIPS_INT8) {
+    sdiv = i8_scale(amax);
+    if (wave == 0 && lane < kFrag) row_scale[(block0 + blk) * kFrag + r] = sdiv;
+  }
 
   uint8_t* out = dst + (block0 + blk) * block_bytes(DT, D);
-  for (int c = wave; c < NCH; c += 4) {
-    const int r = lane & 31;
-    const int64_t lr = row_base + r;
-    const bool live = lr < rows;
-    const float* x = src + lr * D;
-    const float nrm = s_norm[r];
-    u32x4_t v = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int c = wave * CPW + i;
+    if (c >= NCH) break;
+    u32x4_t o = {0u, 0u, 0u, 0u};
     if (DT == MIPS_F32) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const float y = live ? x[slot_dim(DT, c, lane, t)] / nrm : 0.0f;
-        v[t] = __float_as_uint(y);
-      }
+      for (int t = 0; t < 4; ++t) o[t] = __float_as_uint(v[i][t] / nrm);
     } else if (DT == MIPS_BF16) {
 #pragma unroll
-      for (int t = 0; t < 8; t += 2) {
-        const float y0 = live ? x[slot_dim(DT, c, lane, t)] / nrm : 0.0f;
-        const float y1 = live ? x[slot_dim(DT, c, lane, t + 1)] / nrm : 0.0f;
-        v[t >> 1] = (uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16);
-      }
+      for (int t = 0; t < 8; t += 2)
+        o[t >> 1] = (uint32_t)f32_to_bf16(v[i][t] / nrm) |
+                    ((uint32_t)f32_to_bf16(v[i][t + 1] / nrm) << 16);
     } else if (DT == MIPS_INT8) {
-      const float sc = s_scale_inv[r];
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const float y = live ? (x[slot_dim(DT, c, lane, t)] / nrm) / sc : 0.0f;
-        v[t >> 2] |= f32_to_i8(y) << (8 * (t & 3));
-      }
+      for (int t = 0; t < 16; ++t) o[t >> 2] |= f32_to_i8((v[i][t] / nrm) / sdiv) << (8 * (t & 3));
     } else {
-      const float sinv = s_scale_inv[r];
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const float y = live ? (x[slot_dim(DT, c, lane, t)] / nrm) * sinv : 0.0f;
-        v[t >> 2] |= (uint32_t)f32_to_e4m3(y) << (8 * (t & 3));
-      }
+      for (int t = 0; t < 16; ++t)
+        o[t >> 2] |= (uint32_t)f32_to_e4m3((v[i][t] / nrm) * sdiv) << (8 * (t & 3));
     }
-    *(u32x4_t*)(out + (int64_t)c * kChunkBytes + lane * 16) = v;
+    *(u32x4_t*)(out + (int64_t)c * kChunkBytes + lane * 16) = o;
   }
 }
 
@@ -134,11 +148,17 @@ template <int DT, int D>
 static int launch_prepare(const float* src, int64_t rows, int64_t row_offset, void* dst,
                           float* row_scale, hipStream_t s) {
   const int64_t nblk = (rows + kFrag - 1) / kFrag;
+  const bool vec = aligned(src, 16);  // rows are 64-byte multiples: every row stays aligned
   for (int64_t b0 = 0; b0 < nblk; b0 += kMaxGridBlocks) {
     const int64_t nb = nblk - b0 < kMaxGridBlocks ? nblk - b0 : kMaxGridBlocks;
-    hipLaunchKernelGGL((prepare_kernel<DT, D>), dim3((unsigned)nb), dim3(256), 0, s,
-                       src + b0 * kFrag * D, rows - b0 * kFrag, row_offset / kFrag + b0,
-                       (uint8_t*)dst, row_scale);
+    if (vec)
+      hipLaunchKernelGGL((prepare_kernel<DT, D, true>), dim3((unsigned)nb), dim3(256), 0, s,
+                         src + b0 * kFrag * D, rows - b0 * kFrag, row_offset / kFrag + b0,
+                         (uint8_t*)dst, row_scale);
+    else
+      hipLaunchKernelGGL((prepare_kernel<DT, D, false>), dim3((unsigned)nb), dim3(256), 0, s,
+                         src + b0 * kFrag * D, rows - b0 * kFrag, row_offset / kFrag + b0,
+                         (uint8_t*)dst, row_scale);
     if (const int rc = check_launch()) return rc;
   }
   return MIPS_OK;

@@ -107,7 +107,8 @@ MIPS_API int mips_l2_normalize(const float *src, int64_t rows, int32_t d, int32_
  *               row_offset .. row_offset+rows-1 of the corpus.
  *   row_offset  multiple of 32 (lets a large corpus be packed in chunks).
  *   rows        >= 1. If rows is not a multiple of 32, this must be the last chunk: the
- *               rest of the last block is written as zero rows (scale 1).
+ *               rest of the last block is written as zero rows (with a zero row's
+ *               scale: 1 for fp8, 1e-12 for int8).
  *   d           16, 32, 64, 128 or 256 (MIPS_F32: up to 128; MIPS_FP8_E4M3: 64, 128,
  *               256; MIPS_INT8: 32 .. 256).
  *   dtype       MIPS_F32 (rounded to nearest), MIPS_BF16 (nearest even),

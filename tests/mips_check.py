@@ -18,6 +18,10 @@ import oracle
 TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "int8": 6e-2}
 # Expected error floors: fp32 accumulation of the same stored operands (f32, bf16) and
 # E4M3 quantisation of the queries (fp8). Far above these means a bug even inside TOL.
+# A bf16 index also gets one code step per returned row (check_topk): the GPU normalises
+# rows in fp32 and the oracle in fp64, so about one stored element in 10^5 rounds to the
+# neighbouring bf16 code; one step of element d moves a score by |q_d| ulp(c_d), at most
+# 2^-7 |q_d c_d| (8 significant bits).
 FLOOR = {"f32": 2e-6, "bf16": 5e-4, "fp8": 3e-2, "int8": 1e-2}
 
 
@@ -97,6 +101,14 @@ def check_topk(g_scores: np.ndarray, g_ids: np.ndarray, o_scores: np.ndarray, o_
         err = np.abs(sc - e).max()
         stats["max_err"] = max(stats["max_err"], float(err))
         assert err <= tau, f"query {qi}: score error {err} > {tau}"
+        if floor is not None:
+            allow = np.full(kk, floor)
+            if c_dtype == "bf16":
+                qv = oracle.decode(q_codes[qi], q_dtype)
+                cv = oracle.decode(c_codes[ids], c_dtype)
+                allow += 2.0 ** -7 * np.abs(cv * qv).max(axis=1)
+            over = np.abs(sc - e) - allow
+            stats["max_over_floor"] = max(stats.get("max_over_floor", -np.inf), float(over.max()))
         # 3. profile
         prof = np.abs(sc - o_scores[qi, :kk]).max()
         stats["max_profile"] = max(stats["max_profile"], float(prof))
@@ -111,7 +123,8 @@ def check_topk(g_scores: np.ndarray, g_ids: np.ndarray, o_scores: np.ndarray, o_
                 f"query {qi}: id swap beyond tolerance"
             stats["swaps"] += len(diff) // 2
     if floor is not None:
-        assert stats["max_err"] <= floor, f"error {stats['max_err']} far above the expected floor {floor}"
+        assert stats.get("max_over_floor", -np.inf) <= 0.0, \
+            f"error {stats['max_err']} far above the expected floor {floor} (+ one bf16 step)"
     return stats
 
 

@@ -63,9 +63,10 @@ def run_case(n, d, b, k, cdt, qdt, seed, excl=0.0, workspace_bytes=None, x=None,
 
 
 # --------------------------------------------------------------- prepare parity
-@pytest.mark.parametrize("dtype,d", [("f32", 16), ("f32", 64), ("bf16", 32), ("bf16", 128),
-                                     ("bf16", 256), ("fp8", 64), ("fp8", 256), ("int8", 32),
-                                     ("int8", 128), ("int8", 256)])
+@pytest.mark.parametrize("dtype,d", [("f32", 16), ("f32", 64), ("f32", 128), ("bf16", 16),
+                                     ("bf16", 32), ("bf16", 64), ("bf16", 128), ("bf16", 256),
+                                     ("fp8", 64), ("fp8", 128), ("fp8", 256), ("int8", 32),
+                                     ("int8", 64), ("int8", 128), ("int8", 256)])
 def test_prepare_matches_oracle_codes(dtype, d):
     dev = _dev()
     rng = np.random.default_rng(d)
@@ -112,6 +113,36 @@ def test_prepare_matches_oracle_codes(dtype, d):
     bound = np.maximum(np.abs(gv), np.abs(ov)) * 2.0 ** -ulp_bits + (2.0 ** -9) * (1 if gs is None else np.maximum(gs, scale)[:, None])
     assert np.all(diff <= bound)
     assert np.all(got[5] == 0)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 16), ("f32", 128), ("bf16", 64), ("bf16", 256),
+                                     ("fp8", 128), ("int8", 32), ("int8", 256)])
+def test_prepare_unaligned_source_matches_aligned(dtype, d):
+    """A source that is 4- but not 16-byte aligned is read with 4-byte loads instead of
+    16-byte ones; the packed bytes and row scales are the same, bit for bit. Two chunks with
+    a row offset, the second ragged."""
+    dev = _dev()
+    rng = np.random.default_rng(100 + d)
+    n = 32 * 37 + 11
+    x = (rng.standard_normal((n, d)) * rng.uniform(0.01, 30, (n, 1))).astype(np.float32)
+    x[3] = 0.0
+    flat = torch.empty(n * d + 1, dtype=torch.float32, device=dev)
+    flat[1:] = torch.from_numpy(x.ravel()).to(dev)
+    shifted = flat[1:].view(n, d)
+    assert shifted.data_ptr() % 16 == 4
+    aligned = torch.from_numpy(x).to(dev)
+    assert aligned.data_ptr() % 16 == 0
+    print(f"prepare unaligned {dtype} d={d} n={n}", flush=True)
+    out = []
+    for src in (aligned, shifted):
+        c = mips.empty_corpus(n, d, dtype, dev)
+        mips.prepare_rows(c, src[:32 * 20], 0)
+        mips.prepare_rows(c, src[32 * 20:], 32 * 20)
+        out.append(c)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0].packed, out[1].packed)
+    if out[0].row_scale is not None:
+        assert torch.equal(out[0].row_scale.view(torch.int32), out[1].row_scale.view(torch.int32))
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
