@@ -6,7 +6,8 @@ shares no code with the HIP library.
 
 Functions take and return numpy arrays:
 
-* ``prepare(x, dtype)`` -- normalise raw fp32 rows and pack them row-major
+* ``prepare(x, dtype)`` -- normalise raw fp32 rows in binary32 (the precision of the
+  Model's float32 tensors) and pack them row-major, every code decided from that value
   (``"f32"`` -> float32, ``"bf16"`` -> uint16 codes, ``"fp8"`` -> uint8 E4M3 codes plus a
   float32 per-row power-of-two scale, ``"int8"`` -> int8 codes plus a float32 per-row
   scale max|y|/127).

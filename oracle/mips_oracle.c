@@ -10,7 +10,10 @@
  *
  *  - l2 normalisation: y = x / sqrt(max(sum x^2, 1e-12)), the form of
  *    `_l2_normalize_candidates` and of the user-representation normalisation in
- *    recsys_two_tower_model.py (x-algorithm Phoenix). Done in fp64.
+ *    recsys_two_tower_model.py (x-algorithm Phoenix). oracle_l2_normalize gives the
+ *    value in fp64. The index build decides its stored codes from the row normalised
+ *    in binary32, the precision of the Model's float32 tensors: the sum of squares in
+ *    dimension order, the square root and each quotient rounded to binary32.
  *  - packing of the normalised index into a narrow type, as "normalise once at
  *    index time; store f16/int8" ("Two-tower retrieval", mhtirogla.ai, section
  *    "Implementation notes") and the bf16 `post_embeddings` index of
@@ -201,11 +204,30 @@ int oracle_l2_normalize(const float *x, int64_t rows, int32_t d, double *y)
     return OR_OK;
 }
 
-/* Normalise `rows` raw rows and pack them row-major into `out`:
- *   OR_F32:  float  [rows, d]  (y rounded to binary32, nearest-even)
+/* One row normalised in binary32: ss = sum of x_d * x_d in dimension order, nrm =
+ * sqrt(max(ss, 1e-12)), y_d = x_d / nrm, every operation rounded to binary32 (the
+ * build turns floating-point contraction off, so a product is rounded before its sum). */
+static int normalize_row_f32(const float *xr, int32_t d, float *y)
+{
+    float ss = 0.0f;
+    for (int32_t j = 0; j < d; ++j) {
+        if (!isfinite(xr[j]))
+            return OR_NONFINITE;
+        ss = ss + xr[j] * xr[j];
+    }
+    const float nrm = sqrtf(fmaxf(ss, 1e-12f));
+    for (int32_t j = 0; j < d; ++j)
+        y[j] = xr[j] / nrm;
+    return OR_OK;
+}
+
+/* Normalise `rows` raw rows (binary32, normalize_row_f32) and pack them row-major into
+ * `out`; every code is decided from the binary32 value:
+ *   OR_F32:  float  [rows, d]  (y itself)
  *   OR_BF16: uint16 [rows, d]  (bf16 codes)
  *   OR_E4M3: uint8  [rows, d]  (E4M3 codes of y / scale) and scale[rows] (float)
- *   OR_I8:   int8   [rows, d]  (int8 codes of y / scale) and scale[rows] (float)
+ *   OR_I8:   int8   [rows, d]  (int8 codes of y / scale, the quotient and the scale
+ *            max(max|y| / 127, 1e-12) in binary32) and scale[rows] (float)
  */
 int oracle_prepare(const float *x, int64_t rows, int32_t d, int32_t dtype, void *out,
                    float *scale)
@@ -214,38 +236,36 @@ int oracle_prepare(const float *x, int64_t rows, int32_t d, int32_t dtype, void 
         return OR_BAD_ARG;
     if ((dtype == OR_E4M3 || dtype == OR_I8) && !scale)
         return OR_BAD_ARG;
-    double *y = (double *)malloc(sizeof(double) * (size_t)d);
+    float *y = (float *)malloc(sizeof(float) * (size_t)d);
     if (!y)
         return OR_NOMEM;
     for (int64_t r = 0; r < rows; ++r) {
-        int rc = oracle_l2_normalize(x + r * (int64_t)d, 1, d, y);
+        int rc = normalize_row_f32(x + r * (int64_t)d, d, y);
         if (rc != OR_OK) {
             free(y);
             return rc;
         }
         int64_t base = r * (int64_t)d;
+        float amax = 0.0f;
+        for (int32_t j = 0; j < d; ++j)
+            amax = fmaxf(amax, fabsf(y[j]));
         if (dtype == OR_F32) {
             for (int32_t j = 0; j < d; ++j)
-                ((float *)out)[base + j] = (float)y[j];
+                ((float *)out)[base + j] = y[j];
         } else if (dtype == OR_BF16) {
             for (int32_t j = 0; j < d; ++j)
-                ((uint16_t *)out)[base + j] = oracle_bf16_from_f64(y[j]);
+                ((uint16_t *)out)[base + j] = oracle_bf16_from_f64((double)y[j]);
         } else if (dtype == OR_E4M3) {
-            double amax = 0.0;
-            for (int32_t j = 0; j < d; ++j)
-                amax = fmax(amax, fabs(y[j]));
-            double s = oracle_e4m3_row_scale(amax);
+            /* a power of two: y / s is exact */
+            double s = oracle_e4m3_row_scale((double)amax);
             scale[r] = (float)s;
             for (int32_t j = 0; j < d; ++j)
-                ((uint8_t *)out)[base + j] = oracle_e4m3_from_f64(y[j] / s);
+                ((uint8_t *)out)[base + j] = oracle_e4m3_from_f64((double)y[j] / s);
         } else {
-            double amax = 0.0;
+            const float s = fmaxf(amax / 127.0f, 1e-12f);
+            scale[r] = s;
             for (int32_t j = 0; j < d; ++j)
-                amax = fmax(amax, fabs(y[j]));
-            double s = oracle_i8_row_scale(amax);
-            scale[r] = (float)s;
-            for (int32_t j = 0; j < d; ++j)
-                ((int8_t *)out)[base + j] = oracle_i8_from_f64(y[j] / s);
+                ((int8_t *)out)[base + j] = oracle_i8_from_f64((double)(y[j] / s));
         }
     }
     free(y);

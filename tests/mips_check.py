@@ -18,10 +18,10 @@ import oracle
 TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "int8": 6e-2}
 # Expected error floors: fp32 accumulation of the same stored operands (f32, bf16) and
 # E4M3 quantisation of the queries (fp8). Far above these means a bug even inside TOL.
-# A bf16 index also gets one code step per returned row (check_topk): the GPU normalises
-# rows in fp32 and the oracle in fp64, so about one stored element in 10^5 rounds to the
-# neighbouring bf16 code; one step of element d moves a score by |q_d| ulp(c_d), at most
-# 2^-7 |q_d c_d| (8 significant bits).
+# A bf16 index also gets one code step per returned row (check_topk): the GPU and the
+# oracle both normalise rows in binary32 but sum the squares in different orders, so about
+# one stored element in 10^5 rounds to the neighbouring bf16 code; one step of element d
+# moves a score by |q_d| ulp(c_d), at most 2^-7 |q_d c_d| (8 significant bits).
 FLOOR = {"f32": 2e-6, "bf16": 5e-4, "fp8": 3e-2, "int8": 1e-2}
 
 
