@@ -21,7 +21,7 @@ F32, BF16, FP8_E4M3, INT8 = 0, 1, 2, 3
 DTYPE_CODES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "int8": INT8}
 SCALED = ("fp8", "int8")  # packed with one float scale per row
 K_MAX = 1024
-B_MAX = 1 << 24  # result lists per call (queries, or queries x masks)
+B_MAX = 1 << 23  # result lists per call (queries, or queries x masks)
 
 EXPORTS = (
     "mips_corpus_bytes", "mips_scale_count", "mips_l2_normalize", "mips_prepare_corpus",

@@ -58,8 +58,9 @@ extern "C" {
 #define MIPS_K_MAX 1024
 
 /* Largest supported number of result lists per call: b for mips_topk, mips_topk_ranges and
- * the merges, b * nmasks for mips_topk_masks (each list is one workgroup of a launch). */
-#define MIPS_B_MAX 16777216
+ * the merges, b * nmasks for mips_topk_masks. Each list is one 256-thread workgroup of a
+ * launch, whose work-item count must stay below 2^32. */
+#define MIPS_B_MAX 8388608
 
 /*
  * Packed corpus layout ("fragment-tiled"). Rows are grouped in blocks of 32
