@@ -200,3 +200,79 @@ def test_row_kernels_past_the_launch_work_item_limit():
         assert np.all(got[live:] == 0), f"block {g}: padding rows"
     del corpus
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_bf16_n_at_the_id_limit():
+    """N = 2^31 - 65, the largest index the C ABI takes (int32 ids), at D=16 bf16 (68.7 GB
+    packed). The rows follow workloads.lattice_rows, which repeats every P = 128 * 4093 rows,
+    so every row but the planted ones scores exactly as its residue id mod P. Three query
+    vectors are planted, one each in the last (ragged) block, in the block before it and at
+    id 5. The exact top-K therefore merges the planted rows with the first duplicates of the
+    best residues, whose exact scores the oracle computes on one period (523,904 rows).
+    The check: the GPU's ids equal that list except swaps within tolerance of the K-th
+    score, and every returned score is within tolerance of its row's exact score."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from workloads import Workload, lattice_rows
+    dev = torch.device("cuda:0")
+    n, d, k, P = (1 << 31) - 65, 16, 10, 128 * 4093
+    assert n == 0x7FFFFFFF - 64
+    qraw = Workload("planted", "clustered", n=64, d=d, b=3, k=k, corpus_dtype="bf16",
+                    query_dtype="bf16", clusters=2, seed=31).queries()
+    planted = [n - 1, n - 40, 5]  # planted[u] holds query u's raw vector
+    print(f"id limit: building n={n} d={d} bf16 on the GPU", flush=True)
+    corpus = mips.empty_corpus(n, d, "bf16", dev)
+    step = 1 << 25
+    for r0 in range(0, n, step):
+        r1 = min(n, r0 + step)
+        x = lattice_rows(r0, r1, d, dev)
+        for u, p in enumerate(planted):
+            if r0 <= p < r1:
+                x[p - r0] = torch.from_numpy(qraw[u]).to(dev)
+        mips.prepare_rows(corpus, x, r0)
+        del x
+    q = mips.l2_normalize(torch.from_numpy(qraw).to(dev), "bf16")
+    print("id limit: mips_topk", flush=True)
+    s, i = mips.topk(q, corpus, k)
+    torch.cuda.synchronize()
+    s, i = s.cpu().numpy(), i.cpu().numpy()
+    del corpus
+    torch.cuda.empty_cache()
+
+    print("id limit: oracle on one period", flush=True)
+    q_or, _ = oracle.prepare(qraw, "bf16")
+    c_period, _ = oracle.prepare(lattice_rows(0, P, d), "bf16")
+    c_planted, _ = oracle.prepare(qraw, "bf16")
+    nres = 2 * k
+    r_s, r_i = oracle.topk(q_or, "bf16", c_period, "bf16", nres, threads=threads())
+    for t in range(3):
+        ps = oracle.scores(q_or, "bf16", c_planted, "bf16", np.full(3, t), np.arange(3))
+        cand = [(float(ps[u]), planted[u]) for u in range(3)]
+        for sc, r in zip(r_s[t], r_i[t]):
+            ids = [int(r) + m * P for m in range(k + 3)]
+            cand += [(float(sc), j) for j in ids if j < n and j not in planted]
+        cand.sort(key=lambda e: (-e[0], e[1]))
+        want_s = np.array([e[0] for e in cand[:k]])
+        want_i = np.array([e[1] for e in cand[:k]])
+        # complete: residues past the first nres all score below the K-th entry
+        assert r_s[t, -1] < want_s[-1], "too many residues tie at the K-th score"
+        assert i[t, 0] == planted[t], (t, i[t])
+        # every returned row's exact score, from its own codes
+        for rank, (gs, gi) in enumerate(zip(s[t], i[t])):
+            assert 0 <= gi < n
+            if gi in planted:
+                ex = float(ps[planted.index(gi)])
+            else:
+                ex = float(oracle.scores(q_or, "bf16", c_period, "bf16", np.array([t]),
+                                         np.array([gi % P]))[0])
+            assert abs(gs - ex) <= TOL["bf16"], (t, rank, gi, gs, ex)
+        order_ok = (s[t][:-1] > s[t][1:]) | ((s[t][:-1] == s[t][1:]) & (i[t][:-1] < i[t][1:]))
+        assert np.all(order_ok)
+        diff = set(i[t].tolist()) ^ set(want_i.tolist())
+        for gi in diff:
+            ex = (float(ps[planted.index(gi)]) if gi in planted else
+                  float(oracle.scores(q_or, "bf16", c_period, "bf16", np.array([t]),
+                                      np.array([gi % P]))[0]))
+            assert abs(ex - want_s[-1]) <= TOL["bf16"], f"query {t}: id {gi} swapped beyond tolerance"
+        print(f"id limit: query {t}: ids {i[t][:4].tolist()}..., {len(diff) // 2} swaps", flush=True)
