@@ -15,6 +15,12 @@ Functions take and return numpy arrays:
 * ``topk(queries, q_dtype, corpus, c_dtype, k, row_scale=None, exclude=None)`` --
   fp64 scores [b, k] and int32 ids [b, k], sorted by score descending then id ascending.
 * ``scores(...)`` -- exact scores of given (query, id) pairs.
+* ``topk_int8(queries, q_dtype, corpus, k, row_scale, exclude=None)`` and
+  ``scores_int8(...)`` -- the quantised scoring branch against an int8 index, step by step
+  in binary32 (per-query int8 codes with scale max|u|/127, exact integer dot products,
+  then the query scale, then the row scale).
+* ``quantize(x, x_dtype, dtype)`` -- rows as given (no normalisation) quantised to
+  ``"int8"`` (the per-query rule above) or ``"fp8"`` (E4M3 with a power-of-two scale).
 * ``merge_topk(scores, ids, offsets, k)`` -- merge of per-index sorted result lists
   ([p, b, k_in]) into one top-k per query, ids shifted by each index's offset.
 * ``maxsim_topk(queries [b, m, d], ...)`` -- top-k of users with m interest vectors each,
@@ -82,9 +88,13 @@ def lib():
         L.oracle_topk.argtypes = [i32, p, i32, i32, p, p, i64, i32, p, i32, p, p, i32]
         L.oracle_scores.argtypes = [i32, p, i32, i32, p, p, i64, i32, p, p, i64, p]
         L.oracle_merge_topk.argtypes = [p, p, p, i32, i32, i32, i32, p, p]
+        L.oracle_quantize.argtypes = [i32, p, i64, i32, i32, p, p]
+        L.oracle_topk_int8.argtypes = [i32, p, i32, p, p, i64, i32, p, i32, p, p, i32]
+        L.oracle_scores_int8.argtypes = [i32, p, i32, p, p, i64, i32, p, p, i64, p]
         L.oracle_maxsim_topk.argtypes = [i32, p, i32, i32, i32, p, p, i64, i32, p, i32, p, p, i32]
         for f in (L.oracle_l2_normalize, L.oracle_prepare, L.oracle_topk, L.oracle_scores,
-                  L.oracle_merge_topk, L.oracle_maxsim_topk):
+                  L.oracle_merge_topk, L.oracle_maxsim_topk, L.oracle_quantize,
+                  L.oracle_topk_int8, L.oracle_scores_int8):
             f.restype = C.c_int
         _lib = L
     return _lib
@@ -229,6 +239,57 @@ def scores(queries: np.ndarray, q_dtype: str, corpus: np.ndarray, c_dtype: str,
     _check(lib().oracle_scores(DTYPES[q_dtype], _ptr(queries), b, DTYPES[c_dtype], _ptr(corpus),
                                _ptr(row_scale), n, d, _ptr(qidx), _ptr(ids), qidx.size,
                                _ptr(out)), "scores")
+    return out
+
+
+def quantize(x: np.ndarray, x_dtype: str, dtype: str) -> Tuple[np.ndarray, np.ndarray]:
+    """Rows as given ([rows, d] f32 values, or bf16 codes with x_dtype "bf16") quantised
+    without normalisation: (codes [rows, d], scale float32 [rows])."""
+    x = np.ascontiguousarray(x)
+    rows, d = x.shape
+    codes = np.empty((rows, d), _CODE_TYPES[dtype])
+    scale = np.empty(rows, np.float32)
+    _check(lib().oracle_quantize(DTYPES[x_dtype], _ptr(x), rows, d, DTYPES[dtype], _ptr(codes),
+                                 _ptr(scale)), "quantize")
+    return codes, scale
+
+
+def topk_int8(queries: np.ndarray, q_dtype: str, corpus: np.ndarray, k: int,
+              row_scale: np.ndarray, exclude: Optional[np.ndarray] = None,
+              threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Top-k against an int8 index by the quantised scoring branch: binary32 scores [b, k]
+    (as float64, exactly) and int32 ids [b, k], score descending then id ascending."""
+    queries = np.ascontiguousarray(queries)
+    corpus = np.ascontiguousarray(corpus, np.int8)
+    b, d = queries.shape
+    n = corpus.shape[0]
+    assert corpus.shape[1] == d
+    row_scale = np.ascontiguousarray(row_scale, np.float32)
+    if exclude is not None:
+        exclude = np.ascontiguousarray(exclude, np.uint32)
+        assert exclude.size >= (n + 31) // 32
+    out_s = np.empty((b, k), np.float64)
+    out_i = np.empty((b, k), np.int32)
+    _check(lib().oracle_topk_int8(DTYPES[q_dtype], _ptr(queries), b, _ptr(corpus),
+                                  _ptr(row_scale), n, d, _ptr(exclude), k, _ptr(out_s),
+                                  _ptr(out_i), threads or default_threads()), "topk_int8")
+    return out_s, out_i
+
+
+def scores_int8(queries: np.ndarray, q_dtype: str, corpus: np.ndarray, row_scale: np.ndarray,
+                qidx: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """Quantised-branch binary32 scores (as float64) of given (query, id) pairs."""
+    queries = np.ascontiguousarray(queries)
+    corpus = np.ascontiguousarray(corpus, np.int8)
+    b, d = queries.shape
+    n = corpus.shape[0]
+    qidx = np.ascontiguousarray(qidx, np.int32).ravel()
+    ids = np.ascontiguousarray(ids, np.int32).ravel()
+    row_scale = np.ascontiguousarray(row_scale, np.float32)
+    out = np.empty(qidx.size, np.float64)
+    _check(lib().oracle_scores_int8(DTYPES[q_dtype], _ptr(queries), b, _ptr(corpus),
+                                    _ptr(row_scale), n, d, _ptr(qidx), _ptr(ids), qidx.size,
+                                    _ptr(out)), "scores_int8")
     return out
 
 

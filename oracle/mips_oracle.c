@@ -38,6 +38,17 @@
  *    entries (`local_top_k` takes min(k, N)). Missing entries are padded with
  *    (-inf, -1). Excluded ids are never returned.
  *
+ *  - quantised scoring (oracle_topk_int8, oracle_scores_int8), the int8 branch of
+ *    `RecsysTwoTowerModel.forward` (`compute_top_k_int8`) step by step, every step in
+ *    binary32 as the Model's float32 tensors: per user, us = max(max_d |u_d| / 127,
+ *    1e-12); uq_d = u_d / us rounded to nearest (ties to even) and clipped to
+ *    [-127, 127]; the exact integer dot product acc of uq with the item's int8 codes;
+ *    then acc times us, then times the item's scale. The page casts the product to
+ *    bf16; here it stays binary32 (the scores are fp32 throughout this library).
+ *  - quantisation of rows as given, without normalisation (oracle_quantize): the int8
+ *    rule above, or E4M3 codes with the power-of-two scale of the index build (the
+ *    reading used for the queries of an fp8 index).
+ *
  *  - merging: the per-query union of several sorted (score, id) lists -- the
  *    results of separate indexes, each id shifted by its index's offset -- cut to
  *    the best k by the same order ("Two-Tower Retrieval at Industrial Scale",
@@ -299,6 +310,91 @@ static double score_one(const double *q, int32_t c_dtype, const void *corpus,
     return s;
 }
 
+/* ------------------------------------------------------- quantised scoring */
+
+/* The per-user int8 quantisation of the quantised scoring branch, in binary32: the
+ * scale us = max(max_d |u_d| / 127, 1e-12) and the codes uq_d = u_d / us rounded to
+ * nearest, ties to even, clipped to [-127, 127]. u is the row as given (f32 values). */
+static float quantize_row_i8(const float *u, int32_t d, int32_t *uq)
+{
+    float amax = 0.0f;
+    for (int32_t j = 0; j < d; ++j)
+        amax = fmaxf(amax, fabsf(u[j]));
+    const float us = fmaxf(amax / 127.0f, 1e-12f);
+    for (int32_t j = 0; j < d; ++j) {
+        const float t = u[j] / us; /* one binary32 division */
+        uq[j] = (int32_t)oracle_i8_from_f64((double)t);
+    }
+    return us;
+}
+
+/* Score of one item in the quantised branch: the exact integer dot product of the user's
+ * codes with the item's codes, then times the user scale, then times the item scale,
+ * each product rounded to binary32. */
+static float score_int8_row(const int32_t *uq, float us, const int8_t *codes, float scale,
+                            int32_t d)
+{
+    int64_t acc = 0;
+    for (int32_t j = 0; j < d; ++j)
+        acc += (int64_t)uq[j] * (int64_t)codes[j];
+    const float a = (float)acc; /* |acc| <= 127 * 127 * d < 2^24: exact */
+    const float t = a * us;
+    return t * scale;
+}
+
+/* The f32 value of element idx of a query buffer (OR_F32 or OR_BF16); exact. */
+static float query_f32(int32_t dtype, const void *base, int64_t idx)
+{
+    return (float)stored_value(dtype, base, idx);
+}
+
+/* Rows as given (OR_F32 or OR_BF16 values, [rows, d]) quantised without normalisation:
+ *   OR_I8:   codes int8 [rows, d] and scale[rows], the per-user rule of the quantised
+ *            branch (quantize_row_i8);
+ *   OR_E4M3: codes uint8 [rows, d], E4M3 of x / s with s the smallest power of two with
+ *            max|x| <= 448 s (1 for a zero row), and scale[rows] = s. */
+int oracle_quantize(int32_t x_dtype, const void *x, int64_t rows, int32_t d, int32_t dtype,
+                    void *codes, float *scale)
+{
+    if (!x || !codes || !scale || rows < 0 || d <= 0)
+        return OR_BAD_ARG;
+    if ((x_dtype != OR_F32 && x_dtype != OR_BF16) || (dtype != OR_I8 && dtype != OR_E4M3))
+        return OR_BAD_ARG;
+    float *u = (float *)malloc(sizeof(float) * (size_t)d);
+    int32_t *uq = (int32_t *)malloc(sizeof(int32_t) * (size_t)d);
+    if (!u || !uq) {
+        free(u);
+        free(uq);
+        return OR_NOMEM;
+    }
+    int rc = OR_OK;
+    for (int64_t r = 0; r < rows && rc == OR_OK; ++r) {
+        for (int32_t j = 0; j < d; ++j) {
+            u[j] = query_f32(x_dtype, x, r * (int64_t)d + j);
+            if (!isfinite(u[j]))
+                rc = OR_NONFINITE;
+        }
+        if (rc != OR_OK)
+            break;
+        if (dtype == OR_I8) {
+            scale[r] = quantize_row_i8(u, d, uq);
+            for (int32_t j = 0; j < d; ++j)
+                ((int8_t *)codes)[r * (int64_t)d + j] = (int8_t)uq[j];
+        } else {
+            float amax = 0.0f;
+            for (int32_t j = 0; j < d; ++j)
+                amax = fmaxf(amax, fabsf(u[j]));
+            const double s = oracle_e4m3_row_scale((double)amax);
+            scale[r] = (float)s;
+            for (int32_t j = 0; j < d; ++j)
+                ((uint8_t *)codes)[r * (int64_t)d + j] = oracle_e4m3_from_f64((double)u[j] / s);
+        }
+    }
+    free(u);
+    free(uq);
+    return rc;
+}
+
 static int excluded(const uint32_t *bits, int64_t i)
 {
     return bits && ((bits[i >> 5] >> (i & 31)) & 1u);
@@ -322,6 +418,7 @@ static int cmp_pair(const void *a, const void *b)
 
 typedef struct {
     int32_t q_dtype, c_dtype, d, k, b, m; /* m query rows per result row (interests) */
+    int quantised; /* int8 index scored by the quantised branch (score_int8_row) */
     const void *queries, *corpus;
     const float *row_scale;
     const uint32_t *exclude;
@@ -338,12 +435,16 @@ static void *topk_worker(void *arg)
     topk_job_t *J = (topk_job_t *)arg;
     pair_t *pairs = (pair_t *)malloc(sizeof(pair_t) * (size_t)(J->n > 0 ? J->n : 1));
     double *q = (double *)malloc(sizeof(double) * (size_t)J->d * (size_t)J->m);
-    if (!pairs || !q) {
+    float *qf = (float *)malloc(sizeof(float) * (size_t)J->d);
+    int32_t *uq = (int32_t *)malloc(sizeof(int32_t) * (size_t)J->d);
+    if (!pairs || !q || !qf || !uq) {
         pthread_mutex_lock(&J->lock);
         J->status = OR_NOMEM;
         pthread_mutex_unlock(&J->lock);
         free(pairs);
         free(q);
+        free(qf);
+        free(uq);
         return NULL;
     }
     for (;;) {
@@ -355,10 +456,24 @@ static void *topk_worker(void *arg)
         /* result row b: query rows b*m .. b*m+m-1; an item scores its best match */
         for (int64_t j = 0; j < (int64_t)J->d * J->m; ++j)
             q[j] = stored_value(J->q_dtype, J->queries, (int64_t)b * J->m * J->d + j);
+        float us = 1.0f;
+        if (J->quantised) {
+            for (int32_t j = 0; j < J->d; ++j)
+                qf[j] = (float)q[j];
+            us = quantize_row_i8(qf, J->d, uq);
+        }
         int64_t m = 0;
         for (int64_t i = 0; i < J->n; ++i) {
             if (excluded(J->exclude, i))
                 continue;
+            if (J->quantised) {
+                pairs[m].s = (double)score_int8_row(uq, us, (const int8_t *)J->corpus +
+                                                                i * (int64_t)J->d,
+                                                    J->row_scale[i], J->d);
+                pairs[m].id = (int32_t)i;
+                ++m;
+                continue;
+            }
             double best = score_one(q, J->c_dtype, J->corpus, J->row_scale, i, J->d);
             for (int32_t v = 1; v < J->m; ++v) {
                 double sv = score_one(q + (int64_t)v * J->d, J->c_dtype, J->corpus,
@@ -384,6 +499,8 @@ static void *topk_worker(void *arg)
     }
     free(pairs);
     free(q);
+    free(qf);
+    free(uq);
     return NULL;
 }
 
@@ -405,7 +522,7 @@ static int check_finite(int32_t dtype, const void *p, int64_t count)
 static int topk_m(int32_t q_dtype, const void *queries, int32_t b, int32_t mq, int32_t c_dtype,
                   const void *corpus, const float *row_scale, int64_t n, int32_t d,
                   const uint32_t *exclude, int32_t k, double *out_s, int32_t *out_id,
-                  int32_t threads);
+                  int32_t threads, int quantised);
 
 int oracle_topk(int32_t q_dtype, const void *queries, int32_t b, int32_t c_dtype,
                 const void *corpus, const float *row_scale, int64_t n, int32_t d,
@@ -413,7 +530,20 @@ int oracle_topk(int32_t q_dtype, const void *queries, int32_t b, int32_t c_dtype
                 int32_t threads)
 {
     return topk_m(q_dtype, queries, b, 1, c_dtype, corpus, row_scale, n, d, exclude, k, out_s,
-                  out_id, threads);
+                  out_id, threads, 0);
+}
+
+/* Top-k of every query against an int8 index by the quantised branch of
+ * `RecsysTwoTowerModel.forward` (quantize_row_i8, score_int8_row): each query quantised
+ * to int8 with its own scale, exact integer dot products, then the user scale and the
+ * item scale in binary32. Arguments as oracle_topk with c_dtype OR_I8; out_s holds the
+ * binary32 scores (exactly, as doubles). */
+int oracle_topk_int8(int32_t q_dtype, const void *queries, int32_t b, const void *corpus,
+                     const float *row_scale, int64_t n, int32_t d, const uint32_t *exclude,
+                     int32_t k, double *out_s, int32_t *out_id, int32_t threads)
+{
+    return topk_m(q_dtype, queries, b, 1, OR_I8, corpus, row_scale, n, d, exclude, k, out_s,
+                  out_id, threads, 1);
 }
 
 /* Top-k of b users with m query vectors each (queries [b * m, d], user-major): an item's
@@ -427,13 +557,13 @@ int oracle_maxsim_topk(int32_t q_dtype, const void *queries, int32_t b, int32_t 
     if (m < 1)
         return OR_BAD_ARG;
     return topk_m(q_dtype, queries, b, m, c_dtype, corpus, row_scale, n, d, exclude, k, out_s,
-                  out_id, threads);
+                  out_id, threads, 0);
 }
 
 static int topk_m(int32_t q_dtype, const void *queries, int32_t b, int32_t mq, int32_t c_dtype,
                   const void *corpus, const float *row_scale, int64_t n, int32_t d,
                   const uint32_t *exclude, int32_t k, double *out_s, int32_t *out_id,
-                  int32_t threads)
+                  int32_t threads, int quantised)
 {
     if (!queries || !corpus || !out_s || !out_id || b < 0 || n < 0 || d <= 0 || k <= 0)
         return OR_BAD_ARG;
@@ -458,6 +588,7 @@ static int topk_m(int32_t q_dtype, const void *queries, int32_t b, int32_t mq, i
     J.k = k;
     J.b = b;
     J.m = mq;
+    J.quantised = quantised;
     J.queries = queries;
     J.corpus = corpus;
     J.row_scale = row_scale;
@@ -505,6 +636,39 @@ int oracle_scores(int32_t q_dtype, const void *queries, int32_t b, int32_t c_dty
     }
     free(q);
     return OR_OK;
+}
+
+/* Quantised-branch scores of given (query, id) pairs against an int8 index:
+ * out[t] = score_int8_row of query qidx[t] (quantised by quantize_row_i8) and row ids[t]. */
+int oracle_scores_int8(int32_t q_dtype, const void *queries, int32_t b, const void *corpus,
+                       const float *row_scale, int64_t n, int32_t d, const int32_t *qidx,
+                       const int32_t *ids, int64_t count, double *out)
+{
+    if (!queries || !corpus || !row_scale || !qidx || !ids || !out || d <= 0 ||
+        (q_dtype != OR_F32 && q_dtype != OR_BF16))
+        return OR_BAD_ARG;
+    float *u = (float *)malloc(sizeof(float) * (size_t)d);
+    int32_t *uq = (int32_t *)malloc(sizeof(int32_t) * (size_t)d);
+    if (!u || !uq) {
+        free(u);
+        free(uq);
+        return OR_NOMEM;
+    }
+    int rc = OR_OK;
+    for (int64_t t = 0; t < count; ++t) {
+        if (qidx[t] < 0 || qidx[t] >= b || ids[t] < 0 || ids[t] >= n) {
+            rc = OR_BAD_ARG;
+            break;
+        }
+        for (int32_t j = 0; j < d; ++j)
+            u[j] = query_f32(q_dtype, queries, (int64_t)qidx[t] * d + j);
+        const float us = quantize_row_i8(u, d, uq);
+        out[t] = (double)score_int8_row(uq, us, (const int8_t *)corpus + (int64_t)ids[t] * d,
+                                        row_scale[ids[t]], d);
+    }
+    free(u);
+    free(uq);
+    return rc;
 }
 
 /* Merge of p sorted lists per query: in_s/in_id are [p, b, k_in] (list-major), a

@@ -396,3 +396,199 @@ def test_maxsim_equals_brute_force_max():
         best = (qv[u] @ cv.T).max(axis=0)
         order = sorted(range(n), key=lambda i: (-best[i], i))[:k]
         assert ids[u].tolist() == order
+
+
+# ------------------------------------------------ quantised scoring (int8 branch)
+def _rn32(fr: Fraction) -> np.float32:
+    """Nearest binary32 to an exact rational, ties to even, found by comparing exact
+    distances to the neighbours of a first guess (independent of any float multiply)."""
+    f = np.float32(float(fr))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    return min(cands, key=lambda c: (abs(Fraction(float(c)) - fr),
+                                     int(np.array(c, np.float32).view(np.uint32)) & 1))
+
+
+def _torch_quantize_i8(u32: np.ndarray):
+    """The per-user rule with torch's float32 ops: scale max(max|u|/127, 1e-12), codes
+    round-half-even(u / scale) clipped to [-127, 127]."""
+    t = torch.from_numpy(np.ascontiguousarray(u32, np.float32))
+    us = torch.clamp(t.abs().amax(dim=1) / 127.0, min=1e-12)
+    uq = torch.clamp(torch.round(t / us[:, None]), -127, 127).to(torch.int32)
+    return uq.numpy(), us.numpy()
+
+
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+def test_quantize_int8_matches_torch(x_dtype):
+    rng = np.random.default_rng(40)
+    u = rng.standard_normal((400, 64)).astype(np.float32) * rng.uniform(1e-3, 2, (400, 1)).astype(np.float32)
+    # exact half steps: with max 127 * 2^-7 the scale is 2^-7 and (j + 0.5) 2^-7 is a tie
+    u[0] = 0.0
+    u[0, 0] = 127 * 2.0 ** -7
+    u[0, 1:12] = (np.arange(-6, 5) + 0.5) * 2.0 ** -7
+    u[1] = 0.0                                     # zero row: scale 1e-12, codes 0
+    u[2] = 0.0
+    u[2, 3] = -0.5 * np.float32(1e-12)             # below the floor: -0.5 steps -> 0 (even)
+    x = u if x_dtype == "f32" else torch.from_numpy(u).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    vals = oracle.decode(x, x_dtype).astype(np.float32)
+    codes, scale = oracle.quantize(x, x_dtype, "int8")
+    ref_q, ref_s = _torch_quantize_i8(vals)
+    assert np.array_equal(scale.view(np.uint32), ref_s.view(np.uint32))
+    assert np.array_equal(codes.astype(np.int32), ref_q)
+    assert scale[0] == 2.0 ** -7 and codes[0, 0] == 127
+    assert codes[0, 1:12].tolist() == [-6, -4, -4, -2, -2, 0, 0, 2, 2, 4, 4]
+    assert scale[1] == np.float32(1e-12) and not codes[1].any()
+    if x_dtype == "f32":
+        assert scale[2] == np.float32(1e-12) and not codes[2].any()
+
+
+def test_quantize_fp8_matches_torch_float8():
+    rng = np.random.default_rng(41)
+    u = (rng.standard_normal((300, 128)) * rng.uniform(1e-3, 3, (300, 1))).astype(np.float32)
+    u[7] = 0.0
+    codes, scale = oracle.quantize(u, "f32", "fp8")
+    for r in range(u.shape[0]):
+        s = scale[r]
+        assert s == oracle.e4m3_row_scale(float(np.abs(u[r]).max()))   # the pinned scale rule
+        ref = torch.from_numpy(u[r] / s).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(codes[r], ref), r
+    assert scale[7] == 1.0 and not codes[7].any()
+
+
+def _int8_bruteforce(qvals, cq, cs, k, excluded=()):
+    """The quantised branch from pinned pieces: torch's quantisation of the queries, Python
+    integer dot products, and each product rounded to binary32 by exact rationals (user
+    scale first, then the item scale); sorted by (-score, id)."""
+    uq, us = _torch_quantize_i8(qvals)
+    out = []
+    for qi in range(uq.shape[0]):
+        row = []
+        for i in range(cq.shape[0]):
+            if i in excluded:
+                continue
+            acc = sum(int(a) * int(c) for a, c in zip(uq[qi], cq[i]))
+            t = _rn32(Fraction(acc) * Fraction(float(us[qi])))
+            row.append((float(_rn32(Fraction(float(t)) * Fraction(float(cs[i])))), i))
+        out.append(sorted(row, key=lambda e: (-e[0], e[1]))[:k])
+    return out
+
+
+@pytest.mark.parametrize("q_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("with_exclusion", [False, True])
+def test_topk_int8_matches_integer_bruteforce(q_dtype, with_exclusion):
+    rng = np.random.default_rng(42)
+    n, d, b, k = 70, 16, 4, 15
+    cq, cs = oracle.prepare(rng.standard_normal((n, d)).astype(np.float32), "int8")
+    q, _ = oracle.prepare(rng.standard_normal((b, d)).astype(np.float32), q_dtype)
+    # two rows with identical codes and scales tie exactly: the lower id comes first
+    cq[40], cs[40] = cq[3], cs[3]
+    excl = set(rng.choice(n, 12, replace=False).tolist()) - {3, 40} if with_exclusion else set()
+    bitmap = bitmap_from_ids(np.array(sorted(excl), np.int64), n) if excl else None
+    s, ids = oracle.topk_int8(q, q_dtype, cq, k, cs, exclude=bitmap, threads=2)
+    ref = _int8_bruteforce(oracle.decode(q, q_dtype).astype(np.float32), cq, cs, k, excl)
+    for qi in range(b):
+        assert ids[qi].tolist() == [i for _, i in ref[qi]]
+        assert s[qi].tolist() == [v for v, _ in ref[qi]]
+        pos = {i: p for p, i in enumerate(ids[qi].tolist())}
+        if 3 in pos and 40 in pos:
+            assert pos[3] < pos[40]
+    # scores_int8 of the returned pairs is bitwise the listed score
+    qidx = np.repeat(np.arange(b), k)
+    e = oracle.scores_int8(q, q_dtype, cq, cs, qidx, ids.ravel())
+    assert np.array_equal(e, s.ravel())
+
+
+def test_int8_scores_round_the_exact_score_when_the_user_scale_is_a_power_of_two():
+    """u = m 2^-e with max|m| = 127 makes the user scale exactly 2^-e and the codes exactly m,
+    so the first product is exact and the score is the exact inner product of u with the
+    stored row rounded once to binary32; that exact value is the unquantised oracle's."""
+    rng = np.random.default_rng(43)
+    n, d, b = 200, 32, 6
+    cq, cs = oracle.prepare(rng.standard_normal((n, d)).astype(np.float32), "int8")
+    m = rng.integers(-127, 128, (b, d))
+    m[np.arange(b), rng.integers(0, d, b)] = np.where(rng.random(b) < 0.5, 127, -127)
+    e = rng.integers(5, 12, b)
+    u = (m * 2.0 ** -e[:, None]).astype(np.float32)
+    s, ids = oracle.topk_int8(u, "f32", cq, n, cs, threads=2)
+    exact = oracle.scores(u, "f32", cq, "int8", np.repeat(np.arange(b), n), ids.ravel(),
+                          row_scale=cs).reshape(b, n)
+    assert np.array_equal(s.astype(np.float32), exact.astype(np.float32))
+    # the integer dot product itself, with power-of-two row scales as well
+    cs2 = (2.0 ** -rng.integers(6, 9, n)).astype(np.float32)
+    s2 = oracle.scores_int8(u, "f32", cq, cs2, np.repeat(np.arange(b), n), np.tile(np.arange(n), b))
+    acc = (m.astype(np.int64) @ cq.astype(np.int64).T).ravel()
+    assert np.array_equal(s2, acc * 2.0 ** -np.repeat(e, n) * np.tile(cs2.astype(np.float64), b))
+
+
+def test_int8_scores_within_the_quantisation_bound_of_the_exact_score():
+    """Rounding u_d to the nearest code moves it by at most half a step us/2, so the score
+    differs from the exact inner product of the unquantised query with the stored row by at
+    most (us/2) sum_d |c_d| s plus two binary32 roundings; a wrong scale or index would not."""
+    rng = np.random.default_rng(44)
+    n, d, b = 300, 128, 8
+    cq, cs = oracle.prepare(rng.standard_normal((n, d)).astype(np.float32), "int8")
+    q, _ = oracle.prepare(rng.standard_normal((b, d)).astype(np.float32), "bf16")
+    s, ids = oracle.topk_int8(q, "bf16", cq, n, cs, threads=2)
+    qv = oracle.decode(q, "bf16")
+    exact = oracle.scores(q, "bf16", cq, "int8", np.repeat(np.arange(b), n), ids.ravel(),
+                          row_scale=cs).reshape(b, n)
+    us = np.maximum(np.abs(qv).max(axis=1) / 127, 1e-12)
+    l1 = np.abs(cq.astype(np.float64))[ids].sum(axis=2) * cs[ids]
+    bound = us[:, None] / 2 * l1 * (1 + 1e-6) + 2.0 ** -22 * np.abs(exact)
+    assert np.all(np.abs(s - exact) <= bound)
+    assert np.abs(s - exact).max() > 1e-5          # the quantisation is really applied
+
+
+# ------------------------------------------------------- exact scores by pair
+def test_scores_of_pairs_match_numpy_and_topk():
+    rng = np.random.default_rng(45)
+    n, d, b, k = 150, 24, 7, 40
+    for c_dtype, q_dtype in (("bf16", "bf16"), ("fp8", "bf16"), ("f32", "f32"), ("int8", "f32")):
+        cq, cs = oracle.prepare(rng.standard_normal((n, d)).astype(np.float32), c_dtype)
+        q, _ = oracle.prepare(rng.standard_normal((b, d)).astype(np.float32), q_dtype)
+        # arbitrary (query, id) pairs in a shuffled order: numpy's dot of the decoded rows
+        qidx = rng.integers(0, b, 500)
+        ids = rng.integers(0, n, 500)
+        e = oracle.scores(q, q_dtype, cq, c_dtype, qidx, ids, row_scale=cs)
+        ref = np.einsum("td,td->t", oracle.decode(q, q_dtype)[qidx],
+                        oracle.decode(cq, c_dtype, cs)[ids])
+        assert np.allclose(e, ref, rtol=1e-13, atol=1e-16), c_dtype
+        # a wrong query or row index would show: the pairs really differ
+        assert np.abs(ref - ref[rng.permutation(500)]).max() > 1e-2
+        # and topk's scores are bitwise the scores of its own ids
+        s, i = oracle.topk(q, q_dtype, cq, c_dtype, k, row_scale=cs, threads=2)
+        e2 = oracle.scores(q, q_dtype, cq, c_dtype, np.repeat(np.arange(b), k), i.ravel(),
+                           row_scale=cs)
+        assert np.array_equal(e2, s.ravel()), c_dtype
+
+
+# -------------------------------------------------- rows below the norm floor
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8", "int8"])
+def test_prepare_rows_below_the_norm_floor(dtype):
+    """Rows with sum x^2 < 1e-12 are divided by sqrt(1e-12) (the clamp); a zero row stays
+    zero (fp8 scale 1, int8 scale 1e-12). Reference: torch's float32 ops, whose sums of
+    these rows are exact, and torch's own bf16 / E4M3 / round conversions."""
+    x = np.zeros((4, 32), np.float32)
+    x[1, 0] = 1e-7
+    x[2, 0], x[2, 5] = 3e-7, -4e-7
+    x[3, :] = 1e-8
+    codes, scale = oracle.prepare(x, dtype)
+    t = torch.from_numpy(x)
+    ss = torch.clamp((t * t).sum(dim=1, keepdim=True), min=1e-12)
+    y = t / torch.sqrt(ss)
+    assert float(ss[1, 0]) < 1e-12 or float(ss[1, 0]) == np.float32(1e-12)
+    if dtype == "f32":
+        assert np.array_equal(codes.view(np.uint32), y.numpy().view(np.uint32))
+    elif dtype == "bf16":
+        assert np.array_equal(codes, y.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    elif dtype == "fp8":
+        amax = y.abs().amax(dim=1).numpy()
+        want_s = np.array([oracle.e4m3_row_scale(float(a)) for a in amax], np.float32)
+        assert np.array_equal(scale, want_s) and scale[0] == 1.0
+        ref = (y / torch.from_numpy(want_s)[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(codes, ref)
+    else:
+        ref_q, ref_s = _torch_quantize_i8(y.numpy())
+        assert np.array_equal(scale.view(np.uint32), ref_s.view(np.uint32))
+        assert np.array_equal(codes.astype(np.int32), ref_q)
+        assert scale[0] == np.float32(1e-12)
+    assert not np.any(codes[0])
