@@ -141,8 +141,21 @@ def build_gpu_inputs(w, dev, torch, mips):
     return corpus, q, excl, (nbytes_in + out_bytes) / t_prep / 1e9
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_queries):
-    """The oracle as it stands, on the first `budget_queries` queries of the same workload."""
+    """The oracle as it stands (int8 index: its quantised scoring branch), on the first
+    `budget_queries` queries of the same workload against the whole corpus. The rate in
+    scores/s is measured on that sample; the time of the whole batch at that rate is an
+    extrapolation and is labelled as one."""
     import oracle
     t0 = time.perf_counter()
     codes, scale = oracle.prepare_chunks(w.corpus_chunks(), w.n, w.d, w.corpus_dtype)
@@ -151,14 +164,21 @@ def cpu_baseline(w, budget_queries):
     log(f"oracle inputs ready in {time.perf_counter() - t0:.1f}s")
     threads = oracle.default_threads()
     t0 = time.perf_counter()
-    oracle.topk(q_or, w.query_dtype, codes, w.corpus_dtype, w.k, row_scale=scale, exclude=bm,
-                threads=threads)
+    if w.corpus_dtype == "int8":
+        oracle.topk_int8(q_or, w.query_dtype, codes, w.k, scale, exclude=bm, threads=threads)
+    else:
+        oracle.topk(q_or, w.query_dtype, codes, w.corpus_dtype, w.k, row_scale=scale,
+                    exclude=bm, threads=threads)
     dt = time.perf_counter() - t0
+    used = min(threads, budget_queries)
     return {"value": budget_queries * w.n / dt, "unit": "scores/s",
-            "cores": min(threads, budget_queries), "kind": "oracle",
+            "cores": used, "kind": "oracle",
             "sample": f"first {budget_queries} of {w.b} queries against the full corpus "
-                      f"(n={w.n}, d={w.d}, k={w.k}); exact fp64 dot products and a full sort; "
-                      f"{dt:.1f}s"}
+                      f"(n={w.n}, d={w.d}, k={w.k}), {dt:.1f}s; exact fp64 dot products and "
+                      f"a full sort per query; the whole batch of {w.b} would take "
+                      f"{dt * w.b / budget_queries:.0f}s at this rate (extrapolated)",
+            "cpu_model": cpu_model(), "threads": used,
+            "batch_seconds_extrapolated": dt * w.b / budget_queries}
 
 
 def bench_masks(args, w, corpus, q, excl, torch, mips, dev):
@@ -217,7 +237,10 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-queries", type=int, default=0,
-                    help="queries in the CPU-baseline sample (default: host threads)")
+                    help="queries in the CPU-baseline sample (default: twice the host "
+                         "threads, at most 32, at most the batch)")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="MiB of scratch written before every timed call (0: none)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="first run a plain device copy of GIB GiB (counter calibration)")
     ap.add_argument("--masks", type=int, default=0, metavar="T",
@@ -249,6 +272,10 @@ def main():
     ws = mips.empty_workspace(wsb, dev)
     scores = torch.empty((w.b, w.k), dtype=torch.float32, device=dev)
     ids = torch.empty((w.b, w.k), dtype=torch.int32, device=dev)
+    # written before every timed call (outside its events) so that no call finds the
+    # corpus in the 256 MB last-level cache
+    flush = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev) \
+        if args.flush_mib > 0 else None
 
     def step():
         mips.topk(q, corpus, w.k, excl, workspace=ws, out=(scores, ids))
@@ -260,21 +287,37 @@ def main():
 
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(i))
         mips.set_timing_events(pairs[i][0], pairs[i][1])
+        calls[i][0].record()
         step()
+        calls[i][1].record()
     mips.set_timing_events(None, None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     main_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    call_ms = [a.elapsed_time(b) for a, b in calls]
     for a, b in pairs:
         ev.destroy(a)
         ev.destroy(b)
-    log(f"timed {args.steps} steps in {wall:.3f}s")
+    log(f"timed {args.steps} steps in {wall:.3f}s (with a {args.flush_mib} MiB cache flush "
+        f"before each); per call: median {np.median(call_ms):.4f} ms, min {min(call_ms):.4f} ms")
 
-    ms_per_step = wall / args.steps * 1e3
+    # back to back with no flush: the rate of a stream of calls on one index (labelled extra)
+    torch.cuda.synchronize()
+    tb = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - tb) / args.steps * 1e3
+
+    ms_per_step = float(np.median(call_ms))
     scores_per_s = w.b * w.n / (ms_per_step / 1e3)
     E = {"f32": 4, "bf16": 2, "fp8": 1, "int8": 1}[w.corpus_dtype]
     # Algorithmic bytes of the main score pass: every packed corpus row once (plus its
@@ -287,17 +330,26 @@ def main():
     achieved_tflops = flops / main_avg / 1e12
     t_hbm = alg_bytes / (PEAK_HBM_GBS * 1e9)
     t_mfma = flops / (PEAK_TFLOPS[w.corpus_dtype] * 1e12)
+    call_s = ms_per_step / 1e3
     if t_hbm >= t_mfma:
         roof = {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved_gbs / PEAK_HBM_GBS}
+        call_frac = alg_bytes / call_s / 1e9 / PEAK_HBM_GBS
     else:
         roof = {"bound": "mfma", "achieved": achieved_tflops, "peak": PEAK_TFLOPS[w.corpus_dtype],
                 "unit": "TFLOP/s", "frac": achieved_tflops / PEAK_TFLOPS[w.corpus_dtype]}
+        call_frac = flops / call_s / 1e12 / PEAK_TFLOPS[w.corpus_dtype]
     roof["traffic"] = measured_traffic(w.name)
     roof["kernel"] = "score_kernel (main pass)"
     roof["kernel_avg_us"] = main_avg * 1e6
+    roof["kernel_median_us"] = float(np.median(main_ms)) * 1e3
     roof["algorithmic_bytes"] = alg_bytes
     roof["mfma_frac"] = achieved_tflops / PEAK_TFLOPS[w.corpus_dtype]
+    # the same roofline for the whole call (every kernel of mips_topk, median of the timed
+    # calls): what the metric measures
+    roof["call_frac"] = call_frac
+    roof["call_median_ms"] = ms_per_step
+    roof["call_min_ms"] = float(min(call_ms))
     # measured after the timed region: the HBM rate of a plain 1 GiB device copy
     copy_gbs = copy_probe_gbs(torch, dev)
     roof["copy_gbs"] = copy_gbs
@@ -321,11 +373,17 @@ def main():
                    "corpus_dtype": w.corpus_dtype, "query_dtype": w.query_dtype,
                    "exclude_frac": w.exclude_frac, "clusters": w.clusters},
         "queries_per_s": w.b / (ms_per_step / 1e3),
+        "timing": {"per_call": "HIP events around each mips_topk call on its stream, after "
+                               f"writing {args.flush_mib} MiB of scratch (untimed); "
+                               "value and ms_per_step use the median",
+                   "median_ms": ms_per_step, "min_ms": float(min(call_ms)),
+                   "wall_ms_per_step_incl_flush": wall / args.steps * 1e3,
+                   "back_to_back_unflushed_ms": warm_ms},
         "prepare_gbs": prep_gbs,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        nq = args.cpu_queries or min(w.b, max(1, min(16, len(os.sched_getaffinity(0)))))
+        nq = args.cpu_queries or min(w.b, 32, 2 * max(1, len(os.sched_getaffinity(0))))
         log(f"cpu baseline: oracle on {nq} queries")
         result["cpu_baseline"] = cpu_baseline(w, nq)
     print(json.dumps(result), flush=True)

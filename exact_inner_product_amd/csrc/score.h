@@ -269,8 +269,8 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
     auto sbq = [&](int qf) __attribute__((always_inline)) {
       return CT == MIPS_FP8_E4M3 ? sexp_lds[qf * kFrag + (lane & 31)] : 127;
     };
-    // int8: a score is (int32 dot product * row scale) * query scale, in that order. The
-    // query scale is positive, so it can be applied after a max (rounding is monotone).
+    // int8: a score is (int32 dot product * query scale) * row scale, each product rounded
+    // to binary32, in the order of the quantised branch of `RecsysTwoTowerModel.forward`.
     auto qscale = [&](int qf) __attribute__((always_inline)) {
       return CT == MIPS_INT8 ? __int_as_float(sexp_lds[qf * kFrag + (lane & 31)]) : 1.0f;
     };
@@ -401,20 +401,39 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
         }
       }
     };
-    // A lane's 16 values of block g before the query scale: the accumulators, or for int8
-    // the integer dot products times their rows' scales.
-    auto vals = [&](const f32x16_t& acc, const float (&sc)[SCN], float (&x)[16]) __attribute__((always_inline)) {
+    // A lane's 16 scores of block g: the accumulators, or for int8 the integer dot products
+    // times the query scale sq, then times their rows' scales.
+    auto vals = [&](const f32x16_t& acc, const float (&sc)[SCN], float sq, float (&x)[16]) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if constexpr (CT == MIPS_INT8)
-          x[i] = (float)__float_as_int(acc[i]) * sc[i];  // (a bit cast of a vector element
-                                                        // lvalue would read element 0)
+          x[i] = ((float)__float_as_int(acc[i]) * sq) * sc[i];  // (a bit cast of a vector
+                                                               // element lvalue would read
+                                                               // element 0)
         else
           x[i] = acc[i];
       }
     };
-    auto post = [&](float x, float sq) __attribute__((always_inline)) {
-      return CT == MIPS_INT8 ? x * sq : x;
+    // Fast-path bound of a lane's best score in block g, one multiply per value. For int8 it
+    // is max_i((a_i * s_i) * sq), the products in the other order: each order is within a
+    // factor (1 + 2^-24)^2 of the exact a_i sq s_i, so a score of the filter's order that
+    // reaches T implies this bound reaches gate(T) = T - |T| 2^-21.
+    auto fastmax = [&](const f32x16_t& acc, const float (&sc)[SCN], float sq) __attribute__((always_inline)) {
+      float x;
+      if constexpr (CT == MIPS_INT8) {
+        x = (float)__float_as_int(acc[0]) * sc[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) x = fmaxf(x, (float)__float_as_int(acc[i]) * sc[i]);
+        x = x * sq;
+      } else {
+        x = acc[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) x = fmaxf(x, acc[i]);
+      }
+      return x;
+    };
+    auto gate = [&](float T) __attribute__((always_inline)) {
+      return CT == MIPS_INT8 ? fmaf(-fabsf(T), 0x1p-21f, T) : T;  // (NaN for T = +inf: no pass)
     };
 
     // Main epilogue of one query fragment: one max per block (16 scores per lane) and one
@@ -458,28 +477,22 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
     auto epi_main = [&](const f32x16_t (&acc)[RM], const float (&sc)[RM][SCN], uint32_t xwv,
                         int64_t j0, int qf) __attribute__((always_inline)) {
       const float T = Tq(qf);
+      const float Tg = gate(T);
       const float sq = qscale(qf);
       float m[RM];
       bool any = false;
 #pragma unroll
       for (int g = 0; g < RM; ++g) {
-        float xv[16];
-        vals(acc[g], sc[g], xv);
-        float x = xv[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) x = fmaxf(x, xv[i]);
-        m[g] = post(x, sq);
-        any = any || (m[g] >= T);
+        m[g] = fastmax(acc[g], sc[g], sq);
+        any = any || (m[g] >= Tg);
       }
       if (__builtin_expect(__ballot(any) != 0ull, 0)) {
 #pragma unroll
         for (int g = 0; g < RM; ++g) {
-          if (__ballot(m[g] >= T) == 0ull) continue;
+          if (__ballot(m[g] >= Tg) == 0ull) continue;
           const uint32_t idb = (uint32_t)((A.blk0 + j0 + g) * kFrag);
           float y[16];
-          vals(acc[g], sc[g], y);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) y[i] = post(y[i], sq);
+          vals(acc[g], sc[g], sq, y);
           if constexpr (NT == 0) {
             pass_walk(y, (uint32_t)__builtin_amdgcn_readlane((int)xwv, g), T, idb, qf, 0);
           } else {
@@ -489,7 +502,7 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
             for (int t = 0; t < NT; ++t) {
               if (t >= A.nmask) break;
               const float Tt = thrt_lds[(qf * kFrag + (lane & 31)) * NT + t];
-              if (__ballot(m[g] >= Tt) == 0ull) continue;
+              if (__ballot(m[g] >= gate(Tt)) == 0ull) continue;
               pass_walk(y, (uint32_t)__builtin_amdgcn_readlane((int)xwv, g * NT + t), Tt, idb, qf, t);
             }
           }
@@ -524,7 +537,7 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
           asm volatile("" : "+v"(v));
           if (j < A.nfrag && qg >= 0) {
             float x[16];
-            vals(v, sc[g], x);
+            vals(v, sc[g], sq, x);
 #pragma unroll
             for (int t = 0; t < NTS; ++t) {
               if (NT > 0 && t >= A.nmask) break;
@@ -534,7 +547,7 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
                 const int row = acc_row(i, lane);
                 dst[row] = ((wt[t] >> row) & 1u)
                                ? 0ull
-                               : composite(score_key(post(x[i], sq)),
+                               : composite(score_key(x[i]),
                                            (uint32_t)((A.blk0 + j) * kFrag + row));
               }
             }
@@ -551,7 +564,7 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
           for (int g = 0; g < RM; ++g) {
             const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)xwv, NT > 0 ? g * NT + t : g);
             float x[16];
-            vals(acc[g], sc[g], x);
+            vals(acc[g], sc[g], sq, x);
             float mx = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -559,7 +572,7 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
               mx = ((w >> row) & 1u) ? mx : fmaxf(mx, x[i]);
             }
             mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));  // the block's other 16 rows
-            d[g] = (mx == -INFINITY) ? 0u : score_key(post(mx, sq));
+            d[g] = (mx == -INFINITY) ? 0u : score_key(mx);
             asm volatile("" : "+v"(d[g]));  // computed in uniform control flow, as above
           }
           if constexpr (NT > 0) {

@@ -296,8 +296,8 @@ __device__ void fallback_scan(const SelectArgs& A, int q, uint64_t thr, uint64_t
       }
       if (CT == MIPS_FP8_E4M3) s *= A.row_scale[i];
       // int8: the sum of code products is an integer below 2^24, exact in fp32 as in the
-      // MFMA path; then the row scale and the query scale, in the score pass's order
-      if (CT == MIPS_INT8) s = (s * A.row_scale[i]) * __int_as_float(A.qexp[qr]);
+      // MFMA path; then the query scale and the row scale, in the score pass's order
+      if (CT == MIPS_INT8) s = (s * __int_as_float(A.qexp[qr])) * A.row_scale[i];
       const uint64_t key = composite(score_key(s), (uint32_t)i);
       if (key >= thr) buf[atomicAdd(nbuf_p, 1u)] = key;
     }

@@ -24,7 +24,8 @@ Functions take and return numpy arrays:
 * ``merge_topk(scores, ids, offsets, k)`` -- merge of per-index sorted result lists
   ([p, b, k_in]) into one top-k per query, ids shifted by each index's offset.
 * ``maxsim_topk(queries [b, m, d], ...)`` -- top-k of users with m interest vectors each,
-  an item scored by its best match over the user's vectors.
+  an item scored by its best match over the user's vectors (``maxsim_topk_int8``: against
+  an int8 index by the quantised branch).
 * ``e4m3_value``, ``bf16_value``, ``bf16_from``, ``e4m3_from``, ``e4m3_row_scale``,
   ``i8_from``, ``i8_row_scale`` -- the scalar format helpers, exposed for the format pins.
 """
@@ -91,10 +92,11 @@ def lib():
         L.oracle_quantize.argtypes = [i32, p, i64, i32, i32, p, p]
         L.oracle_topk_int8.argtypes = [i32, p, i32, p, p, i64, i32, p, i32, p, p, i32]
         L.oracle_scores_int8.argtypes = [i32, p, i32, p, p, i64, i32, p, p, i64, p]
+        L.oracle_maxsim_topk_int8.argtypes = [i32, p, i32, i32, p, p, i64, i32, p, i32, p, p, i32]
         L.oracle_maxsim_topk.argtypes = [i32, p, i32, i32, i32, p, p, i64, i32, p, i32, p, p, i32]
         for f in (L.oracle_l2_normalize, L.oracle_prepare, L.oracle_topk, L.oracle_scores,
                   L.oracle_merge_topk, L.oracle_maxsim_topk, L.oracle_quantize,
-                  L.oracle_topk_int8, L.oracle_scores_int8):
+                  L.oracle_topk_int8, L.oracle_scores_int8, L.oracle_maxsim_topk_int8):
             f.restype = C.c_int
         _lib = L
     return _lib
@@ -325,4 +327,24 @@ def maxsim_topk(queries: np.ndarray, q_dtype: str, corpus: np.ndarray, c_dtype: 
                                     _ptr(corpus), _ptr(row_scale), n, d, _ptr(exclude), k,
                                     _ptr(out_s), _ptr(out_i), threads or default_threads()),
            "maxsim_topk")
+    return out_s, out_i
+
+
+def maxsim_topk_int8(queries: np.ndarray, q_dtype: str, corpus: np.ndarray, k: int,
+                     row_scale: np.ndarray, exclude: Optional[np.ndarray] = None,
+                     threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """maxsim_topk against an int8 index, each vector scored by the quantised branch."""
+    queries = np.ascontiguousarray(queries)
+    corpus = np.ascontiguousarray(corpus, np.int8)
+    b, m, d = queries.shape
+    n = corpus.shape[0]
+    row_scale = np.ascontiguousarray(row_scale, np.float32)
+    if exclude is not None:
+        exclude = np.ascontiguousarray(exclude, np.uint32)
+    out_s = np.empty((b, k), np.float64)
+    out_i = np.empty((b, k), np.int32)
+    _check(lib().oracle_maxsim_topk_int8(DTYPES[q_dtype], _ptr(queries), b, m, _ptr(corpus),
+                                         _ptr(row_scale), n, d, _ptr(exclude), k, _ptr(out_s),
+                                         _ptr(out_i), threads or default_threads()),
+           "maxsim_topk_int8")
     return out_s, out_i

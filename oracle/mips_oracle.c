@@ -299,14 +299,41 @@ static double stored_value(int32_t dtype, const void *base, int64_t idx)
     }
 }
 
-/* Exact-as-fp64 score of query row `qrow` against corpus row `i`. */
+/* Exact-as-fp64 score of query row `qrow` against corpus row `i`: the sum over
+ * dimensions, in order, of q[j] * (stored value * row scale). (One loop per format, the
+ * same arithmetic as stored_value element by element.) */
 static double score_one(const double *q, int32_t c_dtype, const void *corpus,
                         const float *row_scale, int64_t i, int32_t d)
 {
     double s = 0.0;
     double rs = (c_dtype == OR_E4M3 || c_dtype == OR_I8) ? (double)row_scale[i] : 1.0;
-    for (int32_t j = 0; j < d; ++j)
-        s += q[j] * (stored_value(c_dtype, corpus, i * (int64_t)d + j) * rs);
+    const int64_t base = i * (int64_t)d;
+    switch (c_dtype) {
+    case OR_F32: {
+        const float *c = (const float *)corpus + base;
+        for (int32_t j = 0; j < d; ++j)
+            s += q[j] * ((double)c[j] * rs);
+        break;
+    }
+    case OR_BF16: {
+        const uint16_t *c = (const uint16_t *)corpus + base;
+        for (int32_t j = 0; j < d; ++j)
+            s += q[j] * (oracle_bf16_value(c[j]) * rs);
+        break;
+    }
+    case OR_E4M3: {
+        const uint8_t *c = (const uint8_t *)corpus + base;
+        for (int32_t j = 0; j < d; ++j)
+            s += q[j] * (g_e4m3[c[j]] * rs);
+        break;
+    }
+    default: {
+        const int8_t *c = (const int8_t *)corpus + base;
+        for (int32_t j = 0; j < d; ++j)
+            s += q[j] * ((double)c[j] * rs);
+        break;
+    }
+    }
     return s;
 }
 
@@ -436,8 +463,9 @@ static void *topk_worker(void *arg)
     pair_t *pairs = (pair_t *)malloc(sizeof(pair_t) * (size_t)(J->n > 0 ? J->n : 1));
     double *q = (double *)malloc(sizeof(double) * (size_t)J->d * (size_t)J->m);
     float *qf = (float *)malloc(sizeof(float) * (size_t)J->d);
-    int32_t *uq = (int32_t *)malloc(sizeof(int32_t) * (size_t)J->d);
-    if (!pairs || !q || !qf || !uq) {
+    int32_t *uq = (int32_t *)malloc(sizeof(int32_t) * (size_t)J->d * (size_t)J->m);
+    float *usv = (float *)malloc(sizeof(float) * (size_t)J->m);
+    if (!pairs || !q || !qf || !uq || !usv) {
         pthread_mutex_lock(&J->lock);
         J->status = OR_NOMEM;
         pthread_mutex_unlock(&J->lock);
@@ -445,6 +473,7 @@ static void *topk_worker(void *arg)
         free(q);
         free(qf);
         free(uq);
+        free(usv);
         return NULL;
     }
     for (;;) {
@@ -456,20 +485,26 @@ static void *topk_worker(void *arg)
         /* result row b: query rows b*m .. b*m+m-1; an item scores its best match */
         for (int64_t j = 0; j < (int64_t)J->d * J->m; ++j)
             q[j] = stored_value(J->q_dtype, J->queries, (int64_t)b * J->m * J->d + j);
-        float us = 1.0f;
-        if (J->quantised) {
-            for (int32_t j = 0; j < J->d; ++j)
-                qf[j] = (float)q[j];
-            us = quantize_row_i8(qf, J->d, uq);
-        }
+        if (J->quantised)
+            for (int32_t v = 0; v < J->m; ++v) {
+                for (int32_t j = 0; j < J->d; ++j)
+                    qf[j] = (float)q[(int64_t)v * J->d + j];
+                usv[v] = quantize_row_i8(qf, J->d, uq + (int64_t)v * J->d);
+            }
         int64_t m = 0;
         for (int64_t i = 0; i < J->n; ++i) {
             if (excluded(J->exclude, i))
                 continue;
             if (J->quantised) {
-                pairs[m].s = (double)score_int8_row(uq, us, (const int8_t *)J->corpus +
-                                                                i * (int64_t)J->d,
+                const int8_t *row = (const int8_t *)J->corpus + i * (int64_t)J->d;
+                float best = score_int8_row(uq, usv[0], row, J->row_scale[i], J->d);
+                for (int32_t v = 1; v < J->m; ++v) {
+                    const float sv = score_int8_row(uq + (int64_t)v * J->d, usv[v], row,
                                                     J->row_scale[i], J->d);
+                    if (sv > best)
+                        best = sv;
+                }
+                pairs[m].s = (double)best;
                 pairs[m].id = (int32_t)i;
                 ++m;
                 continue;
@@ -501,6 +536,7 @@ static void *topk_worker(void *arg)
     free(q);
     free(qf);
     free(uq);
+    free(usv);
     return NULL;
 }
 
@@ -558,6 +594,19 @@ int oracle_maxsim_topk(int32_t q_dtype, const void *queries, int32_t b, int32_t 
         return OR_BAD_ARG;
     return topk_m(q_dtype, queries, b, m, c_dtype, corpus, row_scale, n, d, exclude, k, out_s,
                   out_id, threads, 0);
+}
+
+/* As oracle_maxsim_topk against an int8 index, each vector scored by the quantised
+ * branch (as oracle_topk_int8); an item scores its best over the user's vectors. */
+int oracle_maxsim_topk_int8(int32_t q_dtype, const void *queries, int32_t b, int32_t m,
+                            const void *corpus, const float *row_scale, int64_t n, int32_t d,
+                            const uint32_t *exclude, int32_t k, double *out_s, int32_t *out_id,
+                            int32_t threads)
+{
+    if (m < 1)
+        return OR_BAD_ARG;
+    return topk_m(q_dtype, queries, b, m, OR_I8, corpus, row_scale, n, d, exclude, k, out_s,
+                  out_id, threads, 1);
 }
 
 static int topk_m(int32_t q_dtype, const void *queries, int32_t b, int32_t mq, int32_t c_dtype,

@@ -6,7 +6,8 @@ import torch
 
 import exact_inner_product_amd as mips
 import oracle
-from tests.mips_check import TOL, check_topk, floor_for, untile
+from tests.mips_check import (TOL, check_topk, floor_for, int8_step, ref_scores, ref_topk,
+                               untile)
 from workloads import Workload, bitmap_from_ids
 
 pytestmark = pytest.mark.gpu
@@ -57,7 +58,7 @@ def run_case(n, d, b, k, cdt, qdt, seed, excl=0.0, workspace_bytes=None, x=None,
     s, i = s.cpu().numpy(), i.cpu().numpy()
     c_or, sc_or = oracle.prepare(x, cdt)
     q_or, _ = oracle.prepare(qraw, qdt)
-    o_s, o_i = oracle.topk(q_or, qdt, c_or, cdt, k, row_scale=sc_or, exclude=bitmap)
+    o_s, o_i = ref_topk(q_or, qdt, c_or, cdt, k, row_scale=sc_or, exclude=bitmap)
     return check_topk(s, i, o_s, o_i, q_or, qdt, c_or, cdt, sc_or, excluded or set(), n, TOL[cdt],
                       floor=floor_for(cdt, qdt))
 
@@ -367,7 +368,7 @@ def test_row_shards_merged_equal_one_pass(cdt, qdt, d):
     assert np.array_equal(i1, i2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
     c_or, sc_or = oracle.prepare(x, cdt)
     q_or, _ = oracle.prepare(qraw, qdt)
-    o_s, o_i = oracle.topk(q_or, qdt, c_or, cdt, k, row_scale=sc_or)
+    o_s, o_i = ref_topk(q_or, qdt, c_or, cdt, k, row_scale=sc_or)
     check_topk(s2, i2, o_s, o_i, q_or, qdt, c_or, cdt, sc_or, set(), n, TOL[cdt],
                floor=floor_for(cdt, qdt))
 
@@ -425,7 +426,7 @@ def test_topk_ranges_match_masked_oracle(cdt, qdt, d, n):
     for r, (lo, hi) in enumerate(ranges):
         print(f"range {r}: [{lo}, {hi})", flush=True)
         rbm = _range_bitmap(n, lo, hi, bm)
-        o_s, o_i = oracle.topk(q_or, qdt, c_or, cdt, k, row_scale=sc_or, exclude=rbm)
+        o_s, o_i = ref_topk(q_or, qdt, c_or, cdt, k, row_scale=sc_or, exclude=rbm)
         ids = np.arange(n)
         excluded = set(ids[((rbm[ids >> 5] >> (ids & 31).astype(np.uint32)) & 1) == 1].tolist())
         check_topk(s[r], i[r], o_s, o_i, q_or, qdt, c_or, cdt, sc_or, excluded, n, TOL[cdt],
@@ -452,25 +453,35 @@ def test_multi_interest_matches_maxsim_oracle(cdt, m, k):
     s, i = s.cpu().numpy(), i.cpu().numpy()
     c_or, sc_or = oracle.prepare(x, cdt)
     q_or, _ = oracle.prepare(qraw, "bf16")
-    o_s, o_i = oracle.maxsim_topk(q_or.reshape(b, m, d), "bf16", c_or, cdt, k, row_scale=sc_or,
-                                  exclude=bm)
+    if cdt == "int8":   # the quantised branch per vector, then the maximum
+        o_s, o_i = oracle.maxsim_topk_int8(q_or.reshape(b, m, d), "bf16", c_or, k, sc_or,
+                                           exclude=bm)
+    else:
+        o_s, o_i = oracle.maxsim_topk(q_or.reshape(b, m, d), "bf16", c_or, cdt, k,
+                                      row_scale=sc_or, exclude=bm)
     excluded = set(w.excluded_ids().tolist())
     # the acceptance rule per user, with the score of an id its best over the user's vectors
+    # (int8: within one code step of the row's quantised score per vector, else TOL)
     for u in range(b):
         gi = i[u][i[u] >= 0]
         assert len(set(gi.tolist())) == gi.size and not (set(gi.tolist()) & excluded)
         assert np.all(s[u][:-1] >= s[u][1:])
-        e = np.max([oracle.scores(q_or[u * m:(u + 1) * m], "bf16", c_or, cdt,
-                                  np.full(gi.size, v), gi, row_scale=sc_or) for v in range(m)],
+        e = np.max([ref_scores(q_or[u * m:(u + 1) * m], "bf16", c_or, cdt,
+                               np.full(gi.size, v), gi, row_scale=sc_or) for v in range(m)],
                    axis=0)
-        assert np.abs(s[u][: gi.size] - e).max() <= TOL[cdt]
-        assert np.abs(s[u] - o_s[u].astype(np.float32)).max() <= TOL[cdt]
+        if cdt == "int8":
+            tol = np.max([int8_step(q_or[u * m:(u + 1) * m], "bf16", sc_or, v, gi)
+                          for v in range(m)], axis=0)
+        else:
+            tol = np.full(gi.size, TOL[cdt])
+        assert np.all(np.abs(s[u][: gi.size] - e) <= tol)
+        assert np.abs(s[u] - o_s[u].astype(np.float32)).max() <= 2 * tol.max()
         diff = set(gi.tolist()) ^ set(o_i[u].tolist())
         kth = o_s[u, k - 1]
         for t in diff:
-            et = np.max(oracle.scores(q_or[u * m:(u + 1) * m], "bf16", c_or, cdt,
-                                      np.arange(m), np.full(m, t), row_scale=sc_or))
-            assert abs(et - kth) <= TOL[cdt], (u, t, et, kth)
+            et = np.max(ref_scores(q_or[u * m:(u + 1) * m], "bf16", c_or, cdt,
+                                   np.arange(m), np.full(m, t), row_scale=sc_or))
+            assert abs(et - kth) <= 2 * tol.max(), (u, t, et, kth)
 
 
 def test_recall_harness_against_exact():
@@ -504,7 +515,7 @@ def test_topk_per_item_type():
         i, s, v = i.cpu().numpy(), s.cpu().numpy(), v.cpu().numpy()
         other = np.nonzero(types != t)[0]
         tbm = bitmap_from_ids(other, n) | bm
-        o_s, o_i = oracle.topk(q_or, "bf16", c_or, "bf16", k, exclude=tbm)
+        o_s, o_i = ref_topk(q_or, "bf16", c_or, "bf16", k, exclude=tbm)
         excluded = set(other.tolist()) | set(w.excluded_ids().tolist())
         check_topk(s, i, o_s, o_i, q_or, "bf16", c_or, "bf16", None, excluded, n, TOL["bf16"],
                    floor=floor_for("bf16", "bf16"))
@@ -550,7 +561,7 @@ def _check_per_query(s, i, rows, q_or, qdt, c_or, cdt, sc_or, n, k):
     ids_all = np.arange(n)
     for qi in range(rows.shape[0]):
         bm = rows[qi]
-        o_s, o_i = oracle.topk(q_or[qi:qi + 1], qdt, c_or, cdt, k, row_scale=sc_or, exclude=bm)
+        o_s, o_i = ref_topk(q_or[qi:qi + 1], qdt, c_or, cdt, k, row_scale=sc_or, exclude=bm)
         excluded = set(ids_all[((bm[ids_all >> 5] >> (ids_all & 31).astype(np.uint32)) & 1) == 1].tolist())
         check_topk(s[qi:qi + 1], i[qi:qi + 1], o_s, o_i, q_or[qi:qi + 1], qdt, c_or, cdt, sc_or,
                    excluded, n, TOL[cdt], floor=floor_for(cdt, qdt))
@@ -573,7 +584,7 @@ def test_per_query_exclusion_matches_oracle(cdt, qdt, d, n, b, k):
     corpus, q = _gpu_inputs(w, x, qraw, dev)
     c_or, sc_or = oracle.prepare(x, cdt)
     q_or, _ = oracle.prepare(qraw, qdt)
-    _, top = oracle.topk(q_or, qdt, c_or, cdt, min(k, 300), row_scale=sc_or)
+    _, top = ref_topk(q_or, qdt, c_or, cdt, min(k, 300), row_scale=sc_or)
     rows = _per_query_masks(n, b, np.random.default_rng(71), top)
     print(f"case per-query n={n} d={d} b={b} k={k} {cdt}/{qdt}", flush=True)
     s, i = mips.topk(q, corpus, k, torch.from_numpy(rows.view(np.int32)).to(dev))
@@ -653,7 +664,7 @@ def _check_mask_rows(s, i, rows, q_or, qdt, c_or, cdt, sc_or, n, k):
     for t in range(rows.shape[0]):
         print(f"mask {t}", flush=True)
         bm = rows[t]
-        o_s, o_i = oracle.topk(q_or, qdt, c_or, cdt, k, row_scale=sc_or, exclude=bm)
+        o_s, o_i = ref_topk(q_or, qdt, c_or, cdt, k, row_scale=sc_or, exclude=bm)
         excluded = set(ids_all[((bm[ids_all >> 5] >> (ids_all & 31).astype(np.uint32)) & 1) == 1].tolist())
         check_topk(s[t], i[t], o_s, o_i, q_or, qdt, c_or, cdt, sc_or, excluded, n, TOL[cdt],
                    floor=floor_for(cdt, qdt))
@@ -737,7 +748,7 @@ def test_topk_types_more_than_one_pass():
     for t, (i, s) in zip(targets, res):
         i, s = i.cpu().numpy(), s.cpu().numpy()
         other = np.nonzero(types != t)[0]
-        o_s, o_i = oracle.topk(q_or, "bf16", c_or, "bf16", k, exclude=bitmap_from_ids(other, n))
+        o_s, o_i = ref_topk(q_or, "bf16", c_or, "bf16", k, exclude=bitmap_from_ids(other, n))
         check_topk(s, i, o_s, o_i, q_or, "bf16", c_or, "bf16", None, set(other.tolist()), n,
                    TOL["bf16"], floor=floor_for("bf16", "bf16"))
 

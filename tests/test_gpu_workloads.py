@@ -10,7 +10,9 @@ import torch
 
 import exact_inner_product_amd as mips
 import oracle
-from tests.mips_check import TOL, check_topk, floor_for, threads
+from tests.mips_check import (TOL, check_operands, check_topk, floor_for, operand_reference,
+                               operands_are_inputs, query_tensor, ref_topk, threads,
+                               upload_corpus)
 from workloads import WORKLOADS
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -46,7 +48,10 @@ def build_both(w, dev):
     return corpus, q, bm, codes, scale, q_or
 
 
-def run_workload(name, sample):
+def run_workload(name, sample, exact_sample=()):
+    """sample: queries checked end to end (each side builds its own index from the raw
+    rows) against the oracle's top-k; exact_sample: queries checked when the GPU searches the
+    oracle's own codes, against the exact scores of its operands (check_operands)."""
     if not torch.cuda.is_available():
         pytest.skip("needs a GPU")
     dev = torch.device("cuda:0")
@@ -70,42 +75,74 @@ def run_workload(name, sample):
     if excluded:
         ex = np.array(sorted(excluded))
         assert not np.isin(i, ex).any()
-    # sampled queries against the oracle
     sel = np.array(sorted(set(sample)), np.int64)
-    print(f"workload {name}: oracle on queries {sel.tolist()}", flush=True)
-    o_s, o_i = oracle.topk(q_or[sel], w.query_dtype, codes, w.corpus_dtype, w.k, row_scale=scale,
-                           exclude=bm, threads=threads())
+    xsel = np.array(sorted(set(exact_sample)), np.int64)
+    # the oracle's top-k of the operands serves the end-to-end check too when the GPU
+    # multiplies the queries as given
+    share = operands_are_inputs(w.query_dtype, w.corpus_dtype) and set(sel) <= set(xsel)
+    xref = None
+    if xsel.size:
+        print(f"workload {name}: oracle on {xsel.size} queries", flush=True)
+        xref = operand_reference(q_or[xsel], w.query_dtype, codes, w.corpus_dtype, w.k,
+                                 row_scale=scale, exclude=bm, threads_=threads())
+    if share:
+        pos = np.searchsorted(xsel, sel)
+        o_s, o_i = xref[0][pos], xref[1][pos]
+    else:
+        print(f"workload {name}: oracle on queries {sel.tolist()}", flush=True)
+        o_s, o_i = ref_topk(q_or[sel], w.query_dtype, codes, w.corpus_dtype, w.k,
+                            row_scale=scale, exclude=bm, threads=threads())
     stats = check_topk(s[sel], i[sel], o_s, o_i, q_or[sel], w.query_dtype, codes, w.corpus_dtype,
                        scale, excluded, w.n, TOL[w.corpus_dtype],
                        floor=floor_for(w.corpus_dtype, w.query_dtype))
-    print(f"workload {name}: {stats}", flush=True)
+    print(f"workload {name}: end to end: {stats}", flush=True)
+    if not xsel.size:
+        return
+    # the same search over the oracle's own codes, in the same launch configuration
+    del corpus, q
+    torch.cuda.empty_cache()
+    oc = upload_corpus(codes, scale, w.corpus_dtype, dev)
+    s2, i2 = mips.topk(query_tensor(q_or, w.query_dtype, dev), oc, w.k, excl)
+    torch.cuda.synchronize()
+    s2, i2 = s2.cpu().numpy(), i2.cpu().numpy()
+    stats = check_operands(s2[xsel], i2[xsel], q_or[xsel], w.query_dtype, codes, w.corpus_dtype,
+                           scale, excluded, w.n, exclude_bitmap=bm, ref=xref)
+    print(f"workload {name}: oracle codes, {xsel.size} queries: {stats}", flush=True)
+
+
+def _spread(b, count, seed):
+    """count seeded query indices of a batch of b, the first and the last included."""
+    rng = np.random.default_rng(seed)
+    return sorted({0, b - 1, *rng.choice(b, count - 2, replace=False).tolist()})
 
 
 def test_tiny_f32():
-    run_workload("tiny_f32_n400_d16", range(128))
+    run_workload("tiny_f32_n400_d16", range(128), range(128))
 
 
 def test_bf16_n1m():
-    run_workload("bf16_n1m_d128_b16", range(16))
+    run_workload("bf16_n1m_d128_b16", range(16), range(16))
 
 
 @pytest.mark.timeout(900)
 def test_bf16_n10m_headline():
-    run_workload("bf16_n10m_d128_b256_excl5", [0, 1, 31, 32, 100, 128, 200, 255])
+    run_workload("bf16_n10m_d128_b256_excl5", [0, 1, 31, 32, 100, 128, 200, 255], range(256))
 
 
 @pytest.mark.timeout(900)
 def test_fp8_n10m():
-    run_workload("fp8_n10m_d256_b4096", [0, 1, 511, 512, 2047, 3000, 4094, 4095])
+    run_workload("fp8_n10m_d256_b4096", [0, 1, 511, 512, 2047, 3000, 4094, 4095],
+                 _spread(4096, 64, 5))
 
 
 @pytest.mark.timeout(1200)
 def test_int8_n10m():
-    run_workload("int8_n10m_d128_b256_excl5", [0, 1, 63, 64, 127, 200, 254, 255])
+    run_workload("int8_n10m_d128_b256_excl5", [0, 1, 63, 64, 127, 200, 254, 255], range(256))
 
 
+@pytest.mark.timeout(1500)
 def test_bf16_n100m():
-    run_workload("bf16_n100m_d64_b1024", [0, 1023])
+    run_workload("bf16_n100m_d64_b1024", [0, 1023], _spread(1024, 64, 4))
 
 
 @pytest.mark.timeout(1200)
@@ -137,7 +174,7 @@ def test_bf16_n10m_four_masks():
         bad = ((rows[t][np.maximum(i[t], 0) >> 5] >> (np.maximum(i[t], 0) & 31).astype(np.uint32)) & 1) == 1
         assert not (bad & (i[t] >= 0)).any(), f"mask {t}: an excluded id was returned"
         print(f"four masks: oracle, mask {t}", flush=True)
-        o_s, o_i = oracle.topk(q_or[sel], w.query_dtype, codes, w.corpus_dtype, w.k,
+        o_s, o_i = ref_topk(q_or[sel], w.query_dtype, codes, w.corpus_dtype, w.k,
                                exclude=rows[t], threads=threads())
         excluded = set(ids_all[((rows[t][ids_all >> 5] >> (ids_all & 31).astype(np.uint32)) & 1) == 1].tolist())
         stats = check_topk(s[t][sel], i[t][sel], o_s, o_i, q_or[sel], w.query_dtype, codes,

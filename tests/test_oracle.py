@@ -592,3 +592,20 @@ def test_prepare_rows_below_the_norm_floor(dtype):
         assert np.array_equal(codes.astype(np.int32), ref_q)
         assert scale[0] == np.float32(1e-12)
     assert not np.any(codes[0])
+
+
+def test_maxsim_int8_reduces_to_topk_int8_and_takes_the_max():
+    rng = np.random.default_rng(46)
+    n, d, b, m, k = 120, 32, 3, 3, 25
+    cq, cs = oracle.prepare(rng.standard_normal((n, d)).astype(np.float32), "int8")
+    q, _ = oracle.prepare(rng.standard_normal((b * m, d)).astype(np.float32), "bf16")
+    s1, i1 = oracle.maxsim_topk_int8(q.reshape(b * m, 1, d), "bf16", cq, k, cs)
+    s2, i2 = oracle.topk_int8(q, "bf16", cq, k, cs)
+    assert np.array_equal(i1, i2) and np.array_equal(s1, s2)
+    s, i = oracle.maxsim_topk_int8(q.reshape(b, m, d), "bf16", cq, k, cs)
+    for u in range(b):
+        per = np.stack([oracle.scores_int8(q, "bf16", cq, cs, np.full(n, u * m + v), np.arange(n))
+                        for v in range(m)])
+        best = per.max(axis=0)
+        order = sorted(range(n), key=lambda j: (-best[j], j))[:k]
+        assert i[u].tolist() == order and s[u].tolist() == best[order].tolist()
