@@ -113,7 +113,7 @@ def run_workload(name, sample, exact_sample=()):
 def _spread(b, count, seed):
     """count seeded query indices of a batch of b, the first and the last included."""
     rng = np.random.default_rng(seed)
-    return sorted({0, b - 1, *rng.choice(b, count - 2, replace=False).tolist()})
+    return sorted({0, b - 1, *(1 + rng.choice(b - 2, count - 2, replace=False)).tolist()})
 
 
 def test_tiny_f32():
