@@ -41,4 +41,21 @@ int device_cu_count();
 // Timing hook of mips_set_timing_events.
 void timing_events(hipEvent_t* before, hipEvent_t* after);
 
+// The top-k entry points' shared parts (topk.hip): argument validation without any HIP call;
+// validation and the passes over a caller-given workspace; the workspace a call needs with
+// `candidates` per list (< 0: the default capacity), 0 for unsupported arguments.
+int validate_entry(const void* queries, int32_t query_dtype, int32_t b, const void* corpus,
+                   const float* row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
+                   const uint32_t* exclude, int64_t exclude_row_words, const uint32_t* masks,
+                   int32_t nmasks, int64_t mask_words, const int64_t* ranges, int32_t nranges,
+                   int32_t k, const float* out_scores, const int32_t* out_ids);
+int topk_entry(const void* queries, int32_t query_dtype, int32_t b, const void* corpus,
+               const float* row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
+               const uint32_t* exclude, int64_t exclude_row_words, const uint32_t* masks,
+               int32_t nmasks, int64_t mask_words, const int64_t* ranges, int32_t nranges,
+               int32_t k, float* out_scores, int32_t* out_ids, void* workspace,
+               size_t workspace_bytes, void* stream);
+size_t workspace_bytes_for(int32_t b, int64_t n, int32_t d, int32_t k, int32_t qdt, int32_t cdt,
+                           int32_t nmasks, int64_t candidates);
+
 }  // namespace mips

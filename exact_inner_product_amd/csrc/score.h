@@ -169,7 +169,7 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
       }
       if (blockIdx.x == 0) {
         for (int i = threadIdx.x; i < A.nflags; i += kScoreThreads) A.ovf[i] = 0u;
-        if (threadIdx.x == 0) *A.nfail = 0u;
+        if (threadIdx.x < 2) A.nfail[threadIdx.x] = 0u;  // the rescue queue and rescan counts
       }
       for (int i = threadIdx.x; i < QB; i += kScoreThreads) {
         qid_lds[i] = qbase + i < A.b ? qbase + i : -1;
@@ -299,10 +299,15 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
         if (e < nst) {
           const uint64_t ck = st_key[e];
           const int qc = st_q[e];
-          const uint32_t pos = atomicAdd(&seg_lds[qc], 1u);
-          if ((int64_t)pos < A.capw) {
-            const int64_t list = NT > 0 ? listid(qc / NTS, qc % NTS) : qid_lds[qc];
-            A.cand[(list * A.nseg + slice) * A.capw + pos] = ck;
+          const int64_t list = NT > 0 ? listid(qc / NTS, qc % NTS) : qid_lds[qc];
+          if (rescue) {
+            // a rescued list is one run for the whole pass: few lists and few survivors,
+            // so one global atomic per survivor
+            const uint32_t pos = atomicAdd(&A.rtail[list], 1u);
+            if ((int64_t)pos < (int64_t)A.nseg * A.capw) A.cand[list * A.nseg * A.capw + pos] = ck;
+          } else {
+            const uint32_t pos = atomicAdd(&seg_lds[qc], 1u);
+            if ((int64_t)pos < A.capw) A.cand[(list * A.nseg + slice) * A.capw + pos] = ck;
           }
         }
       }
@@ -456,18 +461,23 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
         H &= H - 1ull;
         uint32_t pl = (uint32_t)__builtin_amdgcn_readlane((int)pm, L);
         const int qcol = qf * kFrag + (L & 31);
+        // column L's threshold (T is per lane: each lane holds its own column's)
+        const float TL = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(T), L));
         while (pl != 0u) {
           const int i = __builtin_ctz(pl);
           pl &= pl - 1u;
           const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(y[i]), L));
           const uint32_t id = idb + (uint32_t)(8 * (i >> 2) + 4 * (L >> 5) + (i & 3));
+          // a rescue threshold is composite: at the threshold's own score only ids at or
+          // below its id bound pass (rows tied with the k-th candidate cannot flood it)
+          if (rescue && v == TL && id > A.thr_id[listid(qcol, t)]) continue;
           if (st_n < kStageCap) {
             if (lane == 0) {
               st_key[st_n] = composite(score_key(v), id);
               st_q[st_n] = (uint16_t)(NT > 0 ? qcol * NTS + t : qcol);
             }
           } else if (lane == 0) {
-            atomicOr(&A.ovf[listid(qcol, t)], 1u);  // no room: the query is rescued
+            atomicOr(&A.ovf[listid(qcol, t)], 1u);  // no room: the list is rescued
           }
           ++st_n;
         }
@@ -671,9 +681,10 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
     }
     if (MODE == MODE_MAIN) {
       if (st_n > 0) flush();
-      // this workgroup's segment counts of the block's queries
+      // this workgroup's segment counts of the block's queries (a rescued list counts
+      // through its tail instead)
       __syncthreads();
-      for (int i = threadIdx.x; i < QB * NTS; i += kScoreThreads) {
+      for (int i = threadIdx.x; i < QB * NTS && !rescue; i += kScoreThreads) {
         const int c = i / NTS, t = i % NTS;
         const int q = qid_lds[c];
         if (q >= 0 && (NT == 0 || (t < A.nmask && (!rescue || q / A.b == t))))

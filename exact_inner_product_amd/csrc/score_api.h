@@ -101,6 +101,12 @@ struct ScoreArgs {
   int nqblk;        // query blocks in the grid
   int nslices;      // corpus slices in the grid
   const uint32_t* thr;    // per-query threshold keys (0: query not scored here)
+  // rescue pass: per-list id bound of a composite threshold (a row whose score equals the
+  // list's threshold passes only with an id at or below it), and per-list survivor
+  // counts; a rescued list is one contiguous run of nseg * capw entries, filled through
+  // its count as an atomic tail
+  const uint32_t* thr_id;
+  uint32_t* rtail;
   uint32_t* segcnt;       // [b][nseg] survivors found per (query, segment)
   uint32_t* ovf;
   uint64_t* cand;         // [b][nseg][capw] candidate keys; dense pass: [b][nseg * capw]

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict
   *(u32x4_t*)(qtile + (int64_t)qb * block_bytes(CT, D) + (int64_t)c * kChunkBytes + lane * 16) = v;
   // the overflow flag of every list (query, or virtual query of a multi-mask pass)
   for (int i = blockIdx.x * 64 + lane; i < nflags; i += gridDim.x * 64) ovf[i] = 0u;
-  if (blockIdx.x == 0 && lane == 0) *nfail = 0u;
+  if (blockIdx.x == 0 && lane < 2) nfail[lane] = 0u;  // the rescue queue and rescan counts
 }
 
 // ------------------------------------------------------------ sampled threshold
@@ -216,10 +216,12 @@ struct SelectArgs {
   int64_t dense_count;  // > 0: lists hold one slot per row (0 = empty), this many
   uint32_t* thr;
   uint32_t* thrb;
+  uint32_t* thr_id;     // id bound of a rescue's composite threshold
+  uint32_t* rtail;      // survivors of a rescued list (its contiguous run's tail)
   const uint32_t* segcnt;
   uint32_t* ovf;
   const uint64_t* cand;
-  uint32_t* nfail;
+  uint32_t* nfail;      // [0]: lists queued for rescue; [1]: lists resolved by the rescan
   uint32_t* flist;
   float* out_scores;
   int32_t* out_ids;
@@ -333,6 +335,27 @@ __device__ inline uint2 block_exclusive_sum(uint32_t v, uint32_t* wsum) {
   return make_uint2(before + c - v, total);
 }
 
+// Queues list q for the rescue pass with the composite threshold (key nt, id bound nid);
+// `every` also sets the proven bound to the every-row key. One thread per list.
+__device__ inline void queue_rescue(const SelectArgs& A, int q, uint32_t nt, uint32_t nid,
+                                    bool every) {
+  const uint32_t slot = atomicAdd(A.nfail, 1u);
+  A.flist[slot] = (uint32_t)q;
+  A.thr[q] = nt;
+  A.thr_id[q] = nid;
+  if (every) A.thrb[q] = nt;
+  A.ovf[q] = 0u;
+  A.rtail[q] = 0u;
+}
+
+// The exact rescan of list q (the last resort), counted in nfail[1].
+template <int CT, int D>
+__device__ void rescan(const SelectArgs& A, int q, uint64_t* cache, uint64_t* sel_buf,
+                       SelScratch& S, float* qv, uint32_t* nbuf) {
+  if (threadIdx.x == 0) atomicAdd(A.nfail + 1, 1u);
+  fallback_scan<CT, D>(A, q, 0ull, cache, sel_buf, S, qv, nbuf);
+}
+
 // Lists of at most this many candidates (and at most 4 k) are sorted whole instead of
 // radix-selected first; for a k much smaller than the list, selecting first is cheaper.
 constexpr int kSortAll = 512;
@@ -417,28 +440,33 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
     // few eligible rows): the rescue pass gathers every eligible row on the MFMA path, and
     // its list is complete unless it overflows.
     if (round > 0) {
-      fallback_scan<CT, D>(A, q, 0ull, cache, sel_buf, S, qv, &nbuf);
+      rescan<CT, D>(A, q, cache, sel_buf, S, qv, &nbuf);
       return;
     }
-    if (t == 0) {
-      const uint32_t slot = atomicAdd(A.nfail, 1u);
-      A.flist[slot] = (uint32_t)q;
-      A.thr[q] = kEveryRowKey;
-      A.thrb[q] = kEveryRowKey;
-      A.ovf[q] = 0u;
-    }
+    if (t == 0) queue_rescue(A, q, kEveryRowKey, 0xFFFFFFFFu, true);
     return;
   }
-  // segment s: found (counted by the pass) and stored (what fits the segment)
-  const uint32_t found = t < A.nseg_used ? A.segcnt[(int64_t)q * A.nseg + t] : 0u;
-  const uint32_t mine = found < (uint32_t)A.capw ? found : (uint32_t)A.capw;
+  // segment s: found (counted by the pass) and stored (what fits the segment). A rescued
+  // list (round 1) is one run of nseg * capw entries with its count in rtail; it is read
+  // as nseg segments of capw.
+  uint32_t found, mine;
+  int64_t total;  // everything the pass found for this list
+  if (round == 0) {
+    found = t < A.nseg_used ? A.segcnt[(int64_t)q * A.nseg + t] : 0u;
+    mine = found < (uint32_t)A.capw ? found : (uint32_t)A.capw;
+  } else {
+    const int64_t r = (int64_t)A.rtail[q] - (int64_t)t * A.capw;
+    found = 0u;
+    mine = t < A.nseg && r > 0 ? (uint32_t)min<int64_t>(r, A.capw) : 0u;
+  }
   const uint2 so = block_exclusive_sum(mine, wsum);
   const uint2 sf = block_exclusive_sum(found, wsum);
   segoff[t] = so.x;
   if (t == 0) segoff[kSelThreads] = so.y;
   const int64_t stored = so.y;
-  c = sf.y;
-  const int nsu = A.nseg_used;
+  total = round == 0 ? (int64_t)sf.y : (int64_t)A.rtail[q];
+  c = total;
+  const int nsu = round == 0 ? A.nseg_used : A.nseg;
   // entry i of the concatenated segments: the last segment starting at or before i
   auto at = [&](int64_t i) {
     int lo = 0, hi = nsu;
@@ -472,25 +500,25 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
   const bool shortfall = !over && tu != kEveryRowKey && eligible < A.k && (tu > tb || own);
   if (over || shortfall) {
     if (round > 0 || (shortfall && tu == tb)) {
-      fallback_scan<CT, D>(A, q, 0ull, cache, sel_buf, S, qv, &nbuf);
+      rescan<CT, D>(A, q, cache, sel_buf, S, qv, &nbuf);
       return;
     }
     // Rescue threshold: the proven bound after a shortfall (every row if the sample proved
-    // none); after an overflow, the k-th best stored candidate (k real items reach it).
-    uint32_t nt = tb == 0u ? kEveryRowKey : tb;
+    // none); after an overflow, the composite key of the k-th best stored candidate (k real
+    // items reach it): rows above its score, and rows at its score with an id at or below
+    // its id, so rows tied with it cannot overflow the rescue.
+    uint32_t nt = tb == 0u ? kEveryRowKey : tb, nid = 0xFFFFFFFFu;
     if (over) {
       nt = tu;
       if (eligible >= A.k) {
-        const uint32_t kth = (uint32_t)(select_top(atx, stored, A.k, S).prefix >> 32);
-        nt = kth > nt ? kth : nt;
+        const uint64_t kth = select_top(atx, stored, A.k, S).prefix;
+        if ((uint32_t)(kth >> 32) >= nt) {
+          nt = (uint32_t)(kth >> 32);
+          nid = composite_id(kth);
+        }
       }
     }
-    if (t == 0) {
-      const uint32_t slot = atomicAdd(A.nfail, 1u);
-      A.flist[slot] = (uint32_t)q;
-      A.thr[q] = nt;
-      A.ovf[q] = 0u;
-    }
+    if (t == 0) queue_rescue(A, q, nt, nid, false);
     return;
   }
   const int r = (int)min<int64_t>(eligible, A.k);
@@ -536,8 +564,8 @@ struct Plan {
   int rm, rm_main, nqf, nqblk, G, rest, nseg;  // blocks per stage: sample/dense, main
   bool dense;
   int64_t capw;  // candidate entries per list segment
-  size_t off_qtile, off_qexp, off_thr, off_thrb, off_ovf, off_nfail, off_flist, off_segcnt,
-      off_del, off_cand, fixed;
+  size_t off_qtile, off_qexp, off_thr, off_thrb, off_ovf, off_thrid, off_rtail, off_nfail,
+      off_flist, off_segcnt, off_del, off_cand, fixed;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -603,6 +631,9 @@ static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt,
   p.rest = p.dense ? 0 : estimate_rank(p.n32, p.G, k);
   const int E = elem_bytes(cdt);
   size_t o = 0;
+  // first: the rescue queue count and the rescan count (bytes 0..7 of the workspace)
+  p.off_nfail = o;
+  o = align256(o + 8);
   p.off_qtile = o;
   o = align256(o + (size_t)p.b32 * d * E);
   p.off_qexp = o;
@@ -614,8 +645,10 @@ static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt,
   o = align256(o + (size_t)p.bv * 4);
   p.off_ovf = o;
   o = align256(o + (size_t)p.bv * 4);
-  p.off_nfail = o;
-  o = align256(o + 4);
+  p.off_thrid = o;
+  o = align256(o + (size_t)p.bv * 4);
+  p.off_rtail = o;
+  o = align256(o + (size_t)p.bv * 4);
   p.off_flist = o;
   o = align256(o + (size_t)p.bv * 4);
   p.off_segcnt = o;
@@ -642,6 +675,8 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   uint32_t* flist = (uint32_t*)(ws + p.off_flist);
   uint32_t* del = (uint32_t*)(ws + p.off_del);
   uint64_t* cand = (uint64_t*)(ws + p.off_cand);
+  uint32_t* thr_id = (uint32_t*)(ws + p.off_thrid);
+  uint32_t* rtail = (uint32_t*)(ws + p.off_rtail);
 
   // A sampled pass over a bf16 or f32 index builds the operand tile in its sample pass (no
   // query scale to compute there); otherwise the prep kernel builds it.
@@ -709,6 +744,8 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   S.nseg = p.nseg;
   S.thr = thr;
   S.thrb = thrb;
+  S.thr_id = thr_id;
+  S.rtail = rtail;
   S.segcnt = segcnt;
   S.ovf = ovf;
   S.cand = cand;
@@ -765,6 +802,8 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   ScoreArgs R = A;
   R.qlist = flist;
   R.nlist = nfail;
+  R.thr_id = thr_id;
+  R.rtail = rtail;
   R.nqblk = 1;
   R.nslices = slices_for(A.ntiles, 1);
   if ((rc = launch_score_nqf<CT, D, MODE_MAIN, NT>(p.nqf, R, R.nslices, s))) return rc;
@@ -807,16 +846,14 @@ static int validate_topk(int32_t qdt, int32_t b, int32_t cdt, int64_t n, int32_t
 
 static_assert(kMaxMasks == MIPS_MAX_MASKS, "the header's mask limit is the kernel's");
 
-// Every top-k entry point: validation, then one pass per id range (nmasks > 0: one
-// multi-mask pass over the whole corpus, lists per (mask, query)).
-static int topk_entry(const void* queries, int32_t query_dtype, int32_t b, const void* corpus,
-                      const float* row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
-                      const uint32_t* exclude, int64_t exclude_row_words, const uint32_t* masks,
-                      int32_t nmasks, int64_t mask_words, const int64_t* ranges, int32_t nranges,
-                      int32_t k, float* out_scores, int32_t* out_ids, void* workspace,
-                      size_t workspace_bytes, void* stream) {
-  if (!queries || !corpus || !out_scores || !out_ids || !workspace || !ranges)
-    return MIPS_ERR_INVALID_ARG;
+// Validation shared by every top-k entry point (no HIP call; the workspace is checked by
+// topk_entry).
+int validate_entry(const void* queries, int32_t query_dtype, int32_t b, const void* corpus,
+                   const float* row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
+                   const uint32_t* exclude, int64_t exclude_row_words, const uint32_t* masks,
+                   int32_t nmasks, int64_t mask_words, const int64_t* ranges, int32_t nranges,
+                   int32_t k, const float* out_scores, const int32_t* out_ids) {
+  if (!queries || !corpus || !out_scores || !out_ids || !ranges) return MIPS_ERR_INVALID_ARG;
   const int rc0 = validate_topk(query_dtype, b, corpus_dtype, n, d, k);
   if (rc0 != MIPS_OK) return rc0;
   if (nranges < 1) return MIPS_ERR_INVALID_ARG;
@@ -830,10 +867,26 @@ static int topk_entry(const void* queries, int32_t query_dtype, int32_t b, const
   if ((int64_t)b * std::max(nmasks, 1) > MIPS_B_MAX) return MIPS_ERR_UNSUPPORTED;
   if ((corpus_dtype == MIPS_FP8_E4M3 || corpus_dtype == MIPS_INT8) && !row_scale)
     return MIPS_ERR_INVALID_ARG;
-  if (!aligned(queries, 4) || !aligned(corpus, 16) || !aligned(workspace, 256) ||
-      !aligned(out_scores, 4) || !aligned(out_ids, 4) ||
-      (exclude && !aligned(exclude, 4)) || (row_scale && !aligned(row_scale, 4)))
+  if (!aligned(queries, 4) || !aligned(corpus, 16) || !aligned(out_scores, 4) ||
+      !aligned(out_ids, 4) || (exclude && !aligned(exclude, 4)) ||
+      (row_scale && !aligned(row_scale, 4)))
     return MIPS_ERR_INVALID_ARG;
+  return MIPS_OK;
+}
+
+// Every top-k entry point: validation, then one pass per id range (nmasks > 0: one
+// multi-mask pass over the whole corpus, lists per (mask, query)).
+int topk_entry(const void* queries, int32_t query_dtype, int32_t b, const void* corpus,
+               const float* row_scale, int32_t corpus_dtype, int64_t n, int32_t d,
+               const uint32_t* exclude, int64_t exclude_row_words, const uint32_t* masks,
+               int32_t nmasks, int64_t mask_words, const int64_t* ranges, int32_t nranges,
+               int32_t k, float* out_scores, int32_t* out_ids, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  const int rcv = validate_entry(queries, query_dtype, b, corpus, row_scale, corpus_dtype, n, d,
+                                 exclude, exclude_row_words, masks, nmasks, mask_words, ranges,
+                                 nranges, k, out_scores, out_ids);
+  if (rcv != MIPS_OK) return rcv;
+  if (!workspace || !aligned(workspace, 256)) return MIPS_ERR_INVALID_ARG;
   // the whole corpus's plan bounds every range's fixed part and capacity
   Plan p;
   make_plan(p, b, n, d, k, query_dtype, corpus_dtype, -1, 0, nmasks);
@@ -868,8 +921,8 @@ static int topk_entry(const void* queries, int32_t query_dtype, int32_t b, const
   return MIPS_OK;
 }
 
-static size_t workspace_bytes_for(int32_t b, int64_t n, int32_t d, int32_t k, int32_t qdt,
-                                  int32_t cdt, int32_t nmasks, int64_t candidates) {
+size_t workspace_bytes_for(int32_t b, int64_t n, int32_t d, int32_t k, int32_t qdt,
+                           int32_t cdt, int32_t nmasks, int64_t candidates) {
   if (validate_topk(qdt, b, cdt, n, d, k) != MIPS_OK) return 0;
   if (nmasks < 0 || nmasks > kMaxMasks || (int64_t)b * std::max(nmasks, 1) > MIPS_B_MAX) return 0;
   Plan p;

@@ -12,8 +12,8 @@
  * Entry points: mips_l2_normalize and mips_prepare_corpus (normalisation, index build);
  * mips_topk (one result set per query), mips_topk_ranges (one per id range) and
  * mips_topk_masks (one per exclusion mask, from one pass over the index), with their
- * workspace sizes; mips_merge_topk and mips_merge_interests (merges of sorted result
- * lists); mips_type_bitmap (per-type exclusion bitmaps); status strings and a timing hook.
+ * workspace sizes; mips_merge_topk and mips_merge_interests (merges of sorted result lists);
+ * mips_type_bitmap (per-type exclusion bitmaps); status strings and a timing hook.
  *
  * Conventions shared by every entry point:
  *  - All buffers are caller-owned. Pointers marked "device" are HIP device memory;
@@ -186,8 +186,11 @@ MIPS_API size_t mips_topk_workspace_size_for(int32_t b, int64_t n, int32_t d, in
  *   workspace    device, 256-byte aligned; the fixed part plus at least one candidate
  *                per query and list segment (mips_topk_workspace_size gives the default,
  *                mips_topk_workspace_size_for any other capacity); its contents are
- *                undefined between calls. Calls that share a workspace must be ordered on
- *                one stream.
+ *                undefined between calls, except two diagnostic counts (uint32) that the
+ *                call's last pass leaves in bytes 0..7: the result lists queued for the
+ *                rescue pass, and the lists resolved by the exact one-workgroup rescan
+ *                (slow; 0 unless a rescue pass also overflows). Calls that share a
+ *                workspace must be ordered on one stream.
  * Errors: INVALID_ARG (NULL where a buffer is required, b/n/k out of range, fp8 or int8
  * without row_scale, misalignment), UNSUPPORTED (d, k > MIPS_K_MAX, b > MIPS_B_MAX, dtype
  * pair), WORKSPACE (workspace_bytes too small), HIP (a launch failed); INVALID_ARG also for

@@ -51,7 +51,9 @@ def run_case(n, d, b, k, cdt, qdt, seed, excl=0.0, workspace_bytes=None, x=None,
         ids = np.arange(n)
         excluded = set(ids[((bitmap[ids >> 5] >> (ids & 31).astype(np.uint32)) & 1) == 1].tolist())
     corpus, q = _gpu_inputs(w, x, qraw, dev)
-    ws = None if workspace_bytes is None else mips.empty_workspace(workspace_bytes, dev)
+    if workspace_bytes is None:
+        workspace_bytes = mips.workspace_size(b, n, d, k, qdt, cdt)
+    ws = mips.empty_workspace(workspace_bytes, dev)
     print(f"case n={n} d={d} b={b} k={k} {cdt}/{qdt} excl={excl} seed={seed}", flush=True)
     s, i = mips.topk(q, corpus, k, _excl_tensor(bitmap, dev), workspace=ws)
     torch.cuda.synchronize()
@@ -59,8 +61,18 @@ def run_case(n, d, b, k, cdt, qdt, seed, excl=0.0, workspace_bytes=None, x=None,
     c_or, sc_or = oracle.prepare(x, cdt)
     q_or, _ = oracle.prepare(qraw, qdt)
     o_s, o_i = ref_topk(q_or, qdt, c_or, cdt, k, row_scale=sc_or, exclude=bitmap)
-    return check_topk(s, i, o_s, o_i, q_or, qdt, c_or, cdt, sc_or, excluded or set(), n, TOL[cdt],
-                      floor=floor_for(cdt, qdt))
+    st = check_topk(s, i, o_s, o_i, q_or, qdt, c_or, cdt, sc_or, excluded or set(), n, TOL[cdt],
+                    floor=floor_for(cdt, qdt))
+    st.update(_ws_counts(ws))
+    print(f"case stats: {st}", flush=True)
+    return st
+
+
+def _ws_counts(ws):
+    """The diagnostic counts a call leaves in bytes 0..7 of its workspace (include/mips.h):
+    lists queued for the rescue pass, lists resolved by the exact rescan."""
+    c = ws[:8].cpu().numpy().view(np.uint32)
+    return {"queued": int(c[0]), "rescans": int(c[1])}
 
 
 # --------------------------------------------------------------- prepare parity
@@ -219,20 +231,27 @@ def test_all_excluded_and_k_above_eligible():
     assert np.all(np.sort(i[:, :3], axis=1) == keep) and np.all(i[:, 3:] == -1)
 
 
-@pytest.mark.parametrize("n", [2000, 50000])
+@pytest.mark.parametrize("n", [2000, 50000, 2_000_000])
 def test_all_equal_corpus_ties(n):
     """Every score ties: the result is ids 0..k-1 (and, with exclusions, the k smallest
-    eligible ids). At n=50000 every item passes the sampled threshold, the candidate lists
-    overflow and the exact rescan runs."""
+    eligible ids). From n=50000 every item passes the sampled threshold and the candidate
+    lists overflow; the rescue's composite threshold (the k-th stored candidate's score and
+    id) admits only the tied rows up to that id, so no list reaches the exact rescan."""
     dev = _dev()
     d, k, b = 64, 37, 3
     x = np.ones((n, d), np.float32)
     corpus = mips.prepare_corpus(torch.from_numpy(x).to(dev), "bf16")
     q = mips.l2_normalize(torch.ones((b, d), device=dev), "bf16")
-    s, i = mips.topk(q, corpus, k)
+    ws = mips.empty_workspace(mips.workspace_size(b, n, d, k, "bf16", "bf16"), dev)
+    s, i = mips.topk(q, corpus, k, workspace=ws)
     torch.cuda.synchronize()
     assert np.all(i.cpu().numpy() == np.arange(k))
     assert torch.all(s == s[0, 0])
+    cnt = _ws_counts(ws)
+    print(f"all equal n={n}: {cnt}", flush=True)
+    assert cnt["rescans"] == 0
+    if n >= 50000:
+        assert cnt["queued"] == b
     excl = np.array([0, 1, 5, 31, 32, 36])
     bm = bitmap_from_ids(excl, n)
     s, i = mips.topk(q, corpus, k, torch.from_numpy(bm.view(np.int32)).to(dev))
@@ -241,13 +260,14 @@ def test_all_equal_corpus_ties(n):
     assert np.all(i.cpu().numpy() == np.array(want))
 
 
-def test_small_workspace_forces_exact_rescan():
+def test_small_workspace_is_still_exact():
     """A workspace with room for one candidate per query and list segment: the lists
-    overflow, the queries are rescued and rescanned exactly, and the result still matches
-    the oracle."""
+    overflow, every query is rescued (and rescanned exactly where the rescue's room of one
+    candidate per segment overflows too), and the result still matches the oracle."""
     n, d, b, k = 30000, 128, 9, 40
     wsb = mips.workspace_size(b, n, d, k, "bf16", "bf16", candidates_per_query=1)
-    run_case(n, d, b, k, "bf16", "bf16", seed=12, workspace_bytes=wsb)
+    st = run_case(n, d, b, k, "bf16", "bf16", seed=12, workspace_bytes=wsb)
+    assert st["queued"] == b
 
 
 def _sampled_blocks(n, k, g_max=8192):
@@ -780,4 +800,45 @@ def test_no_estimate_overflow_falls_back_to_exact_rescan():
     keep = np.arange(100_000, 108_000)
     bm = bitmap_from_ids(np.setdiff1d(np.arange(n), keep), n)
     ws = mips.workspace_size(b, n, d, k, "bf16", "bf16", candidates_per_query=2048)
-    run_case(n, d, b, k, "bf16", "bf16", seed=95, bitmap=bm, workspace_bytes=ws)
+    st = run_case(n, d, b, k, "bf16", "bf16", seed=95, bitmap=bm, workspace_bytes=ws)
+    assert st["queued"] == b and st["rescans"] == b
+
+
+def _cluster_sorted(w):
+    """The workload's raw rows reordered so that ids follow the clusters (an index whose ids
+    are grouped, as in a catalogue sorted by category)."""
+    x = w.corpus()
+    return np.ascontiguousarray(x[np.argsort(w.cluster_of_id(), kind="stable")])
+
+
+@pytest.mark.parametrize("cdt,d,k", [("bf16", 128, 100), ("int8", 64, 500), ("bf16", 64, 1000)])
+def test_cluster_sorted_ids_need_no_rescan(cdt, d, k):
+    """Ids grouped by cluster put a query's candidates in the few corpus slices of its
+    cluster, so the per-slice segments of the main pass overflow. The rescue pass keeps one
+    contiguous list per rescued query, so it holds them, and no list reaches the exact
+    rescan."""
+    n, b = 1_000_000, 32
+    w = _workload(n, d, b, k, cdt, "bf16", 96).replace(clusters=1024)
+    st = run_case(n, d, b, k, cdt, "bf16", seed=96, x=_cluster_sorted(w), qraw=w.queries())
+    assert st["queued"] > 0 and st["rescans"] == 0, st
+
+
+@pytest.mark.parametrize("k", [100, 1000])
+def test_duplicated_top_rows_need_no_rescan(k):
+    """40,000 rows identical to a query's own direction, spread over an index of 1.2M rows:
+    every list of that query overflows its segments with rows tied at the top score. The
+    rescue's composite threshold admits only the tied rows up to the k-th stored id, so the
+    query needs no exact rescan, and its result is the k smallest duplicated ids (ties go to
+    the lower id)."""
+    n, d, b = 1_200_000, 64, 4
+    w = _workload(n, d, b, k, "bf16", "bf16", 97)
+    x, qraw = w.corpus(), w.queries()
+    dup = np.sort(np.random.default_rng(97).choice(n, 40_000, replace=False))
+    x[dup] = qraw[0]
+    st = run_case(n, d, b, k, "bf16", "bf16", seed=97, x=x, qraw=qraw)
+    assert st["queued"] >= 1 and st["rescans"] == 0, st
+    dev = _dev()
+    corpus, q = _gpu_inputs(w, x, qraw, dev)
+    _, i = mips.topk(q, corpus, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(i[0].cpu().numpy(), dup[:k])
