@@ -240,7 +240,7 @@ def main():
                     help="queries in the CPU-baseline sample (default: twice the host "
                          "threads, at most 32, at most the batch)")
     ap.add_argument("--flush-mib", type=int, default=1024,
-                    help="MiB of scratch written before every timed call (0: none)")
+                    help="MiB of scratch read before every timed call (0: none)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="first run a plain device copy of GIB GiB (counter calibration)")
     ap.add_argument("--masks", type=int, default=0, metavar="T",
@@ -272,10 +272,13 @@ def main():
     ws = mips.empty_workspace(wsb, dev)
     scores = torch.empty((w.b, w.k), dtype=torch.float32, device=dev)
     ids = torch.empty((w.b, w.k), dtype=torch.int32, device=dev)
-    # written before every timed call (outside its events) so that no call finds the
-    # corpus in the 256 MB last-level cache
-    flush = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev) \
+    # read before every timed call (outside its events) so that no call finds the corpus in
+    # the 256 MB last-level cache; written once here, so the cache holds no dirty lines whose
+    # write-back would compete with the call's reads
+    flush = torch.ones(args.flush_mib << 18, dtype=torch.float32, device=dev) \
         if args.flush_mib > 0 else None
+    flush_out = torch.empty((), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
 
     def step():
         mips.topk(q, corpus, w.k, excl, workspace=ws, out=(scores, ids))
@@ -293,7 +296,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         if flush is not None:
-            flush.fill_(float(i))
+            torch.sum(flush, dim=0, out=flush_out)
         mips.set_timing_events(pairs[i][0], pairs[i][1])
         calls[i][0].record()
         step()
@@ -306,8 +309,8 @@ def main():
     for a, b in pairs:
         ev.destroy(a)
         ev.destroy(b)
-    log(f"timed {args.steps} steps in {wall:.3f}s (with a {args.flush_mib} MiB cache flush "
-        f"before each); per call: median {np.median(call_ms):.4f} ms, min {min(call_ms):.4f} ms")
+    log(f"timed {args.steps} steps in {wall:.3f}s (with a {args.flush_mib} MiB read before "
+        f"each); per call: median {np.median(call_ms):.4f} ms, min {min(call_ms):.4f} ms")
 
     # back to back with no flush: the rate of a stream of calls on one index (labelled extra)
     torch.cuda.synchronize()
@@ -374,7 +377,7 @@ def main():
                    "exclude_frac": w.exclude_frac, "clusters": w.clusters},
         "queries_per_s": w.b / (ms_per_step / 1e3),
         "timing": {"per_call": "HIP events around each mips_topk call on its stream, after "
-                               f"writing {args.flush_mib} MiB of scratch (untimed); "
+                               f"reading {args.flush_mib} MiB of scratch (untimed); "
                                "value and ms_per_step use the median",
                    "median_ms": ms_per_step, "min_ms": float(min(call_ms)),
                    "wall_ms_per_step_incl_flush": wall / args.steps * 1e3,

@@ -48,10 +48,16 @@ def build_both(w, dev):
     return corpus, q, bm, codes, scale, q_or
 
 
-def run_workload(name, sample, exact_sample=()):
-    """sample: queries checked end to end (each side builds its own index from the raw
-    rows) against the oracle's top-k; exact_sample: queries checked when the GPU searches the
-    oracle's own codes, against the exact scores of its operands (check_operands)."""
+_STATE = {}
+
+
+def workload_state(name, sample, exact_sample):
+    """Builds workload `name` once per test process and runs both GPU searches in the
+    launch configuration the benchmark times: each side builds its own index from the raw
+    rows (GPU prepare, oracle prepare), and the GPU also searches the oracle's own codes.
+    Keeps host copies of what the checks need; frees the device memory."""
+    if name in _STATE:
+        return _STATE[name]
     if not torch.cuda.is_available():
         pytest.skip("needs a GPU")
     dev = torch.device("cuda:0")
@@ -63,8 +69,27 @@ def run_workload(name, sample, exact_sample=()):
     s, i = mips.topk(q, corpus, w.k, excl)
     torch.cuda.synchronize()
     s, i = s.cpu().numpy(), i.cpu().numpy()
-    excluded = set(w.excluded_ids().tolist()) if bm is not None else set()
-    # every query: well-formed and within the unit bound
+    del corpus, q
+    torch.cuda.empty_cache()
+    oc = upload_corpus(codes, scale, w.corpus_dtype, dev)
+    s2, i2 = mips.topk(query_tensor(q_or, w.query_dtype, dev), oc, w.k, excl)
+    torch.cuda.synchronize()
+    s2, i2 = s2.cpu().numpy(), i2.cpu().numpy()
+    del oc, excl
+    torch.cuda.empty_cache()
+    st = dict(w=w, s=s, i=i, s2=s2, i2=i2, bm=bm, codes=codes, scale=scale, q_or=q_or,
+              excluded=set(w.excluded_ids().tolist()) if bm is not None else set(),
+              sel=np.array(sorted(set(sample)), np.int64),
+              xsel=np.array(sorted(set(exact_sample)), np.int64))
+    _STATE.clear()  # one workload's host arrays at a time
+    _STATE[name] = st
+    return st
+
+
+def check_end_to_end(st):
+    """Every query: well-formed and within the unit bound; the sampled queries against the
+    oracle's top-k of its own index (the tolerance rule of check_topk)."""
+    w, s, i, excluded = st["w"], st["s"], st["i"], st["excluded"]
     # relative rounding of a stored unit row: int8 moves each element by at most
     # max|y| / 254, i.e. the row by at most sqrt(D) / 254 (< 2^-4 for D <= 256)
     delta = {"f32": 2 ** -23, "bf16": 2 ** -8, "fp8": 2 ** -4, "int8": 2 ** -4}[w.corpus_dtype]
@@ -75,39 +100,28 @@ def run_workload(name, sample, exact_sample=()):
     if excluded:
         ex = np.array(sorted(excluded))
         assert not np.isin(i, ex).any()
-    sel = np.array(sorted(set(sample)), np.int64)
-    xsel = np.array(sorted(set(exact_sample)), np.int64)
-    # the oracle's top-k of the operands serves the end-to-end check too when the GPU
-    # multiplies the queries as given
-    share = operands_are_inputs(w.query_dtype, w.corpus_dtype) and set(sel) <= set(xsel)
-    xref = None
-    if xsel.size:
-        print(f"workload {name}: oracle on {xsel.size} queries", flush=True)
-        xref = operand_reference(q_or[xsel], w.query_dtype, codes, w.corpus_dtype, w.k,
-                                 row_scale=scale, exclude=bm, threads_=threads())
-    if share:
-        pos = np.searchsorted(xsel, sel)
-        o_s, o_i = xref[0][pos], xref[1][pos]
-    else:
-        print(f"workload {name}: oracle on queries {sel.tolist()}", flush=True)
-        o_s, o_i = ref_topk(q_or[sel], w.query_dtype, codes, w.corpus_dtype, w.k,
-                            row_scale=scale, exclude=bm, threads=threads())
-    stats = check_topk(s[sel], i[sel], o_s, o_i, q_or[sel], w.query_dtype, codes, w.corpus_dtype,
-                       scale, excluded, w.n, TOL[w.corpus_dtype],
+    sel = st["sel"]
+    print(f"workload {w.name}: oracle on queries {sel.tolist()}", flush=True)
+    o_s, o_i = ref_topk(st["q_or"][sel], w.query_dtype, st["codes"], w.corpus_dtype, w.k,
+                        row_scale=st["scale"], exclude=st["bm"], threads=threads())
+    stats = check_topk(s[sel], i[sel], o_s, o_i, st["q_or"][sel], w.query_dtype, st["codes"],
+                       w.corpus_dtype, st["scale"], excluded, w.n, TOL[w.corpus_dtype],
                        floor=floor_for(w.corpus_dtype, w.query_dtype))
-    print(f"workload {name}: end to end: {stats}", flush=True)
-    if not xsel.size:
-        return
-    # the same search over the oracle's own codes, in the same launch configuration
-    del corpus, q
-    torch.cuda.empty_cache()
-    oc = upload_corpus(codes, scale, w.corpus_dtype, dev)
-    s2, i2 = mips.topk(query_tensor(q_or, w.query_dtype, dev), oc, w.k, excl)
-    torch.cuda.synchronize()
-    s2, i2 = s2.cpu().numpy(), i2.cpu().numpy()
-    stats = check_operands(s2[xsel], i2[xsel], q_or[xsel], w.query_dtype, codes, w.corpus_dtype,
-                           scale, excluded, w.n, exclude_bitmap=bm, ref=xref)
-    print(f"workload {name}: oracle codes, {xsel.size} queries: {stats}", flush=True)
+    print(f"workload {w.name}: end to end: {stats}", flush=True)
+
+
+def check_oracle_codes(st, part=0, parts=1):
+    """The search of the oracle's own codes against the exact scores of its operands
+    (check_operands), on every parts-th of the exact sample from `part`."""
+    w = st["w"]
+    xsel = st["xsel"][part::parts]
+    print(f"workload {w.name}: oracle on {xsel.size} queries", flush=True)
+    ref = operand_reference(st["q_or"][xsel], w.query_dtype, st["codes"], w.corpus_dtype, w.k,
+                            row_scale=st["scale"], exclude=st["bm"], threads_=threads())
+    stats = check_operands(st["s2"][xsel], st["i2"][xsel], st["q_or"][xsel], w.query_dtype,
+                           st["codes"], w.corpus_dtype, st["scale"], st["excluded"], w.n,
+                           exclude_bitmap=st["bm"], ref=ref)
+    print(f"workload {w.name}: oracle codes, {xsel.size} queries: {stats}", flush=True)
 
 
 def _spread(b, count, seed):
@@ -116,33 +130,74 @@ def _spread(b, count, seed):
     return sorted({0, b - 1, *(1 + rng.choice(b - 2, count - 2, replace=False)).tolist()})
 
 
+# Each test stays well under three minutes (the oracle on at most about 64 queries of
+# 10^7 rows, or 16 of 10^8), so a test run reports progress at least that often.
+SPECS = {
+    "tiny_f32_n400_d16": (range(128), range(128)),
+    "bf16_n1m_d128_b16": (range(16), range(16)),
+    "bf16_n10m_d128_b256_excl5": ([0, 1, 31, 32, 100, 128, 200, 255], range(256)),
+    "fp8_n10m_d256_b4096": ([0, 1, 511, 512, 2047, 3000, 4094, 4095], _spread(4096, 64, 5)),
+    "int8_n10m_d128_b256_excl5": ([0, 1, 63, 64, 127, 200, 254, 255], range(256)),
+    "bf16_n100m_d64_b1024": ([0, 1023], _spread(1024, 64, 4)),
+}
+PARTS = {"bf16_n10m_d128_b256_excl5": 4, "int8_n10m_d128_b256_excl5": 4,
+         "bf16_n100m_d64_b1024": 4}
+
+
+def _state(name):
+    return workload_state(name, *SPECS[name])
+
+
 def test_tiny_f32():
-    run_workload("tiny_f32_n400_d16", range(128), range(128))
+    st = _state("tiny_f32_n400_d16")
+    check_end_to_end(st)
+    check_oracle_codes(st)
 
 
 def test_bf16_n1m():
-    run_workload("bf16_n1m_d128_b16", range(16), range(16))
+    st = _state("bf16_n1m_d128_b16")
+    check_end_to_end(st)
+    check_oracle_codes(st)
 
 
 @pytest.mark.timeout(900)
-def test_bf16_n10m_headline():
-    run_workload("bf16_n10m_d128_b256_excl5", [0, 1, 31, 32, 100, 128, 200, 255], range(256))
+def test_bf16_n10m_headline_end_to_end():
+    check_end_to_end(_state("bf16_n10m_d128_b256_excl5"))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("part", range(4))
+def test_bf16_n10m_headline_oracle_codes(part):
+    check_oracle_codes(_state("bf16_n10m_d128_b256_excl5"), part, 4)
 
 
 @pytest.mark.timeout(900)
 def test_fp8_n10m():
-    run_workload("fp8_n10m_d256_b4096", [0, 1, 511, 512, 2047, 3000, 4094, 4095],
-                 _spread(4096, 64, 5))
+    st = _state("fp8_n10m_d256_b4096")
+    check_end_to_end(st)
+    check_oracle_codes(st)
 
 
 @pytest.mark.timeout(1200)
-def test_int8_n10m():
-    run_workload("int8_n10m_d128_b256_excl5", [0, 1, 63, 64, 127, 200, 254, 255], range(256))
+def test_int8_n10m_end_to_end():
+    check_end_to_end(_state("int8_n10m_d128_b256_excl5"))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("part", range(4))
+def test_int8_n10m_oracle_codes(part):
+    check_oracle_codes(_state("int8_n10m_d128_b256_excl5"), part, 4)
 
 
 @pytest.mark.timeout(1500)
-def test_bf16_n100m():
-    run_workload("bf16_n100m_d64_b1024", [0, 1023], _spread(1024, 64, 4))
+def test_bf16_n100m_end_to_end():
+    check_end_to_end(_state("bf16_n100m_d64_b1024"))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("part", range(4))
+def test_bf16_n100m_oracle_codes(part):
+    check_oracle_codes(_state("bf16_n100m_d64_b1024"), part, 4)
 
 
 @pytest.mark.timeout(1200)
