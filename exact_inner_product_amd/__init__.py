@@ -25,7 +25,8 @@ B_MAX = 1 << 23  # result lists per call (queries, or queries x masks)
 
 EXPORTS = (
     "mips_corpus_bytes", "mips_scale_count", "mips_l2_normalize", "mips_prepare_corpus",
-    "mips_topk_workspace_size", "mips_topk_workspace_size_for", "mips_topk", "mips_topk_ranges",
+    "mips_topk_workspace_size", "mips_topk_workspace_size_for", "mips_topk", "mips_topk_noalloc",
+    "mips_topk_ranges",
     "mips_topk_masks_workspace_size", "mips_topk_masks",
     "mips_merge_topk", "mips_merge_interests", "mips_type_bitmap", "mips_set_timing_events", "mips_status_string", "mips_last_hip_error",
 )
@@ -70,6 +71,7 @@ def lib() -> C.CDLL:
         L.mips_topk_workspace_size_for.argtypes = [i32, i64, i32, i32, i32, i32, i64]
         L.mips_topk_workspace_size_for.restype = sz
         L.mips_topk.argtypes = [p, i32, i32, p, p, i32, i64, i32, p, i64, i32, p, p, p, sz, p]
+        L.mips_topk_noalloc.argtypes = [p, i32, i32, p, p, i32, i64, i32, p, i64, i32, p, p, p]
         L.mips_topk_ranges.argtypes = [p, i32, i32, p, p, i32, i64, i32, p, i64, p, i32, i32, p, p, p,
                                        sz, p]
         L.mips_topk_masks_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32, i64]
@@ -83,7 +85,8 @@ def lib() -> C.CDLL:
         L.mips_status_string.argtypes = [C.c_int]
         L.mips_status_string.restype = C.c_char_p
         L.mips_last_hip_error.argtypes = []
-        for f in (L.mips_l2_normalize, L.mips_prepare_corpus, L.mips_topk, L.mips_topk_ranges,
+        for f in (L.mips_l2_normalize, L.mips_prepare_corpus, L.mips_topk, L.mips_topk_noalloc,
+                  L.mips_topk_ranges,
                   L.mips_topk_masks,
                   L.mips_merge_topk, L.mips_merge_interests, L.mips_type_bitmap,
                   L.mips_set_timing_events, L.mips_last_hip_error):
@@ -260,6 +263,33 @@ def topk(queries: torch.Tensor, corpus: Corpus, k: int, exclude: Optional[torch.
                            _ptr(ids), _ptr(workspace), workspace.numel(),
                            _stream(queries.device)), "mips_topk")
     return scores, ids
+
+
+def topk_noalloc(queries: torch.Tensor, corpus: Corpus, k: int,
+                 exclude: Optional[torch.Tensor] = None,
+                 out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                 model_version: Optional[str] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """As topk, through mips_topk_noalloc: the library's own device scratch instead of a
+    workspace (nothing is allocated when `out` is given). Calls that overlap on one device
+    race; order them on one stream."""
+    check_version(corpus, model_version)
+    assert queries.is_cuda and queries.dim() == 2 and queries.shape[1] == corpus.d
+    queries = queries.contiguous()
+    b = queries.shape[0]
+    if out is None:
+        scores = torch.empty((b, k), dtype=torch.float32, device=queries.device)
+        ids = torch.empty((b, k), dtype=torch.int32, device=queries.device)
+    else:
+        scores, ids = out
+    exclude, row_words = _exclude_arg(exclude, corpus, b)
+    _check(lib().mips_topk_noalloc(_ptr(queries), _qcode(queries), b, _ptr(corpus.packed),
+                                   _ptr(corpus.row_scale), corpus.code, corpus.n, corpus.d,
+                                   _ptr(exclude), row_words, k, _ptr(scores), _ptr(ids),
+                                   _stream(queries.device)), "mips_topk_noalloc")
+    return scores, ids
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 def topk_ranges(queries: torch.Tensor, corpus: Corpus, ranges, k: int,

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmips.so")
-SOURCES = ["api.hip", "normalize.hip", "topk.hip", "merge.hip"]
+SOURCES = ["api.hip", "normalize.hip", "topk.hip", "merge.hip", "noalloc.hip"]
 
 # (dtype macro, width) pairs of the score pass; must match corpus_d_supported in host.h
 SCORE_UNITS = ([("MIPS_F32", d) for d in (16, 32, 64, 128)] +

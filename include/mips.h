@@ -12,12 +12,14 @@
  * Entry points: mips_l2_normalize and mips_prepare_corpus (normalisation, index build);
  * mips_topk (one result set per query), mips_topk_ranges (one per id range) and
  * mips_topk_masks (one per exclusion mask, from one pass over the index), with their
- * workspace sizes; mips_merge_topk and mips_merge_interests (merges of sorted result lists);
+ * workspace sizes; mips_topk_noalloc (mips_topk with library-held scratch);
+ * mips_merge_topk and mips_merge_interests (merges of sorted result lists);
  * mips_type_bitmap (per-type exclusion bitmaps); status strings and a timing hook.
  *
  * Conventions shared by every entry point:
- *  - All buffers are caller-owned. Pointers marked "device" are HIP device memory;
- *    the library never allocates, frees or synchronises. Work is enqueued on
+ *  - All buffers are caller-owned (except the static scratch array of
+ *    mips_topk_noalloc). Pointers marked "device" are HIP device memory; the library
+ *    never allocates, frees or synchronises. Work is enqueued on
  *    `stream` (a hipStream_t; NULL is the default stream) and the call returns after
  *    enqueueing. Results are visible once the stream has reached that point.
  *  - Arguments are validated on the host before anything is enqueued. On any error
@@ -201,6 +203,26 @@ MIPS_API int mips_topk(const void *queries, int32_t query_dtype, int32_t b, cons
               const uint32_t *exclude, int64_t exclude_row_words, int32_t k,
               float *out_scores, int32_t *out_ids, void *workspace, size_t workspace_bytes,
               void *stream);
+
+/*
+ * mips_topk_noalloc -- mips_topk for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * search, arguments, ordering, padding and errors, with no workspace argument. Its scratch
+ * is a device array held by the library, MIPS_NOALLOC_SCRATCH_BYTES per device, from the
+ * first call on a device until the process ends; the call allocates and frees nothing.
+ * Every call on one device shares that device's array: calls that overlap on a device (on
+ * different streams, or from several threads without ordering) race and give undefined
+ * results. The array keeps the last call's contents; a call reads nothing it did not write.
+ * Errors: as mips_topk; WORKSPACE when mips_topk_workspace_size for the same arguments
+ * exceeds MIPS_NOALLOC_SCRATCH_BYTES (e.g. b = 256, n = 10^7, d = 128, k = 500 fits, about
+ * 76 MB; b = 1024, n = 10^8 does not); HIP when the array's address cannot be had.
+ */
+#define MIPS_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+MIPS_API int mips_topk_noalloc(const void *queries, int32_t query_dtype, int32_t b,
+                               const void *corpus, const float *row_scale, int32_t corpus_dtype,
+                               int64_t n, int32_t d, const uint32_t *exclude,
+                               int64_t exclude_row_words, int32_t k, float *out_scores,
+                               int32_t *out_ids, void *stream);
 
 /*
  * mips_topk_ranges -- mips_topk restricted to id ranges, one result set per range: for

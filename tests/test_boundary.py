@@ -297,3 +297,20 @@ def test_lattice_rows_agree_between_numpy_and_torch():
     first = lattice_rows(0, 1, 4)[0]
     want = [((12345 + j * 40503) >> 7) % 4093 - 2046 for j in range(4)]
     assert first.tolist() == [w / 256.0 for w in want]
+
+
+def test_noalloc_validates_before_any_hip_call(L):
+    vp = lambda x: None if x is None else C.c_void_p(x)
+
+    def call(q=0x1000, b=4, n=1000, d=128, k=10, out_s=0x3000, out_i=0x4000, excl=None, rw=0):
+        return L.mips_topk_noalloc(vp(q), BF16, b, vp(0x2000), None, BF16, n, d, vp(excl), rw, k,
+                                   vp(out_s), vp(out_i), None)
+    assert call(q=None) == INVALID
+    assert call(out_i=None) == INVALID
+    assert call(k=0) == INVALID and call(k=1025) == UNSUPPORTED
+    assert call(d=48) == UNSUPPORTED
+    assert call(q=0x1002) == INVALID
+    assert call(excl=None, rw=40) == INVALID
+    # beyond the library's scratch: the default workspace of these sizes does not fit
+    assert L.mips_topk_workspace_size(1024, 100_000_000, 64, 1000, BF16, BF16) > 128 << 20
+    assert call(b=1024, n=100_000_000, d=64, k=1000) == WORKSPACE
