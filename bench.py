@@ -124,7 +124,11 @@ def build_gpu_inputs(w, dev, torch, mips):
     corpus = mips.empty_corpus(w.n, w.d, w.corpus_dtype, dev)
     t_prep = 0.0
     nbytes_in = 0
+    nchunks = 0
     for r0, blk in w.corpus_chunks():
+        nchunks += 1
+        if nchunks % 16 == 0:
+            log(f"index build: {r0 + blk.shape[0]} of {w.n} rows")
         x = torch.from_numpy(blk).to(dev)
         torch.cuda.synchronize()
         t0 = time.perf_counter()

@@ -616,7 +616,12 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
         load_b(bq1, 0);
         static_for<NQF>([&](auto qfc) __attribute__((always_inline)) {
           constexpr int qf = decltype(qfc)::value;
+          // issue priority while this wave issues its MFMAs, none during its epilogue: the
+          // two waves of a SIMD then take turns on the matrix pipe instead of sharing it and
+          // reaching their epilogues together
+          __builtin_amdgcn_s_setprio(3);
           mfmas(acc1, a, sa, bq1, sbq(qf), qf + 1 < NQF ? qf + 1 : -1);
+          __builtin_amdgcn_s_setprio(0);
           epi_main(acc1, sc, xwv, j0, qf);
         });
         return;
@@ -628,8 +633,11 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
       static_for<NQF>([&](auto qfc) __attribute__((always_inline)) {
         constexpr int qf = decltype(qfc)::value;
         constexpr int cur = qf & 1;
-        if constexpr (qf + 1 < NQF)
+        if constexpr (qf + 1 < NQF) {
+          if constexpr (MODE == MODE_MAIN) __builtin_amdgcn_s_setprio(3);  // as above
           mfmas(acc[cur ^ 1], a, sa, bq, sbq(qf + 1), qf + 2 < NQF ? qf + 2 : -1);
+          if constexpr (MODE == MODE_MAIN) __builtin_amdgcn_s_setprio(0);
+        }
         if constexpr (MODE == MODE_MAIN) {
           epi_main(acc[cur], sc, xwv, j0, qf);
         } else {
