@@ -317,8 +317,20 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
 
     // A stage's loads are unconditional: blocks past the end of the pass read the last
     // block again and are masked out, so the compiler's wait counts stay exact. Lane r < RM
-    // also loads the exclusion word of block r, with the rows past n set.
-    auto load_stage = [&](u32x4_t (&a)[RM][NCH], int (&sa)[RM], float (&sc)[RM][SCN], uint32_t& xwv,
+    // (multi-mask: lane NT r + t, for mask t) also loads the exclusion word of block r.
+    // Loaded values are kept as loaded until the stage is computed: a value derived from a
+    // load in flight (the exclusion word with the padding rows set, the exponent of an fp8
+    // row scale) is a use of that load, and the compiler would place it before the loop's
+    // back edge with a wait for the load and so for every load issued before it, draining
+    // the stages in flight once per iteration.
+    auto word_block = [&](int64_t j0, bool& live) __attribute__((always_inline)) {
+      const int rl = NT > 0 ? lane / NTS : lane;
+      const int r = rl < RM ? rl : RM - 1;
+      live = j0 + r < A.nfrag;
+      const int64_t j = live ? j0 + r : A.nfrag - 1;
+      return A.blk0 + ((MODE == MODE_SAMPLE) ? (int64_t)(((uint64_t)j * A.sample_step) >> 32) : j);
+    };
+    auto load_stage = [&](u32x4_t (&a)[RM][NCH], int (&sa)[RM], float (&sc)[RM][SCN], uint32_t& xraw,
                           int64_t j0) __attribute__((always_inline)) {
 #pragma unroll
       for (int r = 0; r < RM; ++r) {
@@ -331,9 +343,8 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
         for (int c = 0; c < NCH; ++c)
           a[r][c] = __builtin_bit_cast(
               u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, c * kChunkBytes, 0));
-        sa[r] = 127;
-        if (CT == MIPS_FP8_E4M3)
-          sa[r] = (int)((__float_as_uint(A.row_scale[fr * kFrag + (lane & 31)]) >> 23) & 0xFFu);
+        sa[r] = 127 << 23;  // the bits of a row scale of 1 (fp8: the row's own scale)
+        if (CT == MIPS_FP8_E4M3) sa[r] = (int)__float_as_uint(A.row_scale[fr * kFrag + (lane & 31)]);
         if constexpr (CT == MIPS_INT8) {
           // rows 8q + 4 (lane >> 5) + (0..3) for q = 0..3: accumulator registers 4q..4q+3
           const __amdgpu_buffer_rsrc_t rsc = block_rsrc(A.row_scale + fr * kFrag, kFrag * 4);
@@ -346,33 +357,39 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
           }
         }
       }
-      // lane r (multi-mask: lane NT r + t, mask t) holds the word of block r
-      const int rl = NT > 0 ? lane / NTS : lane;
-      const int r = rl < RM ? rl : RM - 1;
-      const bool live = j0 + r < A.nfrag;
-      const int64_t j = live ? j0 + r : A.nfrag - 1;
-      const int64_t fr = A.blk0 + ((MODE == MODE_SAMPLE) ? (int64_t)(((uint64_t)j * A.sample_step) >> 32) : j);
-      // branch-free: without a bitmap, any readable word masked to zero (a conditional
-      // load would make the compiler's wait counts conservative at the join); a mask
-      // past the pass's count excludes every row
+      // branch-free: without a bitmap, any readable word (masked to zero by stage_word); a
+      // conditional load would make the compiler's wait counts conservative at the join
+      bool live;
+      const int64_t fr = word_block(j0, live);
       const uint32_t* wp;
-      uint32_t keep, force = 0u;
       if constexpr (NT > 0) {
         const int mt = lane % NTS;
-        const bool use = mt < A.nmask;
-        wp = use ? A.masks + (int64_t)mt * A.mask_words + fr : (const uint32_t*)A.corpus;
+        wp = mt < A.nmask ? A.masks + (int64_t)mt * A.mask_words + fr : (const uint32_t*)A.corpus;
+      } else {
+        wp = A.exclude ? A.exclude + fr : (const uint32_t*)A.corpus;
+      }
+      xraw = *wp;
+    };
+    // The exclusion word of a stage's block (per lane, as loaded by load_stage) with the rows
+    // past n, the rows before lo and every row of a block past the pass set; a mask past
+    // the pass's count excludes every row.
+    auto stage_word = [&](uint32_t xraw, int64_t j0) __attribute__((always_inline)) {
+      bool live;
+      const int64_t fr = word_block(j0, live);
+      uint32_t keep, force = 0u;
+      if constexpr (NT > 0) {
+        const bool use = lane % NTS < A.nmask;
         keep = use ? ~0u : 0u;
         force = use ? 0u : ~0u;
       } else {
-        wp = A.exclude ? A.exclude + fr : (const uint32_t*)A.corpus;
         keep = A.exclude ? ~0u : 0u;
       }
-      uint32_t w = (*wp & keep) | force;
+      uint32_t w = (xraw & keep) | force;
       const int64_t rows = A.n - fr * kFrag;
       if (rows < kFrag) w |= ~0u << rows;
       const int64_t below = A.lo - fr * kFrag;  // rows before the start of the id range
       if (below > 0) w |= below >= kFrag ? ~0u : (1u << below) - 1u;
-      xwv = live ? w : ~0u;
+      return live ? w : ~0u;
     };
 
     auto load_b = [&](u32x4_t (&bq)[NCH], int qf) __attribute__((always_inline)) {
@@ -604,9 +621,13 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
     // One stage against every query fragment, software-pipelined: the MFMAs of fragment
     // qf+1 are issued before the epilogue of fragment qf, so the epilogue (and its rare
     // path) runs while the matrix pipe works on the next fragment.
-    auto compute_stage = [&](const u32x4_t (&a)[RM][NCH], const int (&sa)[RM],
-                             const float (&sc)[RM][SCN], uint32_t xwv,
+    auto compute_stage = [&](const u32x4_t (&a)[RM][NCH], const int (&sa_raw)[RM],
+                             const float (&sc)[RM][SCN], uint32_t xraw,
                              int64_t j0) __attribute__((always_inline)) {
+      const uint32_t xwv = stage_word(xraw, j0);
+      int sa[RM];  // the MFMA's block scale operand: the biased exponent of the row scale
+#pragma unroll
+      for (int g = 0; g < RM; ++g) sa[g] = (int)(((uint32_t)sa_raw[g] >> 23) & 0xFFu);
       if constexpr (SINGLE) {
         // one accumulator set: fragment qf's MFMAs, then its epilogue (the other wave on
         // the SIMD keeps the matrix pipe busy meanwhile); the operand of fragment qf+1
