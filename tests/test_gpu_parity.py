@@ -272,9 +272,10 @@ def test_small_workspace_is_still_exact():
 
 def _sampled_blocks(n, k, g_max=8192):
     """Blocks the sample pass reads: an even integer stride over the 32-row blocks, G of them
-    (at most 8192 and a 16th of the blocks, at least 4 k)."""
+    (a 16th of the blocks but no more than ceil(6 n32 / k), enough for about 6 of the k best
+    items; at least 4 k, at most 8192)."""
     n32 = (n + 31) // 32
-    g = min(n32, g_max, max(n32 // 16, 4 * k))
+    g = min(n32, g_max, max(min(n32 // 16, (6 * n32 + k - 1) // k), 4 * k))
     step = (n32 << 32) // g
     return np.array([(j * step) >> 32 for j in range(g)], np.int64)
 
