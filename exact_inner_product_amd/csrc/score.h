@@ -501,11 +501,13 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
       }
     };
 
+    // (T and sq are the fragment's threshold and int8 query scale, read from LDS by the
+    // caller; with two accumulator sets it reads them ahead of the next fragment's MFMAs,
+    // since read after that fragment's operand reads were issued, their wait would wait
+    // for those reads as well)
     auto epi_main = [&](const f32x16_t (&acc)[RM], const float (&sc)[RM][SCN], uint32_t xwv,
-                        int64_t j0, int qf) __attribute__((always_inline)) {
-      const float T = Tq(qf);
+                        int64_t j0, int qf, float T, float sq) __attribute__((always_inline)) {
       const float Tg = gate(T);
-      const float sq = qscale(qf);
       float m[RM];
       bool any = false;
 #pragma unroll
@@ -643,7 +645,9 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
           __builtin_amdgcn_s_setprio(3);
           mfmas(acc1, a, sa, bq1, sbq(qf), qf + 1 < NQF ? qf + 1 : -1);
           __builtin_amdgcn_s_setprio(0);
-          epi_main(acc1, sc, xwv, j0, qf);
+          // (the threshold is read after the MFMAs here: this path has no register to spare
+          // for it across the chain, and the other wave covers the wait)
+          epi_main(acc1, sc, xwv, j0, qf, Tq(qf), qscale(qf));
         });
         return;
       }
@@ -654,13 +658,18 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
       static_for<NQF>([&](auto qfc) __attribute__((always_inline)) {
         constexpr int qf = decltype(qfc)::value;
         constexpr int cur = qf & 1;
+        float T = 0.0f, sq = 1.0f;
+        if constexpr (MODE == MODE_MAIN) {
+          T = Tq(qf);
+          sq = qscale(qf);
+        }
         if constexpr (qf + 1 < NQF) {
           if constexpr (MODE == MODE_MAIN) __builtin_amdgcn_s_setprio(3);  // as above
           mfmas(acc[cur ^ 1], a, sa, bq, sbq(qf + 1), qf + 2 < NQF ? qf + 2 : -1);
           if constexpr (MODE == MODE_MAIN) __builtin_amdgcn_s_setprio(0);
         }
         if constexpr (MODE == MODE_MAIN) {
-          epi_main(acc[cur], sc, xwv, j0, qf);
+          epi_main(acc[cur], sc, xwv, j0, qf, T, sq);
         } else {
           epi_aux(acc[cur], sc, xwv, j0, qf);
           // the auxiliary epilogues have no branch that would bound the scheduler's region;
