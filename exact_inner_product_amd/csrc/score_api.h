@@ -60,8 +60,9 @@ __host__ __device__ constexpr int stage_frags(int ct, int d) {
 // in a two-stage ring (the same stage bytes in flight per SIMD) with one accumulator set
 // per wave, which fits the 256 registers; the sample and dense passes keep one block.
 __host__ __device__ constexpr bool main_doubles(int ct, int d) {
-  // (the fp8 MFMA's operand packing needs more registers than this estimate allows for)
-  return (ct == MIPS_BF16 || ct == MIPS_INT8) && score_wps(ct, d) == 2 && stage_frags(ct, d) == 1 &&
+  // (f32 keeps its 3-stage ring; fp8 at D=256 reaches the 256 registers with one 4-byte
+  // per-lane value spilled, a constant that only the slow path reloads)
+  return ct != MIPS_F32 && score_wps(ct, d) == 2 && stage_frags(ct, d) == 1 &&
          2 * 2 * chunks_per_block(ct, d) * 4 + (ct == MIPS_INT8 ? 2 * 2 * 16 : 0) + 2 * 16 +
                  chunks_per_block(ct, d) * 4 + 60 <= 256;
 }
