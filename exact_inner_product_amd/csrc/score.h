@@ -440,19 +440,27 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
     // is max_i((a_i * s_i) * sq), the products in the other order: each order is within a
     // factor (1 + 2^-24)^2 of the exact a_i sq s_i, so a score of the filter's order that
     // reaches T implies this bound reaches gate(T) = T - |T| 2^-21.
+    // The maximum of accumulators starts from kMaxSeed: the compiler then builds the chain
+    // from v_max3 alone (raw MFMA results as the first operands of a plain v_max would each
+    // take a quieting v_max first). The seed can only add false positives, which the slow
+    // path resolves: max(seed, values) >= T exactly when some value is, unless T <= seed.
+    constexpr float kMaxSeed = -4.0f;
+    auto fastmax_into = [&](float x, const f32x16_t& acc, const float (&sc)[SCN]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        x = fmaxf(x, CT == MIPS_INT8 ? (float)__float_as_int(acc[i]) * sc[i] : acc[i]);
+      return x;
+    };
     auto fastmax = [&](const f32x16_t& acc, const float (&sc)[SCN], float sq) __attribute__((always_inline)) {
-      float x;
       if constexpr (CT == MIPS_INT8) {
-        x = (float)__float_as_int(acc[0]) * sc[0];
+        // products are canonical already: the chain starts from the first
+        float x = (float)__float_as_int(acc[0]) * sc[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) x = fmaxf(x, (float)__float_as_int(acc[i]) * sc[i]);
-        x = x * sq;
+        return x * sq;
       } else {
-        x = acc[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) x = fmaxf(x, acc[i]);
+        return fastmax_into(kMaxSeed, acc, sc);
       }
-      return x;
     };
     auto gate = [&](float T) __attribute__((always_inline)) {
       return CT == MIPS_INT8 ? fmaf(-fabsf(T), 0x1p-21f, T) : T;  // (NaN for T = +inf: no pass)
@@ -508,16 +516,35 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
     auto epi_main = [&](const f32x16_t (&acc)[RM], const float (&sc)[RM][SCN], uint32_t xwv,
                         int64_t j0, int qf, float T, float sq) __attribute__((always_inline)) {
       const float Tg = gate(T);
+      // one maximum over the stage's RM blocks and one compare (a single-mask pass); the
+      // slow path takes each block's own maximum again
+      bool any;
       float m[RM];
-      bool any = false;
+      if constexpr (NT == 0) {
+        float x;
+        if constexpr (CT == MIPS_INT8) {
+          x = fastmax(acc[0], sc[0], 1.0f);
 #pragma unroll
-      for (int g = 0; g < RM; ++g) {
-        m[g] = fastmax(acc[g], sc[g], sq);
-        any = any || (m[g] >= Tg);
+          for (int g = 1; g < RM; ++g) x = fastmax_into(x, acc[g], sc[g]);
+          x = x * sq;
+        } else {
+          x = kMaxSeed;
+#pragma unroll
+          for (int g = 0; g < RM; ++g) x = fastmax_into(x, acc[g], sc[g]);
+        }
+        any = x >= Tg;
+      } else {
+        any = false;
+#pragma unroll
+        for (int g = 0; g < RM; ++g) {
+          m[g] = fastmax(acc[g], sc[g], sq);
+          any = any || (m[g] >= Tg);
+        }
       }
       if (__builtin_expect(__ballot(any) != 0ull, 0)) {
 #pragma unroll
         for (int g = 0; g < RM; ++g) {
+          if constexpr (NT == 0) m[g] = fastmax(acc[g], sc[g], sq);
           if (__ballot(m[g] >= Tg) == 0ull) continue;
           const uint32_t idb = (uint32_t)((A.blk0 + j0 + g) * kFrag);
           float y[16];
