@@ -65,3 +65,54 @@ def test_search_of_oracle_codes(cdt, qdt, d, n, b, k, excl):
     stats = check_operands(s.cpu().numpy(), i.cpu().numpy(), q_codes, qdt, codes, cdt, scale,
                            excluded, n, exclude_bitmap=bm)
     print(f"oracle codes: {stats}", flush=True)
+
+
+def _int8_exact(codes, scale, q_codes, qdt, k, dev, tag):
+    n = codes.shape[0]
+    print(f"int8 {tag}: n={n} d={codes.shape[1]} b={q_codes.shape[0]} k={k}", flush=True)
+    corpus = upload_corpus(codes, scale, "int8", dev)
+    s, i = mips.topk(query_tensor(q_codes, qdt, dev), corpus, k)
+    torch.cuda.synchronize()
+    stats = check_operands(s.cpu().numpy(), i.cpu().numpy(), q_codes, qdt, codes, "int8", scale,
+                           set(), n)
+    print(f"int8 {tag}: {stats}", flush=True)
+    return s.cpu().numpy()
+
+
+def test_int8_scales_far_from_a_unit_row():
+    """Row scales that no normalised row has (up to 40 times its largest, and zero) on a
+    sampled int8 search: scores far above 1 and exact zeros must still come out bitwise equal
+    to the oracle's quantised branch."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    dev = torch.device("cuda:0")
+    n, d, b, k = 120_000, 128, 19, 60
+    w = Workload("case", "clustered", n=n, d=d, b=b, k=k, corpus_dtype="int8", query_dtype="bf16",
+                 clusters=3000, seed=4242)
+    codes, scale = oracle.prepare(w.corpus(), "int8")
+    q_codes, _ = oracle.prepare(w.queries(), "bf16")
+    rng = np.random.default_rng(7)
+    scale = scale.copy()
+    big = rng.choice(n, n // 10, replace=False)
+    scale[big] = (scale[big] * rng.choice([2.0, 5.0, 40.0], big.size)).astype(np.float32)
+    scale[32 * 1000:32 * 1001] = np.float32(0.5)        # one whole block far out of range
+    scale[rng.choice(n, 200, replace=False)] = np.float32(0.0)
+    _int8_exact(codes, scale, q_codes, "bf16", k, dev, "wide scales")
+
+
+def test_int8_negative_thresholds():
+    """Queries opposite to every row: every score and the K-th threshold are negative (the
+    fast path's bound then lies on the other side of the products), results still exact."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    dev = torch.device("cuda:0")
+    n, d, b, k = 60_000, 64, 7, 100
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((n, d)) * 0.1).astype(np.float32)
+    x[:, 0] += 1.0
+    qraw = (rng.standard_normal((b, d)) * 0.1).astype(np.float32)
+    qraw[:, 0] -= 1.0
+    codes, scale = oracle.prepare(x, "int8")
+    q_codes, _ = oracle.prepare(qraw, "bf16")
+    s = _int8_exact(codes, scale, q_codes, "bf16", k, dev, "negative scores")
+    assert (s < 0).all()
