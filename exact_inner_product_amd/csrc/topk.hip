@@ -43,8 +43,11 @@ namespace mips {
 // ------------------------------------------------------------------ query prep
 // Queries -> MFMA operand tile (the packed layout of the corpus, 32 queries per block).
 // One workgroup of 64 threads per (32-query block, 1 KiB chunk); thread s writes slot s.
-// For an fp8 corpus each query row is quantised with its own power-of-two scale (the
-// corpus rule), recomputed by every thread that needs it. Clears the per-query flags.
+// The wave first copies the block's 32 query rows into LDS with coalesced 4-byte loads,
+// all in flight at once; every value it needs, and each row's max |q|, then come from LDS.
+// For an fp8 or int8 corpus each query row is quantised with its own scale (the corpus
+// rule): lanes s and s + 32 each take the max over half the row's dimensions and combine
+// them. Clears the per-query flags.
 template <int CT, int QT, int D>
 __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict__ queries, int b,
                                                           uint8_t* __restrict__ qtile,
@@ -52,26 +55,36 @@ __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict
                                                           uint32_t* __restrict__ ovf, int nflags,
                                                           uint32_t* __restrict__ nfail) {
   constexpr int NCH = chunks_per_block(CT, D);
+  constexpr int RW = D * (QT == MIPS_F32 ? 4 : 2) / 4;  // 4-byte words per query row
+  constexpr int RWP = RW + 1;  // LDS row stride: odd, so the 32 rows of a column lie in 32 banks
+  __shared__ uint32_t rows[kFrag * RWP];
   const int lane = threadIdx.x;
   const int qb = blockIdx.x / NCH, c = blockIdx.x % NCH;
   const int q = qb * kFrag + (lane & 31);
-  const bool live = q < b;
+  const int nrows = min(kFrag, b - qb * kFrag);
+  const uint32_t* src = (const uint32_t*)queries + (int64_t)qb * kFrag * RW;
+#pragma unroll 32
+  for (int i = lane; i < kFrag * RW; i += 64) rows[(i / RW) * RWP + i % RW] = i < nrows * RW ? src[i] : 0u;
+  __syncthreads();
   auto val = [&](int dim) -> float {
-    if (!live) return 0.0f;
-    if (QT == MIPS_F32) return ((const float*)queries)[(int64_t)q * D + dim];
-    return bf16_to_f32(((const uint16_t*)queries)[(int64_t)q * D + dim]);
+    const uint32_t* r = rows + (lane & 31) * RWP;
+    if (QT == MIPS_F32) return __uint_as_float(r[dim]);
+    return bf16_to_f32((uint16_t)(r[dim >> 1] >> (16 * (dim & 1))));
   };
   float sinv = 1.0f, sq = 1.0f;
+  float m = 0.0f;  // max |q| of this lane's row (fp8 and int8): half each, then combined
+  if (CT == MIPS_FP8_E4M3 || CT == MIPS_INT8) {
+    const int h = lane >> 5;
+#pragma unroll 8
+    for (int j = h * (D / 2); j < (h + 1) * (D / 2); ++j) m = fmaxf(m, fabsf(val(j)));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+  }
   if (CT == MIPS_FP8_E4M3) {
-    float m = 0.0f;
-    for (int j = 0; j < D; ++j) m = fmaxf(m, fabsf(val(j)));
     int t = e4m3_scale_exp(m);
     t = t < -126 ? -126 : (t > 127 ? 127 : t);
     sinv = exp2_int(-t);
     if (c == 0 && lane < 32) qexp[q] = t + 127;
   } else if (CT == MIPS_INT8) {
-    float m = 0.0f;
-    for (int j = 0; j < D; ++j) m = fmaxf(m, fabsf(val(j)));
     sq = i8_scale(m);
     if (c == 0 && lane < 32) qexp[q] = __float_as_int(sq);
   }
