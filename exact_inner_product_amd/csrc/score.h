@@ -4,6 +4,8 @@
 
 #include <utility>
 
+#include <hip/hip_ext.h>
+
 #include "host.h"
 #include "score_api.h"
 
@@ -760,7 +762,7 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
 }
 
 template <int CT, int D, int NQF, int MODE, int NT>
-static int launch_score(const ScoreArgs& A, int grid, hipStream_t s) {
+static int launch_score(const ScoreArgs& A, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr int lds = score_lds_bytes(CT, D, NQF, NT);
   static bool attr = false;
   if (!attr) {
@@ -768,23 +770,29 @@ static int launch_score(const ScoreArgs& A, int grid, hipStream_t s) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     attr = true;
   }
-  hipLaunchKernelGGL((score_kernel<CT, D, NQF, MODE, NT>), dim3(grid), dim3(score_threads(CT, D)), lds, s, A);
+  if (e0 && e1)
+    // timing events taken by the dispatch itself (events recorded as packets of their
+    // own around the launch would add a dispatch gap on each side)
+    hipExtLaunchKernelGGL((score_kernel<CT, D, NQF, MODE, NT>), dim3(grid), dim3(score_threads(CT, D)), lds, s,
+                          e0, e1, 0, A);
+  else
+    hipLaunchKernelGGL((score_kernel<CT, D, NQF, MODE, NT>), dim3(grid), dim3(score_threads(CT, D)), lds, s, A);
   return check_launch();
 }
 
 template <int CT, int D, int MODE, int NT>
-int launch_score_nqf(int nqf, const ScoreArgs& A, int grid, hipStream_t s) {
+int launch_score_nqf(int nqf, const ScoreArgs& A, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (nqf) {
-    case 1: return launch_score<CT, D, 1, MODE, NT>(A, grid, s);
-    case 2: return launch_score<CT, D, 2, MODE, NT>(A, grid, s);
+    case 1: return launch_score<CT, D, 1, MODE, NT>(A, grid, s, e0, e1);
+    case 2: return launch_score<CT, D, 2, MODE, NT>(A, grid, s, e0, e1);
     case 4:
-      if constexpr (nqf_fits(CT, D, 4, NT)) return launch_score<CT, D, 4, MODE, NT>(A, grid, s);
+      if constexpr (nqf_fits(CT, D, 4, NT)) return launch_score<CT, D, 4, MODE, NT>(A, grid, s, e0, e1);
       break;
     case 8:
-      if constexpr (NT == 0 && nqf_fits(CT, D, 8)) return launch_score<CT, D, 8, MODE, NT>(A, grid, s);
+      if constexpr (NT == 0 && nqf_fits(CT, D, 8)) return launch_score<CT, D, 8, MODE, NT>(A, grid, s, e0, e1);
       break;
     case 16:
-      if constexpr (NT == 0 && nqf_fits(CT, D, 16)) return launch_score<CT, D, 16, MODE, NT>(A, grid, s);
+      if constexpr (NT == 0 && nqf_fits(CT, D, 16)) return launch_score<CT, D, 16, MODE, NT>(A, grid, s, e0, e1);
       break;
   }
   return MIPS_ERR_UNSUPPORTED;

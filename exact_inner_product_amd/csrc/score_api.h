@@ -136,8 +136,10 @@ struct ScoreArgs {
 
 // Launches score_kernel<CT, D, nqf, MODE, NT> (nqf in {1, 2, 4, 8, 16}; NT = 0 for one
 // result set, kMaxMasks for a multi-mask pass); defined in score_inst.hip, built once per
-// corpus dtype and width.
+// corpus dtype and width. With both events given, the dispatch records e0 at the kernel's
+// start and e1 at its end.
 template <int CT, int D, int MODE, int NT = 0>
-int launch_score_nqf(int nqf, const ScoreArgs& A, int grid, hipStream_t s);
+int launch_score_nqf(int nqf, const ScoreArgs& A, int grid, hipStream_t s, hipEvent_t e0 = nullptr,
+                     hipEvent_t e1 = nullptr);
 
 }  // namespace mips

@@ -778,9 +778,7 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
     A.nfrag = p.n32;
     A.ntiles = (p.n32 + p.rm - 1) / p.rm;
     A.nslices = slices_for(A.ntiles, p.nqblk);
-    if (ev0) (void)hipEventRecord(ev0, s);
-    if ((rc = launch_score_nqf<CT, D, MODE_DENSE, NT>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
-    if (ev1) (void)hipEventRecord(ev1, s);
+    if ((rc = launch_score_nqf<CT, D, MODE_DENSE, NT>(p.nqf, A, A.nslices * p.nqblk, s, ev0, ev1))) return rc;
     S.dense_count = p.n32 * kFrag;
     hipLaunchKernelGGL((final_select_kernel<CT, D>), dim3(p.bv), dim3(kSelThreads), 0, s, S, 0);
     return check_launch();
@@ -807,9 +805,7 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   A.nfrag = p.n32;
   A.ntiles = (p.n32 + p.rm_main - 1) / p.rm_main;
   A.nslices = slices_for(A.ntiles, p.nqblk);
-  if (ev0) (void)hipEventRecord(ev0, s);
-  if ((rc = launch_score_nqf<CT, D, MODE_MAIN, NT>(p.nqf, A, A.nslices * p.nqblk, s))) return rc;
-  if (ev1) (void)hipEventRecord(ev1, s);
+  if ((rc = launch_score_nqf<CT, D, MODE_MAIN, NT>(p.nqf, A, A.nslices * p.nqblk, s, ev0, ev1))) return rc;
   S.dense_count = 0;
   S.nseg_used = A.nslices;
   hipLaunchKernelGGL((final_select_kernel<CT, D>), dim3(p.bv), dim3(kSelThreads), 0, s, S, 0);

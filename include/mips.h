@@ -340,9 +340,10 @@ MIPS_API int mips_merge_interests(const float *in_scores, const int32_t *in_ids,
 
 /*
  * mips_set_timing_events -- profiling hook (host, per calling thread). When both are
- * non-NULL, later mips_topk calls on this thread record `before` (a hipEvent_t)
- * immediately before and `after` immediately after the launch of the main score
- * kernel, on the call's stream. Pass NULL, NULL to stop. Returns MIPS_OK.
+ * non-NULL, later mips_topk calls on this thread launch the main score kernel so that its
+ * dispatch records `before` (a hipEvent_t) at the kernel's start and `after` at its end,
+ * on the call's stream (no packets of their own, so no gap between the call's kernels).
+ * Pass NULL, NULL to stop. Returns MIPS_OK.
  */
 MIPS_API int mips_set_timing_events(void *before, void *after);
 
