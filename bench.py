@@ -5,7 +5,7 @@ sampled threshold, the fused MFMA score/filter pass and the final merge. Default
 N=10,000,000 x D=128 bf16 corpus (clustered/Zipf, 16384 clusters), B=256 queries, K=500,
 5% of ids excluded. Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 40] [--warmup 3] [--workload NAME] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -236,7 +236,7 @@ def bench_masks(args, w, corpus, q, excl, torch, mips, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
