@@ -63,8 +63,16 @@ __global__ __launch_bounds__(64) void prep_queries_kernel(const void* __restrict
   const int q = qb * kFrag + (lane & 31);
   const int nrows = min(kFrag, b - qb * kFrag);
   const uint32_t* src = (const uint32_t*)queries + (int64_t)qb * kFrag * RW;
+  // Unconditional loads (words past the batch read its last word and are stored as zero): a
+  // load under a branch would be waited for before the next one is issued.
+  const int nw = nrows * RW;
+  static_assert(kFrag * RW % 64 == 0, "whole rounds of the 64 lanes");
 #pragma unroll 32
-  for (int i = lane; i < kFrag * RW; i += 64) rows[(i / RW) * RWP + i % RW] = i < nrows * RW ? src[i] : 0u;
+  for (int it = 0; it < kFrag * RW / 64; ++it) {
+    const int i = it * 64 + lane;
+    const uint32_t x = src[min(i, nw - 1)];
+    rows[(i / RW) * RWP + i % RW] = i < nw ? x : 0u;
+  }
   __syncthreads();
   auto val = [&](int dim) -> float {
     const uint32_t* r = rows + (lane & 31) * RWP;
@@ -447,7 +455,17 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
     write_out(A, q, sel_buf, r);
     return;
   }
-  const uint32_t tu = A.thr[q], tb = A.thrb[q];
+  // The list's words, issued together: its thresholds, overflow flag, rescued-run tail and
+  // segment counts (each thread reads a segment count in bounds; only those of the segments
+  // the pass wrote are used).
+  uint32_t tu = A.thr[q], tb = A.thrb[q];
+  uint32_t ovq = A.ovf[q];
+  const uint32_t rt_raw = A.rtail[q];
+  const uint32_t cnt_t = A.segcnt[(int64_t)q * A.nseg + min(t, A.nseg_used - 1)];
+  // (passed through one empty asm statement, so that the compiler issues every load before
+  // the first use of any of them instead of waiting for each in turn)
+  asm volatile("" : "+v"(tu), "+v"(tb), "+v"(ovq) : "v"(cnt_t), "v"(rt_raw));
+  const uint32_t rtq = round == 0 ? 0u : rt_raw;
   if (tu == 0u) {
     // No sampled bound (fewer than K sampled blocks hold an eligible row, so the query has
     // few eligible rows): the rescue pass gathers every eligible row on the MFMA path, and
@@ -465,10 +483,10 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
   uint32_t found, mine;
   int64_t total;  // everything the pass found for this list
   if (round == 0) {
-    found = t < A.nseg_used ? A.segcnt[(int64_t)q * A.nseg + t] : 0u;
+    found = t < A.nseg_used ? cnt_t : 0u;
     mine = found < (uint32_t)A.capw ? found : (uint32_t)A.capw;
   } else {
-    const int64_t r = (int64_t)A.rtail[q] - (int64_t)t * A.capw;
+    const int64_t r = (int64_t)rtq - (int64_t)t * A.capw;
     found = 0u;
     mine = t < A.nseg && r > 0 ? (uint32_t)min<int64_t>(r, A.capw) : 0u;
   }
@@ -477,7 +495,7 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
   segoff[t] = so.x;
   if (t == 0) segoff[kSelThreads] = so.y;
   const int64_t stored = so.y;
-  total = round == 0 ? (int64_t)sf.y : (int64_t)A.rtail[q];
+  total = round == 0 ? (int64_t)sf.y : (int64_t)rtq;
   c = total;
   const int nsu = round == 0 ? A.nseg_used : A.nseg;
   // entry i of the concatenated segments: the last segment starting at or before i
@@ -506,7 +524,7 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
     eligible = nbuf;
   }
   __syncthreads();
-  const bool over = stored < c || A.ovf[q] != 0u;
+  const bool over = stored < c || ovq != 0u;
   // Fewer than k candidates: final when the threshold was the proven bound. With one
   // bitmap per query the sample pass applied none, so its bound is not proven and a short
   // list is always rescued; at the bound itself only the exact rescan is left.
@@ -537,12 +555,13 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
   const int r = (int)min<int64_t>(eligible, A.k);
   if (r > 0) {
     if (c <= kSelCache) {
-      // each thread copies its own segment, 8 entries per round trip
+      // each thread copies its own segment, 8 entries per round trip (unconditional loads of
+      // stored entries: the last one again past the end, so that all 8 are in flight at once)
       const uint64_t* seg = qlist + (int64_t)t * A.capw;
       for (uint32_t i0 = 0; i0 < mine; i0 += 8) {
         uint64_t v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = i0 + e < mine ? seg[i0 + e] : 0ull;
+        for (int e = 0; e < 8; ++e) v[e] = seg[min(i0 + e, mine - 1)];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (i0 + e < mine) cache[segoff[t] + i0 + e] = own && excluded(v[e]) ? 0ull : v[e];
