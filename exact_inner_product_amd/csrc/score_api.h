@@ -17,7 +17,7 @@ constexpr int kMaxSample = 8192;    // sampled 32-row blocks
 constexpr int kMaxSegments = 256;   // list segments per query (corpus slices of a pass)
 constexpr int kSimdStageBytes = 16384;  // corpus bytes per SIMD and pipeline stage
 constexpr int kPipeStages = 3;      // corpus stages per wave: one in use, two in flight
-constexpr int kSelCache = 6144;     // candidates the final select caches in LDS
+constexpr int kSelCacheMax = 8192;  // candidates the final select caches in LDS, at most
 constexpr int kMaxMasks = 4;        // result sets (exclusion masks) of one multi-mask pass
 constexpr int kMaskNqfMax = 4;      // query fragments per workgroup of a multi-mask pass
 
@@ -83,6 +83,15 @@ __host__ __device__ constexpr int score_lds_bytes(int ct, int d, int nqf, int nt
 }
 __host__ __device__ constexpr bool nqf_fits(int ct, int d, int nqf, int nt = 0) {
   return score_lds_bytes(ct, d, nqf, nt) <= kLdsLimit;
+}
+// Entries of the final select's LDS candidate cache for k results: room for about 8 k
+// candidates (a longer list is read from memory on every pass over it), at least 2048 (the
+// exact rescan compacts a buffer that holds k + 1024 keys) and at most kSelCacheMax. The
+// smaller the cache, the more lists a compute unit selects at once.
+__host__ __device__ constexpr int sel_cache_entries(int k) {
+  int c = 2048;
+  while (c < 8 * k && c < kSelCacheMax) c <<= 1;
+  return c;
 }
 
 struct ScoreArgs {

@@ -56,19 +56,20 @@ struct SelScratch {
   uint64_t red[8];
 };
 
-// The r largest of n keys (1 <= r <= n), MSD radix select with 8-bit digits starting at
-// the highest bit where the keys differ; stops as soon as the boundary bin holds exactly
-// the remaining rank. With distinct keys exactly r keys satisfy the returned test; with
-// ties, prefix is still a lower bound of the r-th largest key.
-template <typename Get>
-__device__ Sel64 select_top(Get get, int64_t n, int r, SelScratch& S) {
+// The r largest of the workgroup's keys (1 <= r <= their number), MSD radix select with
+// 8-bit digits starting at the highest bit where the keys differ; stops as soon as the
+// boundary bin holds exactly the remaining rank. With distinct keys exactly r keys satisfy
+// the returned test; with ties, prefix is still a lower bound of the r-th largest key.
+// each(f) calls f(key) for every key the calling thread holds; the keys must be the same
+// on every call.
+template <typename Each>
+__device__ Sel64 select_top_each(Each each, int r, SelScratch& S) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   uint64_t lo = ~0ull, hi = 0ull;
-  for (int64_t i = t; i < n; i += kSelThreads) {
-    const uint64_t k = get(i);
+  each([&](uint64_t k) {
     lo = k < lo ? k : lo;
     hi = k > hi ? k : hi;
-  }
+  });
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const uint64_t l2 = shfl_xor_u64(lo, o), h2 = shfl_xor_u64(hi, o);
@@ -99,10 +100,9 @@ __device__ Sel64 select_top(Get get, int64_t n, int r, SelScratch& S) {
     const uint64_t dmask = (1ull << width) - 1ull;
     S.hist[t] = 0u;
     __syncthreads();
-    for (int64_t i = t; i < n; i += kSelThreads) {
-      const uint64_t k = get(i);
+    each([&](uint64_t k) {
       if ((k & mask) == prefix) atomicAdd(&S.hist[(k >> lb) & dmask], 1u);
-    }
+    });
     __syncthreads();
     const DigitPick pk = pick_digit(S.hist, rem, S.wsum, &S.pick);
     prefix |= (uint64_t)pk.digit << lb;
@@ -112,6 +112,16 @@ __device__ Sel64 select_top(Get get, int64_t n, int r, SelScratch& S) {
     hb = lb - 1;
   }
   return Sel64{prefix, mask};
+}
+
+// The r largest of n keys get(0 .. n-1), thread t taking i = t, t + kSelThreads, ...
+template <typename Get>
+__device__ Sel64 select_top(Get get, int64_t n, int r, SelScratch& S) {
+  return select_top_each(
+      [&](auto f) {
+        for (int64_t i = threadIdx.x; i < n; i += kSelThreads) f(get(i));
+      },
+      r, S);
 }
 
 __device__ __forceinline__ int pow2_at_least(int x) {
@@ -195,21 +205,29 @@ __device__ inline void bitonic_sort_desc(uint64_t* s, int r) {
   else bitonic_sort_desc_p<1024>(s, r);
 }
 
-// Gathers the r selected keys of `get` into out[0..r) and sorts them descending. The keys
-// are distinct (composite keys carry the id).
-template <typename Get>
-__device__ void gather_sort(Get get, int64_t n, int r, Sel64 sel, uint64_t* out, uint32_t* cnt) {
+// Gathers the r selected keys (visited as by select_top_each) into out[0..r) and sorts
+// them descending. The keys are distinct (composite keys carry the id).
+template <typename Each>
+__device__ void gather_sort_each(Each each, int r, Sel64 sel, uint64_t* out, uint32_t* cnt) {
   if (threadIdx.x == 0) *cnt = 0u;
   __syncthreads();
-  for (int64_t i = threadIdx.x; i < n; i += kSelThreads) {
-    const uint64_t key = get(i);
+  each([&](uint64_t key) {
     if ((key & sel.mask) >= sel.prefix) {
       const uint32_t slot = atomicAdd(cnt, 1u);
       if (slot < (uint32_t)r) out[slot] = key;
     }
-  }
+  });
   __syncthreads();
   bitonic_sort_desc(out, r);
+}
+
+template <typename Get>
+__device__ void gather_sort(Get get, int64_t n, int r, Sel64 sel, uint64_t* out, uint32_t* cnt) {
+  gather_sort_each(
+      [&](auto f) {
+        for (int64_t i = threadIdx.x; i < n; i += kSelThreads) f(get(i));
+      },
+      r, sel, out, cnt);
 }
 
 }  // namespace mips

@@ -234,6 +234,7 @@ struct SelectArgs {
   int64_t capw;         // entries per list segment
   int nseg;             // segments per query list
   int nseg_used;        // segments written by the pass being selected from
+  int cache_n;          // entries of the LDS candidate cache (sel_cache_entries(k))
   int64_t dense_count;  // > 0: lists hold one slot per row (0 = empty), this many
   uint32_t* thr;
   uint32_t* thrb;
@@ -289,7 +290,7 @@ __device__ void fallback_scan(const SelectArgs& A, int q, uint64_t thr, uint64_t
   __syncthreads();
   constexpr int kRound = kSelThreads * 4;
   for (int64_t base = A.lo; base < A.n; base += kRound) {
-    if (*nbuf_p + (uint32_t)kRound > (uint32_t)kSelCache) {
+    if (*nbuf_p + (uint32_t)kRound > (uint32_t)A.cache_n) {
       // Compact to the k best and raise the threshold to their lower bound.
       const int m = (int)*nbuf_p;
       const int r = min(A.k, m);
@@ -389,12 +390,11 @@ constexpr uint32_t kEveryRowKey = 0x007FFFFFu;
 // thread s handles segment s.
 template <int CT, int D>
 __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A, int round) {
-  __shared__ uint64_t cache[kSelCache];
+  extern __shared__ __attribute__((aligned(16))) uint64_t cache[];  // A.cache_n entries
   __shared__ uint64_t sel_buf[MIPS_K_MAX];
   __shared__ SelScratch S;
   __shared__ float qv[D];
   __shared__ uint32_t nbuf;
-  __shared__ uint32_t segoff[kSelThreads + 1];
   __shared__ uint32_t wsum[kSelThreads / kWave];
   int q = blockIdx.x;
   if (round > 0) {
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
     // dense list: one slot per row; empty slots (key 0) are not candidates, so select
     // among the others only and no tie at the boundary involves an empty slot
     c = A.dense_count;
-    cached = c <= kSelCache;
+    cached = c <= A.cache_n;
     if (t == 0) nbuf = 0u;
     __syncthreads();
     uint32_t mine = 0u;
@@ -492,33 +492,30 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
   }
   const uint2 so = block_exclusive_sum(mine, wsum);
   const uint2 sf = block_exclusive_sum(found, wsum);
-  segoff[t] = so.x;
-  if (t == 0) segoff[kSelThreads] = so.y;
   const int64_t stored = so.y;
   total = round == 0 ? (int64_t)sf.y : (int64_t)rtq;
   c = total;
-  const int nsu = round == 0 ? A.nseg_used : A.nseg;
-  // entry i of the concatenated segments: the last segment starting at or before i
-  auto at = [&](int64_t i) {
-    int lo = 0, hi = nsu;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if ((int64_t)segoff[mid] <= i) lo = mid; else hi = mid;
+  // Visits the thread's stored entries (its segment), 8 per round trip: unconditional loads
+  // of stored entries (the last one again past the end), so that all 8 are in flight at
+  // once. An entry the query's own bitmap excludes reads as key 0, below every real key.
+  const uint64_t* seg = qlist + (int64_t)t * A.capw;
+  auto each = [&](auto f) {
+    for (uint32_t i0 = 0; i0 < mine; i0 += 8) {
+      uint64_t v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = seg[min(i0 + e, mine - 1)];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (i0 + e < mine) f(own && excluded(v[e]) ? 0ull : v[e]);
     }
-    return qlist[(int64_t)lo * A.capw + (i - segoff[lo])];
-  };
-  auto atx = [&](int64_t i) {
-    const uint64_t key = at(i);
-    return own && excluded(key) ? 0ull : key;
   };
   // eligible: the stored candidates the query's own bitmap keeps (all without one)
   int64_t eligible = stored;
   if (own) {
     if (t == 0) nbuf = 0u;
     __syncthreads();
-    const uint64_t* seg = qlist + (int64_t)t * A.capw;
     uint32_t keep = 0u;
-    for (uint32_t i = 0; i < mine; ++i) keep += excluded(seg[i]) ? 0u : 1u;
+    each([&](uint64_t key) { keep += key != 0ull; });
     atomicAdd(&nbuf, keep);
     __syncthreads();
     eligible = nbuf;
@@ -542,7 +539,7 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
     if (over) {
       nt = tu;
       if (eligible >= A.k) {
-        const uint64_t kth = select_top(atx, stored, A.k, S).prefix;
+        const uint64_t kth = select_top_each(each, A.k, S).prefix;
         if ((uint32_t)(kth >> 32) >= nt) {
           nt = (uint32_t)(kth >> 32);
           nid = composite_id(kth);
@@ -554,18 +551,10 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
   }
   const int r = (int)min<int64_t>(eligible, A.k);
   if (r > 0) {
-    if (c <= kSelCache) {
-      // each thread copies its own segment, 8 entries per round trip (unconditional loads of
-      // stored entries: the last one again past the end, so that all 8 are in flight at once)
-      const uint64_t* seg = qlist + (int64_t)t * A.capw;
-      for (uint32_t i0 = 0; i0 < mine; i0 += 8) {
-        uint64_t v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = seg[min(i0 + e, mine - 1)];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (i0 + e < mine) cache[segoff[t] + i0 + e] = own && excluded(v[e]) ? 0ull : v[e];
-      }
+    if (c <= A.cache_n) {
+      // each thread copies its own segment to its place in the cache
+      uint32_t j = so.x;
+      each([&](uint64_t key) { cache[j++] = key; });
       __syncthreads();
       if (c <= kSortAll && c <= 4 * (int64_t)A.k) {
         // a short list: one sort of every candidate (excluded ones, key 0, sink to the end)
@@ -578,12 +567,26 @@ __global__ __launch_bounds__(kSelThreads) void final_select_kernel(SelectArgs A,
       if (c > r) sel = select_top(get, c, r, S);
       gather_sort(get, c, r, sel, sel_buf, &S.hist[0]);
     } else {
+      // a list longer than the cache: each pass reads the segments again
       Sel64 sel{0ull, 0ull};
-      if (c > r) sel = select_top(atx, c, r, S);
-      gather_sort(atx, c, r, sel, sel_buf, &S.hist[0]);
+      if (c > r) sel = select_top_each(each, r, S);
+      gather_sort_each(each, r, sel, sel_buf, &S.hist[0]);
     }
   }
   write_out(A, q, sel_buf, r);
+}
+
+template <int CT, int D>
+static void launch_select(const SelectArgs& S, int grid, int round, hipStream_t s) {
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)final_select_kernel<CT, D>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              kSelCacheMax * (int)sizeof(uint64_t));
+    attr = true;
+  }
+  hipLaunchKernelGGL((final_select_kernel<CT, D>), dim3(grid), dim3(kSelThreads),
+                     (size_t)S.cache_n * sizeof(uint64_t), s, S, round);
 }
 
 // ------------------------------------------------------------------- planning
@@ -773,6 +776,7 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   S.lo = p.lo;
   S.b = p.bv;
   S.k = p.k;
+  S.cache_n = sel_cache_entries(p.k);
   S.masks = masks;
   S.mask_words = mask_words;
   S.breal = NT > 0 ? p.b : 0;
@@ -799,7 +803,7 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
     A.nslices = slices_for(A.ntiles, p.nqblk);
     if ((rc = launch_score_nqf<CT, D, MODE_DENSE, NT>(p.nqf, A, A.nslices * p.nqblk, s, ev0, ev1))) return rc;
     S.dense_count = p.n32 * kFrag;
-    hipLaunchKernelGGL((final_select_kernel<CT, D>), dim3(p.bv), dim3(kSelThreads), 0, s, S, 0);
+    launch_select<CT, D>(S, p.bv, 0, s);
     return check_launch();
   }
 
@@ -827,7 +831,7 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   if ((rc = launch_score_nqf<CT, D, MODE_MAIN, NT>(p.nqf, A, A.nslices * p.nqblk, s, ev0, ev1))) return rc;
   S.dense_count = 0;
   S.nseg_used = A.nslices;
-  hipLaunchKernelGGL((final_select_kernel<CT, D>), dim3(p.bv), dim3(kSelThreads), 0, s, S, 0);
+  launch_select<CT, D>(S, p.bv, 0, s);
   if ((rc = check_launch())) return rc;
 
   // rescue pass over the queued queries (one workgroup per slice loops over them)
@@ -840,7 +844,7 @@ static int run_topk(const Plan& p, const void* queries, const void* corpus, cons
   R.nslices = slices_for(A.ntiles, 1);
   if ((rc = launch_score_nqf<CT, D, MODE_MAIN, NT>(p.nqf, R, R.nslices, s))) return rc;
   S.nseg_used = R.nslices;
-  hipLaunchKernelGGL((final_select_kernel<CT, D>), dim3(p.bv), dim3(kSelThreads), 0, s, S, 1);
+  launch_select<CT, D>(S, p.bv, 1, s);
   return check_launch();
 }
 
