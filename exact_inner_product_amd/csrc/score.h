@@ -623,14 +623,29 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
             const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)xwv, NT > 0 ? g * NT + t : g);
             float x[16];
             vals(acc[g], sc[g], sq, x);
-            float mx = -INFINITY;
+            // The maximum starts from kMaxSeed, below every score of unit vectors; a block
+            // whose maximum stays at or below it has no delegate (key 0). That can only
+            // drop a delegate, so the bound stays proven.
+            float mx = kMaxSeed;
+            if (w == 0u) {
+              // every row of the block is eligible (the usual case; w is wave-uniform): a
+              // plain chain of v_max3
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int row = acc_row(i, lane);
-              mx = ((w >> row) & 1u) ? mx : fmaxf(mx, x[i]);
+              for (int i = 0; i < 16; ++i) mx = fmaxf(mx, x[i]);
+            } else {
+              // Register i holds row acc_row(i, lane): bit 8 (i / 4) + i % 4 of w in lanes
+              // 0-31, that bit + 4 in lanes 32-63. Its exclusion is thus a wave-uniform lane
+              // mask, built on the scalar unit and applied by one select.
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int b0 = 8 * (i >> 2) + (i & 3);
+                const uint64_t m = (((w >> b0) & 1u) ? 0x00000000FFFFFFFFull : 0ull) |
+                                   (((w >> (b0 + 4)) & 1u) ? 0xFFFFFFFF00000000ull : 0ull);
+                mx = fmaxf(mx, __builtin_amdgcn_inverse_ballot_w64(m) ? -INFINITY : x[i]);
+              }
             }
             mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));  // the block's other 16 rows
-            d[g] = (mx == -INFINITY) ? 0u : score_key(mx);
+            d[g] = (mx <= kMaxSeed) ? 0u : score_key(mx);
             asm volatile("" : "+v"(d[g]));  // computed in uniform control flow, as above
           }
           if constexpr (NT > 0) {
