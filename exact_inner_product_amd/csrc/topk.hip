@@ -659,14 +659,15 @@ static void make_plan(Plan& p, int b, int64_t n, int d, int k, int qdt, int cdt,
   p.capw = capq < 0 ? default_capw(p.n32, k, p.nseg) : capq / p.nseg;
   p.dense = p.n32 < 2 * (int64_t)k + 64 && p.n32 * kFrag <= p.nseg * p.capw;
   // sampled blocks: a 16th of the corpus (the sample pass re-reads them), but no more than
-  // needed for about 6 of the K best items to be expected in the sample (K G / n32 = 6, where
-  // the margin c of estimate_rank is 3.45; a larger sample costs the sample pass more than
-  // its fewer survivors save the main pass and the select); at least 4 K, so that the K-th
-  // delegate usually exists; at most kMaxSample
-  const int64_t g6 = (6 * p.n32 + k - 1) / k;
+  // needed for about 12 of the K best items to be expected in the sample (K G / n32 = 12,
+  // where the margin c of estimate_rank is 2.73). Every survivor of the main pass costs it a
+  // slow-path walk, so a larger sample shortens that pass; beyond about 12 items the sample
+  // pass costs more than the main pass saves. At least 4 K, so that the K-th delegate usually
+  // exists; at most kMaxSample.
+  const int64_t g12 = (12 * p.n32 + k - 1) / k;
   p.G = p.dense ? 0
                 : (int)std::min<int64_t>(std::min<int64_t>(p.n32, kMaxSample),
-                                         std::max<int64_t>(std::min<int64_t>(p.n32 / 16, g6), 4 * (int64_t)k));
+                                         std::max<int64_t>(std::min<int64_t>(p.n32 / 16, g12), 4 * (int64_t)k));
   p.rest = p.dense ? 0 : estimate_rank(p.n32, p.G, k);
   const int E = elem_bytes(cdt);
   size_t o = 0;
