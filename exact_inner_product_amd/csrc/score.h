@@ -686,12 +686,13 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
           // issue priority while this wave issues its MFMAs, none during its epilogue: the
           // two waves of a SIMD then take turns on the matrix pipe instead of sharing it and
           // reaching their epilogues together
+          // the fragment's threshold is read ahead of the operand refills issued among its
+          // MFMAs, so that the compare waits for that read alone, not for the refills too
+          const float Tf = Tq(qf);
           __builtin_amdgcn_s_setprio(3);
           mfmas(acc1, a, sa, bq1, sbq(qf), qf + 1 < NQF ? qf + 1 : -1);
           __builtin_amdgcn_s_setprio(0);
-          // (the threshold is read after the MFMAs here: this path has no register to spare
-          // for it across the chain, and the other wave covers the wait)
-          epi_main(acc1, sc, xwv, j0, qf, Tq(qf), qscale(qf));
+          epi_main(acc1, sc, xwv, j0, qf, Tf, qscale(qf));
         });
         return;
       }
