@@ -488,19 +488,20 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
         H &= H - 1ull;
         uint32_t pl = (uint32_t)__builtin_amdgcn_readlane((int)pm, L);
         const int qcol = qf * kFrag + (L & 31);
-        // column L's threshold (T is per lane: each lane holds its own column's)
-        const float TL = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(T), L));
+        // column L's threshold key (T is per lane: each lane holds its own column's); the
+        // walk compares keys, so that it stays on the scalar unit
+        const uint32_t kTL = score_key(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(T), L)));
         while (pl != 0u) {
           const int i = __builtin_ctz(pl);
           pl &= pl - 1u;
-          const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(y[i]), L));
+          const uint32_t kv = score_key(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(y[i]), L)));
           const uint32_t id = idb + (uint32_t)(8 * (i >> 2) + 4 * (L >> 5) + (i & 3));
           // a rescue threshold is composite: at the threshold's own score only ids at or
           // below its id bound pass (rows tied with the k-th candidate cannot flood it)
-          if (rescue && v == TL && id > A.thr_id[listid(qcol, t)]) continue;
+          if (rescue && kv == kTL && id > A.thr_id[listid(qcol, t)]) continue;
           if (st_n < kStageCap) {
             if (lane == 0) {
-              st_key[st_n] = composite(score_key(v), id);
+              st_key[st_n] = composite(kv, id);
               st_q[st_n] = (uint16_t)(NT > 0 ? qcol * NTS + t : qcol);
             }
           } else if (lane == 0) {
