@@ -111,8 +111,20 @@ __attribute__((amdgpu_waves_per_eu(score_wps(CT, D), score_wps(CT, D)))) void sc
   uint64_t* st_key = (uint64_t*)(sexp_lds + QB + QB * NT) + wave * kStageCap;
   uint16_t* st_q = (uint16_t*)((uint64_t*)(sexp_lds + QB + QB * NT) + kScoreWaves * kStageCap) + wave * kStageCap;
 
-  const int64_t t_begin = (int64_t)slice * A.ntiles / A.nslices;
-  const int64_t t_end = (int64_t)(slice + 1) * A.ntiles / A.nslices;
+  // The corpus slices' shares of the tiles. With the slices spread over the 8 XCDs (slice s on
+  // XCD s % 8, the dispatch order), an odd XCD's slice takes 24 shares to an even XCD's 25:
+  // timed per workgroup, the odd XCDs ran 2-5% slower than the even ones (a lower shader
+  // clock) on every call, so that the pass ended with them.
+  int64_t t_begin, t_end;
+  if (A.nslices % 8 == 0) {
+    auto cum = [](int64_t s) { return (s >> 1) * 49 + (s & 1) * 25; };
+    const int64_t W = cum(A.nslices);
+    t_begin = A.ntiles * cum(slice) / W;
+    t_end = A.ntiles * cum(slice + 1) / W;
+  } else {
+    t_begin = (int64_t)slice * A.ntiles / A.nslices;
+    t_end = (int64_t)(slice + 1) * A.ntiles / A.nslices;
+  }
   const int nq_total = rescue ? (int)*A.nlist : A.b;
   const int qstep = rescue ? 1 : A.nqblk;
 
